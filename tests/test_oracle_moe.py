@@ -1,0 +1,421 @@
+"""Pins of the oracle's MoE functions against brute force, closed forms,
+invariants and finite differences.
+
+Each test is chosen so that a plausible mistake in the oracle (a dropped bias,
+swapped gate/up halves, a transposed operand, a wrong sign in a derivative,
+an off-by-one in the grouping) fails it.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import formats as F
+from oracle import moe as O
+
+
+# ------------------------------------------------------------------ routing / grouping
+def _route_bruteforce(logits, k):
+    T, E = logits.shape
+    ids = []
+    for t in range(T):
+        pairs = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))
+        ids.append(pairs[:k])
+    counts = [0] * E
+    for t in range(T):
+        for j in range(k):
+            counts[ids[t][j]] += 1
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + counts[e])
+    fill = list(offsets[:-1])
+    dst = [[0] * k for _ in range(T)]
+    src = [0] * (T * k)
+    for t in range(T):                       # (t, j) ascending = stable
+        for j in range(k):
+            e = ids[t][j]
+            dst[t][j] = fill[e]
+            src[fill[e]] = t
+            fill[e] += 1
+    return ids, counts, offsets, dst, src
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(7, 4, 2, 0), (33, 8, 3, 1), (64, 5, 1, 2), (20, 6, 6, 3)])
+def test_route_matches_bruteforce(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.integers(-3, 4, size=(T, E)).astype(np.float32)   # many exact ties
+    ids, counts, off, dst, src = O.route_topk(logits, k)
+    bids, bcounts, boff, bdst, bsrc = _route_bruteforce(logits, k)
+    assert ids.tolist() == bids
+    assert counts.tolist() == bcounts and off.tolist() == boff
+    assert dst.tolist() == bdst and src.tolist() == bsrc
+
+
+def test_route_invariants_gptoss():
+    d = W.gptoss(with_weights=False)
+    ids, counts, off, dst, src = O.route_topk(d["logits"], d["k"])
+    T, k, E = d["T"], d["k"], d["E"]
+    assert counts.sum() == T * k and off[-1] == T * k
+    assert np.all(np.diff(off) >= 0)
+    assert np.array_equal(np.sort(dst.reshape(-1)), np.arange(T * k))
+    for t in (0, 17, T - 1):
+        assert len(set(ids[t].tolist())) == k
+        for j in range(k):
+            r = dst[t, j]
+            assert src[r] == t and off[ids[t, j]] <= r < off[ids[t, j] + 1]
+    mean = T * k / E
+    assert counts[0] == 0 and counts.max() > 2 * mean      # the workload's stated properties
+
+
+def test_route_tiny_empty_expert():
+    d = W.tiny(empty_expert=True)
+    _, counts, off, _, _ = O.route_topk(d["logits"], d["k"])
+    assert counts[3] == 0 and off[3] == off[4]
+
+
+def test_dsv3_counts_zipf():
+    c = W.dsv3_counts()
+    assert c.sum() == 16384 and len(c) == 32
+    s = np.sort(c)[::-1]
+    assert s.tolist()[:4] == [4649, 2169, 1388, 1012] and s[-1] == 103
+    # proportional to r^-1.1 within apportionment error
+    w = np.arange(1, 33) ** -1.1
+    assert np.all(np.abs(s - 16384 * w / w.sum()) < 1.0)
+
+
+# ------------------------------------------------------------------ repack
+def test_repack_roundtrip_and_permutation():
+    rng = np.random.default_rng(3)
+    E, H, I = 3, 16, 192
+    w = rng.integers(0, 2 ** 16, size=(E, H, 2 * I)).astype(np.uint16)
+    b = rng.integers(0, 2 ** 16, size=(E, 2 * I)).astype(np.uint16)
+    wp, bp = O.repack_gate_up(w, b)
+    assert wp.shape == (E, 2 * I, H)
+    w2, b2 = O.unpack_gate_up(wp, bp)
+    assert np.array_equal(w2, w) and np.array_equal(b2, b)
+    assert np.array_equal(np.sort(wp.reshape(-1)), np.sort(w.reshape(-1)))
+    # each 128-column packed block holds gate j..j+63 then the same up columns
+    for p in range(I // 64):
+        for s in range(64):
+            assert np.array_equal(wp[:, 128 * p + s, :], w[:, :, 64 * p + s])
+            assert np.array_equal(wp[:, 128 * p + 64 + s, :], w[:, :, I + 64 * p + s])
+
+
+# ------------------------------------------------------------------ FC1 + GLU
+def _act_scalar(g, act, alpha):
+    if act == "swiglu":
+        return g / (1.0 + math.exp(-alpha * g)) if g > -700 else 0.0
+    if act == "geglu":
+        return 0.5 * g * (1.0 + math.erf(g / math.sqrt(2.0)))
+    if act == "geglu_tanh":
+        return 0.5 * g * (1.0 + math.tanh(math.sqrt(2 / math.pi) * (g + 0.044715 * g ** 3)))
+    if act == "srelu":
+        return max(g, 0.0) ** 2
+    raise ValueError
+
+
+def _fc1_glu_loops(x, counts, w1, ep, bias=None):
+    """Brute force in pure Python loops: the GLU identity
+    y = act(x.Wg + bg) * (x.Wu + bu) on the plain (un-repacked) W1."""
+    E, H, N2 = w1.shape
+    I = N2 // 2
+    off = np.concatenate([[0], np.cumsum(counts)])
+    M = int(off[-1])
+    y = np.zeros((M, I))
+    for e in range(E):
+        for r in range(off[e], off[e + 1]):
+            for i in range(I):
+                g = sum(x[r, h] * w1[e, h, i] for h in range(H))
+                u = sum(x[r, h] * w1[e, h, I + i] for h in range(H))
+                if bias is not None:
+                    g += bias[e, i]
+                    u += bias[e, I + i]
+                g = min(max(g, ep.gate_lo), ep.gate_hi)
+                u = min(max(u, ep.up_lo), ep.up_hi) + ep.up_offset
+                y[r, i] = _act_scalar(g, ep.act, ep.alpha) * u
+    return y
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu", "geglu_tanh", "srelu"])
+def test_fc1_glu_matches_bruteforce_loops(act):
+    rng = np.random.default_rng(4)
+    counts = np.array([3, 0, 5, 1])
+    E, H, I = 4, 6, 64
+    x = W.to_bf16_bits(rng.standard_normal((9, H)).astype(np.float32))
+    w1 = W.to_bf16_bits(rng.standard_normal((E, H, 2 * I)).astype(np.float32) * 0.5)
+    b1 = W.to_bf16_bits(rng.standard_normal((E, 2 * I)).astype(np.float32) * 0.1)
+    ep = O.Epilogue(act=act, alpha=1.702 if act == "swiglu" else 1.0, gate_lo=-1.0, gate_hi=1.5,
+                    up_lo=-2.0, up_hi=1.0, up_offset=0.25, bias=b1)
+    preact, y = O.fc1_glu(x, counts, w1, ep)
+    ref = _fc1_glu_loops(F.bf16_bits_to_f64(x), counts, F.bf16_bits_to_f64(w1), ep,
+                         F.bf16_bits_to_f64(b1))
+    assert np.array_equal(y, F.f64_to_bf16_bits(ref))
+    assert y.shape == (9, I) and preact.shape == (9, 2 * I)
+
+
+def test_fc1_glu_through_packed_weights():
+    """The packed layout carries the pairing: a GEMM on the packed weights whose
+    every 128-column block is split 64 | 64 gives the same GLU as gate | up."""
+    rng = np.random.default_rng(5)
+    E, H, I = 2, 32, 128
+    counts = np.array([7, 4])
+    x = W.to_bf16_bits(rng.standard_normal((11, H)).astype(np.float32))
+    w1 = W.to_bf16_bits(rng.standard_normal((E, H, 2 * I)).astype(np.float32) * 0.3)
+    wp, _ = O.repack_gate_up(w1)
+    ep = O.Epilogue()
+    _, y = O.fc1_glu(x, counts, w1, ep)
+    xf = F.bf16_bits_to_f64(x)
+    off = [0, 7, 11]
+    ypk = np.zeros((11, I))
+    for e in range(E):
+        zp = xf[off[e]:off[e + 1]] @ F.bf16_bits_to_f64(wp[e]).T       # packed order
+        for p in range(I // 64):
+            g = zp[:, 128 * p:128 * p + 64]
+            u = zp[:, 128 * p + 64:128 * p + 128]
+            ypk[off[e]:off[e + 1], 64 * p:64 * p + 64] = g / (1 + np.exp(-g)) * u
+    assert np.array_equal(y, F.f64_to_bf16_bits(ypk))
+
+
+def test_fc1_zero_token_experts_produce_nothing():
+    rng = np.random.default_rng(6)
+    E, H, I = 3, 8, 64
+    w1 = W.to_bf16_bits(rng.standard_normal((E, H, 2 * I)).astype(np.float32))
+    x = W.to_bf16_bits(rng.standard_normal((5, H)).astype(np.float32))
+    p1, y1 = O.fc1_glu(x, [0, 5, 0], w1, O.Epilogue())
+    # same rows, expert 0/2 weights replaced by NaN: nothing changes
+    w1n = w1.copy()
+    w1n[0] = 0x7FC0
+    w1n[2] = 0x7FC0
+    p2, y2 = O.fc1_glu(x, [0, 5, 0], w1n, O.Epilogue())
+    assert np.array_equal(y1, y2) and np.array_equal(p1, p2)
+    assert y1.shape[0] == 5
+
+
+def test_fc1_row_permutation_within_group():
+    rng = np.random.default_rng(7)
+    E, H, I = 2, 16, 64
+    counts = np.array([6, 5])
+    w1 = W.to_bf16_bits(rng.standard_normal((E, H, 2 * I)).astype(np.float32) * 0.2)
+    x = W.to_bf16_bits(rng.standard_normal((11, H)).astype(np.float32))
+    perm = np.concatenate([rng.permutation(6), 6 + rng.permutation(5)])
+    p1, y1 = O.fc1_glu(x, counts, w1, O.Epilogue())
+    p2, y2 = O.fc1_glu(x[perm], counts, w1, O.Epilogue())
+    assert np.array_equal(y1[perm], y2) and np.array_equal(p1[perm], p2)
+    q1, s1 = O.mx_quantize_rows(y1)
+    q2, s2 = O.mx_quantize_rows(y2)
+    assert np.array_equal(q1[perm], q2) and np.array_equal(s1[perm], s2)
+
+
+# ------------------------------------------------------------------ activations
+def test_activation_special_values():
+    z = np.array([0.0])
+    assert O.activation(z, "swiglu")[0] == 0.0
+    assert O.activation_grad(z, "swiglu")[0] == 0.5
+    assert O.activation(z, "geglu")[0] == 0.0
+    assert O.activation_grad(z, "geglu")[0] == 0.5
+    assert O.activation_grad(z, "geglu_tanh")[0] == 0.5
+    assert O.activation_grad(z, "srelu")[0] == 0.0
+    big = np.array([-1e4, -800.0])
+    for a in ("swiglu", "geglu", "geglu_tanh", "srelu"):
+        v = O.activation(big, a)
+        d = O.activation_grad(big, a)
+        assert np.all(np.isfinite(v)) and np.all(np.abs(v) < 1e-30)
+        assert np.all(np.isfinite(d)) and np.all(np.abs(d) < 1e-30)
+    assert O.activation(np.array([3.0]), "srelu")[0] == 9.0
+    # silu(x) -> x for large x; gelu(x) -> x
+    assert abs(O.activation(np.array([40.0]), "swiglu")[0] - 40.0) < 1e-12
+    assert abs(O.activation(np.array([40.0]), "geglu")[0] - 40.0) < 1e-12
+
+
+@pytest.mark.parametrize("act,alpha", [("swiglu", 1.0), ("swiglu", 1.702), ("geglu", 1.0),
+                                       ("geglu_tanh", 1.0), ("srelu", 1.0)])
+def test_activation_grad_finite_difference(act, alpha):
+    g = np.linspace(-6, 6, 241) + 0.013
+    h = 1e-6
+    fd = (O.activation(g + h, act, alpha) - O.activation(g - h, act, alpha)) / (2 * h)
+    an = O.activation_grad(g, act, alpha)
+    assert np.max(np.abs(fd - an) / np.maximum(1, np.abs(an))) < 1e-7
+
+
+# ------------------------------------------------------------------ backward: finite differences
+def _tiny_chain(seed, act, ep_kw):
+    rng = np.random.default_rng(seed)
+    T, H, I, E = 4, 8, 8, 2
+    counts = np.array([3, 1])
+    x = F.bf16_round(rng.standard_normal((T, H)))
+    w1 = F.bf16_round(rng.standard_normal((E, H, 2 * I)) * 0.5)
+    b1 = F.bf16_round(rng.standard_normal((E, 2 * I)) * 0.1)
+    w2 = F.bf16_round(rng.standard_normal((E, I, H)) * 0.5)
+    dy2 = F.bf16_round(rng.standard_normal((T, H)))
+    ep = O.Epilogue(act=act, **ep_kw)
+    return counts, x, w1, b1, w2, dy2, ep
+
+
+def _loss(x, counts, w1, b1, w2, dy2, ep):
+    """L = <dY2, FC2(GLU(FC1(X)))> in exact float64 (no rounding)."""
+    off = np.concatenate([[0], np.cumsum(counts)])
+    L = 0.0
+    for e in range(len(counts)):
+        a, b = off[e], off[e + 1]
+        z = x[a:b] @ w1[e] + b1[e]
+        y = O.glu_from_preact(z, ep)
+        L += float(np.sum(dy2[a:b] * (y @ w2[e])))
+    return L
+
+
+@pytest.mark.parametrize("act,ep_kw", [
+    ("swiglu", {}), ("swiglu", dict(alpha=1.702, gate_lo=-0.7, gate_hi=0.7, up_lo=-0.7, up_hi=0.7)),
+    ("geglu", {}), ("geglu_tanh", dict(up_offset=1.0)), ("srelu", {}),
+])
+def test_dglu_and_dx_against_finite_differences(act, ep_kw):
+    counts, x, w1, b1, w2, dy2, ep = _tiny_chain(21, act, ep_kw)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    # analytic: G = dY2 W2^T, dz = dglu(G, z), dX = dz W1^T
+    dz_all, dx_all, z_all = [], [], []
+    for e in range(2):
+        a, b = off[e], off[e + 1]
+        z = x[a:b] @ w1[e] + b1[e]
+        G = dy2[a:b] @ w2[e].T
+        dz = O.dglu(G, z, ep)
+        dz_all.append(dz)
+        dx_all.append(dz @ w1[e].T)
+        z_all.append(z)
+    dX = np.concatenate(dx_all)
+
+    # finite differences on X
+    checked = 0
+    for t in range(x.shape[0]):
+        for hh in range(x.shape[1]):
+            h = 1e-6 * max(1.0, abs(x[t, hh]))
+            xp, xm = x.copy(), x.copy()
+            xp[t, hh] += h
+            xm[t, hh] -= h
+            # skip points whose perturbation crosses a clamp bound or the srelu kink
+            e = int(np.searchsorted(off, t, side="right") - 1)
+            z = x[t] @ w1[e] + b1[e]
+            dzmax = 2 * h * np.max(np.abs(w1[e][hh]))
+            I = z.shape[0] // 2
+            bounds = [ep.gate_lo, ep.gate_hi]
+            near = np.any([np.any(np.abs(z[:I] - bd) <= 2 * dzmax) for bd in bounds if np.isfinite(bd)])
+            near |= np.any([np.any(np.abs(z[I:] - bd) <= 2 * dzmax) for bd in (ep.up_lo, ep.up_hi) if np.isfinite(bd)])
+            if act == "srelu":
+                near |= np.any(np.abs(z[:I]) <= 2 * dzmax)
+            if near:
+                continue
+            fd = (_loss(xp, counts, w1, b1, w2, dy2, ep) - _loss(xm, counts, w1, b1, w2, dy2, ep)) / (2 * h)
+            assert abs(fd - dX[t, hh]) <= 1e-6 * max(1.0, abs(fd)), (t, hh, fd, dX[t, hh])
+            checked += 1
+    assert checked >= 16
+
+
+def test_dgrad_dglu_and_dx_bf16_functions_match_f64_chain():
+    """The bf16-rounding oracle functions equal the float64 chain above up to
+    the final bf16 rounding of each output."""
+    rng = np.random.default_rng(22)
+    E, H, I = 3, 32, 64
+    counts = np.array([5, 0, 9])
+    M = 14
+    dy2 = W.to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    w2 = W.to_bf16_bits(rng.standard_normal((E, I, H)).astype(np.float32) * 0.2)
+    w1 = W.to_bf16_bits(rng.standard_normal((E, H, 2 * I)).astype(np.float32) * 0.2)
+    pre = W.to_bf16_bits(rng.standard_normal((M, 2 * I)).astype(np.float32))
+    ep = O.Epilogue(alpha=1.702, gate_lo=-7, gate_hi=7, up_lo=-7, up_hi=7)
+    dgu = O.dgrad_dglu(dy2, counts, w2, pre, ep)
+    off = [0, 5, 5, 14]
+    for e in (0, 2):
+        a, b = off[e], off[e + 1]
+        G = F.bf16_bits_to_f64(dy2[a:b]) @ F.bf16_bits_to_f64(w2[e]).T
+        want = O.dglu(G, F.bf16_bits_to_f64(pre[a:b]), ep)
+        assert np.array_equal(dgu[a:b], F.f64_to_bf16_bits(want))
+    dX = O.dx(dgu, counts, w1)
+    for e in (0, 2):
+        a, b = off[e], off[e + 1]
+        want = F.bf16_bits_to_f64(dgu[a:b]) @ F.bf16_bits_to_f64(w1[e]).T
+        assert np.array_equal(dX[a:b], F.f64_to_bf16_bits(want))
+
+
+# ------------------------------------------------------------------ GEMM, integer-exact
+def test_group_gemm_integer_exact_against_loops():
+    E, K, N = 3, 40, 24
+    counts = np.array([4, 0, 6])
+    a = W.ternary_bf16(1, (10, K))
+    b = np.stack([W.ternary_bf16(2 + e, (K, N)) for e in range(E)])
+    out = O.group_gemm(a, counts, b)
+    af, bf = F.bf16_bits_to_f64(a), F.bf16_bits_to_f64(b)
+    off = [0, 4, 4, 10]
+    for e in range(E):
+        for r in range(off[e], off[e + 1]):
+            for n in range(N):
+                s = 0.0
+                for k in range(K):
+                    s += af[r, k] * bf[e, k, n]
+                assert F.bf16_bits_to_f64(out[r:r + 1, n:n + 1])[0, 0] == s
+
+
+# ------------------------------------------------------------------ MXFP8 rows / cols
+def test_mx_rows_scale_rule_and_bound():
+    rng = np.random.default_rng(30)
+    v = W.to_bf16_bits((rng.standard_t(3, size=(7, 96)) * 0.5).astype(np.float32))
+    q, s = O.mx_quantize_rows(v)
+    vf = F.bf16_bits_to_f64(v)
+    deq = O.mx_dequantize_rows(q, s)
+    for r in range(7):
+        for cb in range(3):
+            blk = vf[r, 32 * cb:32 * cb + 32]
+            X = 2.0 ** (int(s[r, cb]) - 127)
+            amax = np.max(np.abs(blk))
+            assert amax / X <= 448 and (amax == 0 or amax / (X / 2) > 448)
+            assert np.all(np.abs(deq[r, 32 * cb:32 * cb + 32] - blk) <= 0.5 * F.e4m3_ulp(blk / X) * X)
+
+
+def test_mx_cols_restart_per_group_and_match_rows_of_transpose():
+    rng = np.random.default_rng(31)
+    counts = np.array([64, 0, 37, 5])
+    M = int(counts.sum())
+    m_cap = M + 11
+    C = 64
+    v = W.to_bf16_bits(rng.standard_normal((m_cap, C)).astype(np.float32))
+    col_q, col_s = O.mx_quantize_cols(v[:M], counts, m_cap=m_cap)
+    assert col_q.shape == (C, m_cap) and col_s.shape == (C, (m_cap + 31) // 32 + 4)
+    so = O.mx_scale_col_offsets(counts)
+    assert so.tolist() == [0, 2, 2, 4, 5]
+    # group 0 has two full blocks: equals the row-wise quantisation of its transpose
+    q0, s0 = O.mx_quantize_rows(np.ascontiguousarray(v[0:64].T))
+    assert np.array_equal(col_q[:, 0:64], q0) and np.array_equal(col_s[:, 0:2], s0)
+    # group 2 (rows 64..100): a full block then a partial 5-row block; group 3 partial
+    vf = F.bf16_bits_to_f64(v)
+    for (r0, r1, sc) in [(64, 96, 2), (96, 101, 3), (101, 106, 4)]:
+        for c in range(C):
+            blk = vf[r0:r1, c]
+            X = 2.0 ** (int(col_s[c, sc]) - 127)
+            assert np.max(np.abs(blk)) / X <= 448
+            assert np.max(np.abs(blk)) == 0 or np.max(np.abs(blk)) / (X / 2) > 448
+            deq = F.e4m3_decode(col_q[c, r0:r1]) * X
+            assert np.all(np.abs(deq - blk) <= 0.5 * F.e4m3_ulp(blk / X) * X)
+    # rows beyond M are never written
+    assert np.all(col_q[:, M:] == 0)
+
+
+def test_group_gemm_mx_against_loops():
+    rng = np.random.default_rng(32)
+    E, K, N = 2, 64, 8
+    counts = np.array([3, 2])
+    a = W.to_bf16_bits(rng.standard_normal((5, K)).astype(np.float32))
+    aq, as_ = O.mx_quantize_rows(a)
+    bw = W.to_bf16_bits(rng.standard_normal((E, N, K)).astype(np.float32))
+    bq = np.zeros((E, N, K), np.uint8)
+    bs = np.zeros((E, N, K // 32), np.uint8)
+    for e in range(E):
+        bq[e], bs[e] = O.mx_quantize_rows(bw[e])
+    out = O.group_gemm_mx(aq, as_, counts, bq, bs)
+    off = [0, 3, 5]
+    for e in range(E):
+        for r in range(off[e], off[e + 1]):
+            for n in range(N):
+                s = 0.0
+                for k in range(K):
+                    xa = F.e4m3_decode(aq[r, k]) * 2.0 ** (int(as_[r, k // 32]) - 127)
+                    xb = F.e4m3_decode(bq[e, n, k]) * 2.0 ** (int(bs[e, n, k // 32]) - 127)
+                    s += xa * xb
+                assert out[r, n] == F.f64_to_bf16_bits(np.array([s]))[0]
