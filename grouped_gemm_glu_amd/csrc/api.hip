@@ -1,0 +1,339 @@
+// C ABI of the MoE GroupGEMM + GLU library: argument checking, the cached
+// device properties and the launches.  Every entry point validates what the
+// host can see and returns before any launch on error; nothing here
+// allocates, synchronises or reads device memory back.
+#include <math.h>
+#include <string.h>
+
+#include "aux_kernels.hpp"
+#include "internal.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_num_cus[kMaxDevices];  // 0 = not initialised
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+moe_status_t ensure_init(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  if (g_num_cus[dev] == 0) {
+    moe_status_t st = moe_init(dev);
+    if (st != MOE_OK) return st;
+  }
+  *cus = g_num_cus[dev];
+  return MOE_OK;
+}
+
+moe_status_t check_groups(const moe_groups_t* g) {
+  if (!g || !g->counts) return MOE_ERR_NULL;
+  if (g->E < 1 || g->E > kMaxExperts || g->M_cap < 0) return MOE_ERR_SHAPE;
+  if (!aligned4(g->counts) || (g->offsets_out && !aligned4(g->offsets_out)) ||
+      (g->status_out && !aligned4(g->status_out)))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+moe_status_t check_mx(const moe_mx_out_t* mx) {
+  if (!mx) return MOE_OK;
+  if ((mx->row_q == nullptr) != (mx->row_s == nullptr)) return MOE_ERR_NULL;
+  if ((mx->col_q == nullptr) != (mx->col_s == nullptr)) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+moe_status_t fill_epilogue(const moe_epilogue_t* ep, EpiParams* out) {
+  if (!ep) return MOE_ERR_NULL;
+  if (ep->act < MOE_ACT_SWIGLU || ep->act > MOE_ACT_SRELU) return MOE_ERR_UNSUPPORTED;
+  if (ep->bias && !aligned16(ep->bias)) return MOE_ERR_ALIGN;
+  if (ep->row_scale && !aligned4(ep->row_scale)) return MOE_ERR_ALIGN;
+  if (isnan(ep->alpha) || isnan(ep->gate_lo) || isnan(ep->gate_hi) || isnan(ep->up_lo) ||
+      isnan(ep->up_hi) || isnan(ep->up_offset))
+    return MOE_ERR_SHAPE;
+  out->act = ep->act;
+  out->alpha = ep->alpha;
+  out->gate_lo = ep->gate_lo;
+  out->gate_hi = ep->gate_hi;
+  out->up_lo = ep->up_lo;
+  out->up_hi = ep->up_hi;
+  out->up_offset = ep->up_offset;
+  out->bias = static_cast<const uint16_t*>(ep->bias);
+  out->row_scale = ep->row_scale;
+  return MOE_OK;
+}
+
+void fill_groups(GemmArgs* a, const moe_groups_t* g) {
+  a->counts = g->counts;
+  a->E = g->E;
+  a->M_cap = g->M_cap;
+  a->offsets_out = g->offsets_out;
+  a->status_out = g->status_out;
+}
+
+void fill_mx(GemmArgs* a, const moe_mx_out_t* mx, int cols, const moe_groups_t* g) {
+  a->row_q = mx ? mx->row_q : nullptr;
+  a->row_s = mx ? mx->row_s : nullptr;
+  a->col_q = mx ? mx->col_q : nullptr;
+  a->col_s = mx ? mx->col_s : nullptr;
+  a->mx_cols = cols;
+  a->col_s_ld = (g->M_cap + 31) / 32 + g->E;
+}
+
+// Persistent grid: one workgroup per usable CU (the kernel holds a CU's LDS),
+// capped by an upper bound on the tile count (each expert adds at most one
+// partial m-tile).
+int persistent_grid(int cus, int cu_margin, int M_cap, int E, int ntiles_n) {
+  int usable = cus - (cu_margin > 0 ? cu_margin : 0);
+  if (usable < 1) usable = 1;
+  long long bound = ((long long)(M_cap + GM_BM - 1) / GM_BM + E) * ntiles_n;
+  if (bound < 1) bound = 1;
+  return (int)(bound < usable ? bound : usable);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return MOE_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MOE_ERR_DEVICE;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
+  g_num_cus[device] = prop.multiProcessorCount;
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or not a supported multiple";
+    case MOE_ERR_ALIGN: return "a pointer is not suitably aligned";
+    case MOE_ERR_UNSUPPORTED: return "unsupported option combination";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_DEVICE: return "no usable gfx950 device";
+  }
+  return "unknown status";
+}
+
+size_t moe_packed_w1_bytes(int E, int H, int I) {
+  if (E <= 0 || H <= 0 || I <= 0) return 0;
+  return (size_t)E * 2 * (size_t)I * (size_t)H * 2;
+}
+
+static moe_status_t repack_common(const void* src, int E, int H, int I, void* dst, void* stream,
+                                  int unpack) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (E < 1 || H < 1 || I < 64 || I % 64 != 0 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  int cus;
+  moe_status_t st = ensure_init(&cus);
+  if (st != MOE_OK) return st;
+  dim3 grid(2 * I / 64, (H + 63) / 64, E);
+  hipLaunchKernelGGL(repack_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), H, I, unpack);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status_t moe_repack_gate_up(const void* w1, int E, int H, int I, void* w1_packed,
+                                void* stream) {
+  return repack_common(w1, E, H, I, w1_packed, stream, 0);
+}
+
+moe_status_t moe_unpack_gate_up(const void* w1_packed, int E, int H, int I, void* w1,
+                                void* stream) {
+  return repack_common(w1_packed, E, H, I, w1, stream, 1);
+}
+
+moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T, int E, int k,
+                             int32_t* topk_ids_out, int32_t* counts, int32_t* offsets,
+                             int32_t* dst, int32_t* src, const void* x, int H, void* xg,
+                             void* stream) {
+  if ((logits == nullptr) == (topk_ids == nullptr)) return MOE_ERR_NULL;
+  if (!topk_ids_out || !counts || !offsets || !dst || !src) return MOE_ERR_NULL;
+  if ((x == nullptr) != (xg == nullptr)) return MOE_ERR_NULL;
+  if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > 16 || k > E) return MOE_ERR_SHAPE;
+  if ((long long)T * k >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (x && (H < 8 || H % 8 != 0)) return MOE_ERR_SHAPE;
+  if (x && (!aligned16(x) || !aligned16(xg))) return MOE_ERR_ALIGN;
+  int cus;
+  moe_status_t st = ensure_init(&cus);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int TK = T * k;
+  if (logits) {
+    if (T > 0)
+      hipLaunchKernelGGL(topk_kernel, dim3((T + 255) / 256), dim3(256), 0, s, logits, T, E, k,
+                         topk_ids_out);
+  } else if (topk_ids != topk_ids_out && TK > 0) {
+    if (hipMemcpyAsync(topk_ids_out, topk_ids, (size_t)TK * 4, hipMemcpyDeviceToDevice, s) !=
+        hipSuccess)
+      return MOE_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, topk_ids_out, TK, k, E, counts,
+                     offsets, dst, src);
+  if (x && TK > 0) {
+    long long chunks = (long long)TK * (H / 8);
+    long long blocks = (chunks + 255) / 256;
+    int grid = (int)(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(x), src, TK, H, static_cast<uint16_t*>(xg));
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
+                                    const void* w1_packed, int H, int I,
+                                    const moe_epilogue_t* ep, void* y, void* preact,
+                                    const moe_mx_out_t* mx, int cu_margin, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!xg || !w1_packed || !ep) return MOE_ERR_NULL;
+  if ((st = check_mx(mx)) != MOE_OK) return st;
+  if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (ep->gated != 1) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(xg) || !aligned16(w1_packed) || (y && !aligned16(y)) ||
+      (preact && !aligned16(preact)))
+    return MOE_ERR_ALIGN;
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = fill_epilogue(ep, &a.ep)) != MOE_OK) return st;
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  fill_groups(&a, groups);
+  a.A = static_cast<const uint16_t*>(xg);
+  a.B = static_cast<const uint16_t*>(w1_packed);
+  a.b_estride = 2LL * I * H;
+  a.ldb = H;
+  a.N = 2 * I;
+  a.K = H;
+  a.I = I;
+  a.C = static_cast<uint16_t*>(y);
+  a.preact = static_cast<uint16_t*>(preact);
+  fill_mx(&a, mx, I, groups);
+  a.ntiles_n = (2 * I + GM_BN - 1) / GM_BN;
+  int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
+  return launch_group_gemm_fwd(EPI_GLU, BL_NK, a, grid, (hipStream_t)stream);
+}
+
+moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const void* w2, int H, int I,
+                                     const moe_groups_t* groups, const void* preact,
+                                     const moe_epilogue_t* ep, void* dgu,
+                                     const moe_mx_out_t* mx, int cu_margin, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!dy2 || !w2 || !preact || !ep) return MOE_ERR_NULL;
+  if ((st = check_mx(mx)) != MOE_OK) return st;
+  if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (ep->gated != 1) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(dy2) || !aligned16(w2) || !aligned16(preact) || (dgu && !aligned16(dgu)))
+    return MOE_ERR_ALIGN;
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = fill_epilogue(ep, &a.ep)) != MOE_OK) return st;
+  a.ep.bias = nullptr;
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  fill_groups(&a, groups);
+  a.A = static_cast<const uint16_t*>(dy2);
+  a.B = static_cast<const uint16_t*>(w2);  // W2_e [I][H] = (W2_e^T stored [N=I][K=H])
+  a.b_estride = (long long)I * H;
+  a.ldb = H;
+  a.N = I;
+  a.K = H;
+  a.I = I;
+  a.C = static_cast<uint16_t*>(dgu);
+  a.preact = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
+  fill_mx(&a, mx, 2 * I, groups);
+  a.ntiles_n = (I + GM_BN - 1) / GM_BN;
+  int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
+  return launch_group_gemm_bwd(EPI_DGLU, BL_NK, a, grid, (hipStream_t)stream);
+}
+
+moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t* b_op, int N,
+                                  int K, const moe_groups_t* groups, void* c_bf16,
+                                  const moe_mx_out_t* mx, int cu_margin, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!a_op || !b_op || !a_op->data || !b_op->data) return MOE_ERR_NULL;
+  if ((st = check_mx(mx)) != MOE_OK) return st;
+  if (N < 64 || N % 64 != 0 || K < 64 || K % 64 != 0) return MOE_ERR_SHAPE;
+  if (a_op->dtype != MOE_DT_BF16 || b_op->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(a_op->data) || !aligned16(b_op->data) || (c_bf16 && !aligned16(c_bf16)))
+    return MOE_ERR_ALIGN;
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  fill_groups(&a, groups);
+  a.A = static_cast<const uint16_t*>(a_op->data);
+  a.B = static_cast<const uint16_t*>(b_op->data);
+  a.N = N;
+  a.K = K;
+  a.C = static_cast<uint16_t*>(c_bf16);
+  fill_mx(&a, mx, N, groups);
+  a.ntiles_n = (N + GM_BN - 1) / GM_BN;
+  int blay;
+  switch (b_op->layout) {
+    case MOE_B_KN: blay = BL_KN; a.ldb = N; a.b_estride = (long long)K * N; break;
+    case MOE_B_NK: blay = BL_NK; a.ldb = K; a.b_estride = (long long)N * K; break;
+    case MOE_B_W1_PACKED_T:
+      if (K % 128 != 0) return MOE_ERR_SHAPE;
+      blay = BL_W1T; a.ldb = N; a.I = K / 2; a.b_estride = (long long)K * N; break;
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+  int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
+  if (blay == BL_W1T) return launch_group_gemm_bwd(EPI_STORE, blay, a, grid, (hipStream_t)stream);
+  return launch_group_gemm_fwd(EPI_STORE, blay, a, grid, (hipStream_t)stream);
+}
+
+moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
+                             const moe_epilogue_t* ep, void* y, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!z || !y || !ep) return MOE_ERR_NULL;
+  if (I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (ep->gated != 1) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(z) || !aligned16(y)) return MOE_ERR_ALIGN;
+  EpiParams e;
+  if ((st = fill_epilogue(ep, &e)) != MOE_OK) return st;
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  hipLaunchKernelGGL(glu_unfused_kernel, dim3(cus * 8), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(z), groups->counts, groups->E, groups->M_cap, I,
+                     e, static_cast<uint16_t*>(y));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status_t moe_mxfp8_quantize(const void* v, int R, int C, const moe_groups_t* groups,
+                                const moe_mx_out_t* mx, void* stream) {
+  if (!v || !mx) return MOE_ERR_NULL;
+  moe_status_t st = check_mx(mx);
+  if (st != MOE_OK) return st;
+  if (groups && (st = check_groups(groups)) != MOE_OK) return st;
+  if (groups && groups->M_cap != R) return MOE_ERR_SHAPE;
+  if (R < 0 || C < 32 || C % 32 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(v)) return MOE_ERR_ALIGN;
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int* counts = groups ? groups->counts : nullptr;
+  const int E = groups ? groups->E : 0;
+  if (mx->row_q && R > 0) {
+    hipLaunchKernelGGL(mx_rows_kernel, dim3(cus * 8), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(v), R, C, counts, E, mx->row_q, mx->row_s);
+  }
+  if (mx->col_q && R > 0) {
+    int s_ld = (R + 31) / 32 + (groups ? E : 0);
+    long long by = (long long)(R + 31) / 32 + E;
+    int gy = (int)(by < 65535 ? by : 65535);
+    hipLaunchKernelGGL(mx_cols_kernel, dim3((C + 255) / 256, gy), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(v), R, C, counts, E, mx->col_q, mx->col_s, s_ld);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+}  // extern "C"

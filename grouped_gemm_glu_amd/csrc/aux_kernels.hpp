@@ -1,0 +1,327 @@
+// Memory-bound kernels around the grouped GEMM: the offline gate/up repack,
+// device routing and grouping, the unfused GLU pass and the standalone MXFP8
+// quantize/transpose.  All are bandwidth kernels: 16-byte coalesced accesses,
+// LDS only where a transpose needs it.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------- repack
+// Packed row of plain FC1 column j ("Boosting MoE Training Throughput…",
+// section "Optimizando GLU…", Figure 2: one tile holds half a tile width of the
+// gate and of the input/up columns).  128-row block p = gate columns 64p..64p+63
+// then up columns I+64p..I+64p+63.
+__device__ __forceinline__ int packed_row_of(int j, int I) {
+  int up = j >= I;
+  int c = up ? j - I : j;
+  return (c >> 6) * 128 + (up ? 64 : 0) + (c & 63);
+}
+
+// W1 [E][H][2I] -> W1p [E][2I][H].  Block = 64 (h) x 64 (j) transpose through
+// LDS; grid (2I/64, ceil(H/64), E), 256 threads.
+__global__ __launch_bounds__(256) void repack_kernel(const uint16_t* __restrict__ w1,
+                                                     uint16_t* __restrict__ w1p, int H, int I,
+                                                     int unpack) {
+  __shared__ uint16_t tile[64][66];
+  const int N2 = 2 * I;
+  const int j0 = blockIdx.x * 64, h0 = blockIdx.y * 64, e = blockIdx.z;
+  const uint16_t* src = w1 + (long long)e * H * N2;
+  uint16_t* dst = w1p + (long long)e * H * N2;
+  const int t = threadIdx.x;
+  if (!unpack) {
+    // read 64 rows h x 64 plain columns j (128 B per row), write 64 packed rows x 64 h
+    for (int i = t; i < 64 * 8; i += 256) {
+      int r = i >> 3, ch = i & 7;
+      int h = h0 + r;
+      if (h < H) {
+        uint4 v = *reinterpret_cast<const uint4*>(src + (long long)h * N2 + j0 + ch * 8);
+        const uint16_t* pv = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tile[r][ch * 8 + q] = pv[q];
+      }
+    }
+    __syncthreads();
+    for (int i = t; i < 64 * 64; i += 256) {
+      int jj = i >> 6, hh = i & 63;
+      int h = h0 + hh;
+      if (h < H) dst[(long long)packed_row_of(j0 + jj, I) * H + h] = tile[hh][jj];
+    }
+  } else {
+    // read 64 packed rows (of plain columns j0..j0+63) x 64 h, write plain [h][j]
+    for (int i = t; i < 64 * 64; i += 256) {
+      int jj = i >> 6, hh = i & 63;
+      int h = h0 + hh;
+      if (h < H) tile[hh][jj] = src[(long long)packed_row_of(j0 + jj, I) * H + h];
+    }
+    __syncthreads();
+    for (int i = t; i < 64 * 8; i += 256) {
+      int r = i >> 3, ch = i & 7;
+      int h = h0 + r;
+      if (h < H) {
+        uint4 v;
+        uint16_t* pv = reinterpret_cast<uint16_t*>(&v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) pv[q] = tile[r][ch * 8 + q];
+        *reinterpret_cast<uint4*>(dst + (long long)h * N2 + j0 + ch * 8) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- routing
+// Top-k of one token's logits ([MEGA] §2.1), ties to the lower expert id:
+// a candidate enters when it beats the current k-th entry, or equals it with a
+// lower id.  One thread per token.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int* __restrict__ ids_out) {
+  int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float val[16];
+  int id[16];
+  for (int j = 0; j < 16; ++j) { val[j] = -INFINITY; id[j] = 0x7FFFFFFF; }
+  const float* lg = logits + (long long)t * E;
+  for (int e = 0; e < E; ++e) {
+    float v = lg[e];
+    bool better = (v > val[k - 1]) || (v == val[k - 1] && e < id[k - 1]);
+    if (!better) continue;
+    int pos = k - 1;
+    while (pos > 0 && ((v > val[pos - 1]) || (v == val[pos - 1] && e < id[pos - 1]))) {
+      val[pos] = val[pos - 1];
+      id[pos] = id[pos - 1];
+      --pos;
+    }
+    val[pos] = v;
+    id[pos] = e;
+  }
+  for (int j = 0; j < k; ++j) ids_out[(long long)t * k + j] = id[j];
+}
+
+// Counting sort of the T*k (token, slot) pairs by expert, stable in (t, j)
+// order ([MEGA] §4.3: rows for one expert contiguous).  One workgroup of 1024
+// threads: LDS histogram, exclusive scan, then each wave ranks the pairs of
+// its experts with ballots (order-independent of scheduling, so bit-exact).
+__global__ __launch_bounds__(1024) void group_kernel(const int* __restrict__ ids, int TK, int k,
+                                                     int E, int* __restrict__ counts,
+                                                     int* __restrict__ offsets,
+                                                     int* __restrict__ dst, int* __restrict__ src) {
+  __shared__ int hist[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  const int t = threadIdx.x;
+  for (int e = t; e < E; e += 1024) hist[e] = 0;
+  __syncthreads();
+  for (int p = t; p < TK; p += 1024) {
+    int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) { off[e] = run; run += hist[e]; }
+    off[E] = run;
+  }
+  __syncthreads();
+  for (int e = t; e < E; e += 1024) counts[e] = hist[e];
+  for (int e = t; e <= E; e += 1024) offsets[e] = off[e];
+  const int lane = t & 63, wave = t >> 6;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int e = wave; e < E; e += 16) {
+    int base = off[e];
+    for (int c = 0; c < TK; c += 64) {
+      int p = c + lane;
+      bool m = p < TK && ids[p] == e;
+      unsigned long long mask = __ballot(m);
+      if (m) {
+        int r = base + __popcll(mask & below);
+        dst[p] = r;
+        src[r] = p / k;
+      }
+      base += __popcll(mask);
+    }
+  }
+}
+
+// xg[r] = x[src[r]]: one 16-byte chunk per thread.
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ x,
+                                                     const int* __restrict__ src, int R, int H,
+                                                     uint16_t* __restrict__ xg) {
+  const int cpr = H >> 3;
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  long long total = (long long)R * cpr;
+  for (; i < total; i += (long long)gridDim.x * blockDim.x) {
+    int r = (int)(i / cpr), ch = (int)(i - (long long)r * cpr);
+    int s = src[r];
+    *reinterpret_cast<uint4*>(xg + (long long)r * H + ch * 8) =
+        *reinterpret_cast<const uint4*>(x + (long long)s * H + ch * 8);
+  }
+}
+
+// ---------------------------------------------------------------- unfused GLU
+// y = GLU epilogue of the plain-order FC1 output z [M_cap][2I] (+ bias), one
+// 8-column chunk per thread per step; rows beyond the groups are skipped.
+// Each workgroup scans the counts to find row ranges and experts.
+__global__ __launch_bounds__(256) void glu_unfused_kernel(const uint16_t* __restrict__ z,
+                                                          const int* __restrict__ counts, int E,
+                                                          int M_cap, int I, EpiParams ep,
+                                                          uint16_t* __restrict__ y) {
+  __shared__ GroupScan gs;
+  build_group_scan<256>(gs, counts, E, M_cap, 1, nullptr, nullptr, false);
+  const int M = gs.row_off[E];
+  const int cpr = I >> 3;
+  long long total = (long long)M * cpr;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (long long)gridDim.x * 256) {
+    int r = (int)(i / cpr), ch = (int)(i - (long long)r * cpr);
+    const uint16_t* zr = z + (long long)r * 2 * I;
+    uint4 gv = *reinterpret_cast<const uint4*>(zr + ch * 8);
+    uint4 uv = *reinterpret_cast<const uint4*>(zr + I + ch * 8);
+    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(&gv);
+    const uint16_t* u16 = reinterpret_cast<const uint16_t*>(&uv);
+    float bg[8] = {0, 0, 0, 0, 0, 0, 0, 0}, bu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (ep.bias) {
+      int lo = 0, hi = E;  // expert of row r: last e with row_off[e] <= r and rows in it
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (gs.row_off[mid] <= r) lo = mid; else hi = mid;
+      }
+      const uint16_t* b = ep.bias + (long long)lo * 2 * I;
+      uint4 bgv = *reinterpret_cast<const uint4*>(b + ch * 8);
+      uint4 buv = *reinterpret_cast<const uint4*>(b + I + ch * 8);
+      const uint16_t* bg16 = reinterpret_cast<const uint16_t*>(&bgv);
+      const uint16_t* bu16 = reinterpret_cast<const uint16_t*>(&buv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { bg[q] = bf16_to_f32(bg16[q]); bu[q] = bf16_to_f32(bu16[q]); }
+    }
+    float rs = ep.row_scale ? ep.row_scale[r] : 1.0f;
+    uint4 out;
+    uint16_t* o16 = reinterpret_cast<uint16_t*>(&out);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float g = bf16_to_f32(g16[q]) + bg[q];
+      float u = bf16_to_f32(u16[q]) + bu[q];
+      float gc = fminf(fmaxf(g, ep.gate_lo), ep.gate_hi);
+      float uc = fminf(fmaxf(u, ep.up_lo), ep.up_hi) + ep.up_offset;
+      float v = act_fwd(ep.act, gc, ep.alpha) * uc;
+      if (ep.row_scale) v *= rs;
+      o16[q] = f32_to_bf16(v);
+    }
+    *reinterpret_cast<uint4*>(y + (long long)r * I + ch * 8) = out;
+  }
+}
+
+// ---------------------------------------------------------------- MXFP8 quantize
+__device__ __forceinline__ uint8_t mx_block_quant(const float* v, int nvalid, uint32_t* w) {
+  float amax = 0.0f;
+  bool has_nan = false;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (i < nvalid) {
+      amax = fmaxf(amax, fabsf(v[i]));
+      if (v[i] != v[i]) has_nan = true;
+    }
+  int E = has_nan ? 128 : mx_scale_exponent(amax);
+  if (E == 128) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0x7F7F7F7Fu;
+    return 0xFF;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t q = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q |= f32_to_e4m3(ldexpf(v[4 * i + j], -E)) << (8 * j);
+    w[i] = q;
+  }
+  return e8m0_byte(E);
+}
+
+__device__ __forceinline__ void store_q32(uint8_t* dst, const uint32_t* w, int nvalid) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+  if (nvalid == 32 && (a & 15) == 0) {
+    uint4* d = reinterpret_cast<uint4*>(dst);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    for (int i = 0; i < nvalid; ++i) dst[i] = static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3)));
+  }
+}
+
+// Row-wise: one thread per (row, 32-column block) over rows [0, R_used).
+__global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ v, int R, int C,
+                                                      const int* __restrict__ counts, int E,
+                                                      uint8_t* __restrict__ q,
+                                                      uint8_t* __restrict__ s) {
+  __shared__ GroupScan gs;
+  int Ruse = R;
+  if (counts) {
+    build_group_scan<256>(gs, counts, E, R, 1, nullptr, nullptr, false);
+    Ruse = gs.row_off[E];
+  }
+  const int nb = C >> 5;
+  long long total = (long long)Ruse * nb;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (long long)gridDim.x * 256) {
+    int r = (int)(i / nb), cb = (int)(i - (long long)r * nb);
+    const uint4* src = reinterpret_cast<const uint4*>(v + (long long)r * C + cb * 32);
+    float x[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 u = src[c];
+      uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * c + 2 * j] = __uint_as_float(ww[j] << 16);
+        x[8 * c + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+      }
+    }
+    uint32_t w[8];
+    uint8_t sb = mx_block_quant(x, 32, w);
+    store_q32(q + (long long)r * C + cb * 32, w, 32);
+    s[(long long)r * nb + cb] = sb;
+  }
+}
+
+// Column-wise: one thread per (column, 32-row block); blocks restart at each
+// group's first row (with counts) or run over all R rows (without).  Grid.y
+// walks blocks; grid.x covers columns in 256-column chunks.
+__global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict__ v, int R, int C,
+                                                      const int* __restrict__ counts, int E,
+                                                      uint8_t* __restrict__ q,
+                                                      uint8_t* __restrict__ s, int s_ld) {
+  __shared__ GroupScan gs;
+  int nblocks;
+  if (counts) {
+    build_group_scan<256>(gs, counts, E, R, 1, nullptr, nullptr, false);
+    nblocks = gs.mxs_off[E];
+  } else {
+    nblocks = (R + 31) >> 5;
+  }
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  for (int b = blockIdx.y; b < nblocks; b += gridDim.y) {
+    int r0, nvalid;
+    if (counts) {
+      int lo = 0, hi = E;  // group owning scale column b: last e with mxs_off[e] <= b
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (gs.mxs_off[mid] <= b) lo = mid; else hi = mid;
+      }
+      int blk = b - gs.mxs_off[lo];
+      r0 = gs.row_off[lo] + blk * 32;
+      nvalid = min(32, gs.row_off[lo + 1] - r0);
+    } else {
+      r0 = b * 32;
+      nvalid = min(32, R - r0);
+    }
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = (i < nvalid) ? bf16_to_f32(v[(long long)(r0 + i) * C + c]) : 0.0f;
+    uint32_t w[8];
+    uint8_t sb = mx_block_quant(x, nvalid, w);
+    store_q32(q + (long long)c * R + r0, w, nvalid);
+    s[(long long)c * s_ld + b] = sb;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,245 @@
+// Device helpers shared by the library's kernels (gfx950 / CDNA4, wave64):
+// bf16 and e4m3fn encoders, the E8M0 block-scale rule, the GLU activations and
+// their derivatives, and the per-workgroup scan of the device-resident expert
+// counts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMxBlock = 32;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even.  Overflow rounds to +-inf,
+// NaN becomes the quiet NaN 0x7FC0 (sign kept).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ---------------------------------------------------------------- MXFP8
+// Block-scale exponent for a block maximum (OCP MX, E8M0 scale): the smallest
+// E with amax / 2^E <= 448 (the largest e4m3fn value, 1.75 * 2^8), clamped to
+// [-127, 127]; an all-zero block gives -127; a non-finite amax gives 128 (the
+// NaN scale byte 0xFF).  With amax = 1.m * 2^e, amax <= 1.75 * 2^(E+8) holds
+// for E = e - 8 exactly when the mantissa fraction is <= 0.75.
+__device__ __forceinline__ int mx_scale_exponent(float amax) {
+  uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
+  if (u >= 0x7F800000u) return 128;
+  uint32_t ebits = u >> 23;
+  if (ebits == 0) return -127;                 // zero or subnormal: ceil(log2(amax/448)) < -127
+  int E = static_cast<int>(ebits) - 127 - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+__device__ __forceinline__ uint8_t e8m0_byte(int E) {
+  return E >= 128 ? static_cast<uint8_t>(0xFF) : static_cast<uint8_t>(E + 127);
+}
+
+// fp32 -> e4m3fn code, round to nearest, ties to even, saturating at 448; the
+// sign bit is kept (also on zero).  Integer arithmetic on the fp32 bits: the
+// three kept mantissa bits are rounded on the 20 dropped ones; below 2^-6 the
+// value is a multiple of the subnormal quantum 2^-9, rounded by rintf (RNE).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;    // NaN
+  uint32_t code;
+  if (a < 0x3C800000u) {                       // |x| < 2^-6
+    code = static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.0f));  // 0..8, 8 == 2^-6
+  } else {
+    uint32_t e = (a >> 23) - 120u;             // biased e4m3 exponent (bias 7)
+    uint32_t keep = (a >> 20) & 7u;
+    uint32_t rem = a & 0xFFFFFu;
+    uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (keep & 1u));
+    code = (e << 3) + keep + up;
+    if (code > 0x7Eu || e > 15u) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
+// ---------------------------------------------------------------- activations
+enum { ACT_SWIGLU = 0, ACT_GEGLU = 1, ACT_GEGLU_TANH = 2, ACT_SRELU = 3 };
+
+__device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ float act_fwd(int act, float g, float alpha) {
+  switch (act) {
+    case ACT_SWIGLU: return g * sigmoidf_fast(alpha * g);
+    case ACT_GEGLU: return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+    case ACT_GEGLU_TANH: {
+      float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
+      return 0.5f * g * (1.0f + tanhf(u));
+    }
+    default: { float r = fmaxf(g, 0.0f); return r * r; }
+  }
+}
+
+// a(g) and a'(g) together (the backward epilogue needs both).
+__device__ __forceinline__ void act_fwd_bwd(int act, float g, float alpha, float& a, float& da) {
+  switch (act) {
+    case ACT_SWIGLU: {
+      float s = sigmoidf_fast(alpha * g);
+      a = g * s;
+      da = s * (1.0f + alpha * g * (1.0f - s));
+      break;
+    }
+    case ACT_GEGLU: {
+      float cdf = 0.5f * (1.0f + erff(g * 0.70710678118654752f));
+      float pdf = 0.39894228040143268f * __expf(-0.5f * g * g);
+      a = g * cdf;
+      da = cdf + g * pdf;
+      break;
+    }
+    case ACT_GEGLU_TANH: {
+      float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
+      float t = tanhf(u);
+      float du = 0.79788456080286536f * (1.0f + 3.0f * 0.044715f * g * g);
+      a = 0.5f * g * (1.0f + t);
+      da = 0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * du;
+      break;
+    }
+    default: {
+      float r = fmaxf(g, 0.0f);
+      a = r * r;
+      da = 2.0f * r;
+      break;
+    }
+  }
+}
+
+struct EpiParams {
+  int act;
+  float alpha;
+  float gate_lo, gate_hi, up_lo, up_hi, up_offset;
+  const uint16_t* bias;      // plain [E][2I] or null
+  const float* row_scale;    // [M_cap] or null
+};
+
+// ---------------------------------------------------------------- group scan
+// Per-workgroup view of the device-resident expert counts.  Every workgroup
+// rebuilds it in LDS at kernel start (E <= 1024, a few hundred cycles), so no
+// extra launch and no host readback is needed.  Counts are clamped: negative
+// counts become 0 (status bit 0) and rows past M_cap are dropped (bit 1).
+struct GroupScan {
+  int row_off[kMaxExperts + 1];   // o_e of the clamped counts
+  int tile_off[kMaxExperts + 1];  // prefix of m-tiles per expert
+  int mxs_off[kMaxExperts + 1];   // prefix of ceil(m_e/32): MX column-scale offsets
+  long long wave_tmp[16];
+  long long total_raw;
+};
+
+// Block-wide inclusive scan of one value per thread (NT threads, NT % 64 == 0).
+template <int NT, typename T>
+__device__ __forceinline__ T block_incl_scan(T v, long long* wave_tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    T o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) wave_tmp[wave] = static_cast<long long>(v);
+  __syncthreads();
+  T add = 0;
+  for (int w = 0; w < wave; ++w) add += static_cast<T>(wave_tmp[w]);
+  __syncthreads();
+  return v + add;
+}
+
+// Fills gs from counts[0..E) for m-tiles of BM rows.  NT threads, each owning
+// up to kMaxExperts/NT consecutive experts.  The writer workgroup also stores
+// the clamped offsets and the status bits.  gs is valid after the final barrier.
+template <int NT>
+__device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, int E, int M_cap,
+                                 int BM, int* offsets_out, int* status_out, bool writer) {
+  const int t = threadIdx.x;
+  constexpr int PER = (kMaxExperts + NT - 1) / NT;
+  int c[PER];
+  long long raw_sum = 0;
+  int bad_neg = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    int e = t * PER + i;
+    int v = (e < E) ? counts[e] : 0;
+    if (v < 0) { bad_neg = 1; v = 0; }
+    c[i] = v;
+    raw_sum += v;
+  }
+  long long incl = block_incl_scan<NT, long long>(raw_sum, gs.wave_tmp);
+  long long run = incl - raw_sum;  // exclusive prefix of the non-negative counts
+  int mt_sum = 0, mx_sum = 0;
+  int mloc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    int e = t * PER + i;
+    long long room = (long long)M_cap - run;
+    if (room < 0) room = 0;
+    int m = (long long)c[i] < room ? c[i] : (int)room;
+    mloc[i] = m;
+    if (e < E) gs.row_off[e] = run < M_cap ? (int)run : M_cap;
+    run += c[i];
+    mt_sum += (m + BM - 1) / BM;
+    mx_sum += (m + kMxBlock - 1) / kMxBlock;
+  }
+  if (t == NT - 1) gs.total_raw = run;
+  int mt_incl = block_incl_scan<NT, int>(mt_sum, gs.wave_tmp);
+  int mx_incl = block_incl_scan<NT, int>(mx_sum, gs.wave_tmp);
+  int mt_run = mt_incl - mt_sum, mx_run = mx_incl - mx_sum;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    int e = t * PER + i;
+    if (e < E) {
+      gs.tile_off[e] = mt_run;
+      gs.mxs_off[e] = mx_run;
+    }
+    mt_run += (mloc[i] + BM - 1) / BM;
+    mx_run += (mloc[i] + kMxBlock - 1) / kMxBlock;
+  }
+  if (t == NT - 1) {
+    gs.tile_off[E] = mt_run;
+    gs.mxs_off[E] = mx_run;
+  }
+  int neg_any = __syncthreads_or(bad_neg);
+  if (t == 0) gs.row_off[E] = gs.total_raw < M_cap ? (int)gs.total_raw : M_cap;
+  __syncthreads();
+  if (writer) {
+    if (offsets_out)
+      for (int e = t; e <= E; e += NT) offsets_out[e] = gs.row_off[e];
+    if (status_out && t == 0) {
+      int st = (neg_any ? 1 : 0) | (gs.total_raw > M_cap ? 2 : 0);
+      if (st) atomicOr(status_out, st);
+    }
+  }
+}
+
+// Index of the expert owning global tile t: the last e with tile_off[e] <= t
+// (experts with zero tiles are skipped because their range is empty).
+__device__ __forceinline__ int find_expert(const int* tile_off, int E, int t) {
+  int lo = 0, hi = E;  // invariant: tile_off[lo] <= t < tile_off[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (tile_off[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace moe

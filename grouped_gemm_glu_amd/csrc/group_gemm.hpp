@@ -1,0 +1,471 @@
+// Persistent grouped GEMM for gfx950 with fused epilogues.
+//
+// One launch covers every expert.  The group sizes exist only in device
+// memory ("Boosting MoE Training Throughput with Advanced Fusion Kernels",
+// section "Eliminando la sincronización host-device"): each workgroup scans
+// counts[E] into LDS, then walks global tile ids t = slot, slot + P, ... and
+// decodes each into (expert, m-tile, n-tile) by binary search over the tile
+// prefix.  Rows of one expert are contiguous ([MEGA] §4.3); the last m-tile of
+// a group is partial and handled by clamped loads and masked stores ([MEGA]
+// §5.3).
+//
+// Tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave owning
+// a 128 x 128 sub-tile as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16.  Operands
+// are staged in LDS as [rows][64] bf16, 128 bytes per row, with the 16-byte
+// chunk index XOR-swizzled by ((r ^ (r >> 3)) & 7) so that the fragment reads
+// (8 consecutive rows, one chunk) and the transposed weight writes (rows 8
+// apart) are both free of bank conflicts.  Two LDS stages; the next K-tile is
+// fetched into registers while the current one feeds the MFMAs.
+//
+// Epilogues (fused; the accumulators never go to HBM in fp32):
+//   EPI_GLU   FC1: bias, clamp, activation * up, row scale -> bf16 y; optional
+//             bf16 pre-activation; optional MXFP8 row-wise / transposed copies.
+//   EPI_STORE plain bf16 output (FC2, dX) with optional MXFP8 copies.
+//   EPI_DGLU  backward: reads the saved pre-activation, writes d(gate | up).
+// Output tiles are staged in LDS and written with 16-byte coalesced stores.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace moe {
+
+constexpr int GM_BM = 256;
+constexpr int GM_BN = 256;
+constexpr int GM_BK = 64;
+constexpr int GM_NT = 256;
+constexpr int GM_TILE_BYTES = GM_BM * GM_BK * 2;              // one operand tile: 32 KB
+constexpr int GM_STAGE_BYTES = 2 * GM_TILE_BYTES;             // A + B
+constexpr int GM_MAIN_BYTES = 2 * GM_STAGE_BYTES;             // two stages: 128 KB
+constexpr int GM_STG_LD_256 = 264;                            // staged row, 256 cols (+16 B pad)
+constexpr int GM_STG_LD_128 = 136;                            // staged row, 128 cols (+16 B pad)
+constexpr int GM_STG_BYTES = GM_BM * GM_STG_LD_256 * 2;       // 132 KB
+constexpr int GM_SMEM_BYTES = GM_STG_BYTES > GM_MAIN_BYTES ? GM_STG_BYTES : GM_MAIN_BYTES;
+
+enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2 };
+enum { BL_NK = 0, BL_KN = 1, BL_W1T = 2 };
+
+struct GemmArgs {
+  const uint16_t* A;        // [M_cap][K] grouped rows, K contiguous
+  const uint16_t* B;        // expert e at B + e * b_estride
+  long long b_estride;      // elements between experts
+  int ldb;                  // elements between consecutive rows of the stored B
+  int M_cap, N, K;          // N = GEMM output columns (FC1: 2I, packed order)
+  int I;                    // GLU / dGLU intermediate size
+  const int* counts;
+  int E;
+  int* offsets_out;
+  int* status_out;
+  EpiParams ep;
+  uint16_t* C;              // GLU: y [M_cap][I]; STORE: [M_cap][N]; DGLU: dgu [M_cap][2I]
+  uint16_t* preact;         // GLU: optional output; DGLU: input; [M_cap][2I] plain order
+  uint8_t* row_q;
+  uint8_t* row_s;
+  uint8_t* col_q;
+  uint8_t* col_s;
+  int mx_cols;              // columns of the quantised output (row length of row_q)
+  int col_s_ld;             // ceil(M_cap/32) + E
+  int ntiles_n;
+};
+
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+}
+
+// ---------------------------------------------------------------- MX helpers
+__device__ __forceinline__ void store_bytes(uint8_t* dst, const uint32_t* w, int nvalid) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+  if (nvalid == 32 && (a & 15) == 0) {
+    uint4* d = reinterpret_cast<uint4*>(dst);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else if (nvalid == 32 && (a & 3) == 0) {
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = w[i];
+  } else {
+    for (int i = 0; i < nvalid; ++i) dst[i] = static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3)));
+  }
+}
+
+// Quantises 32 values (nvalid of them real) to e4m3 with one E8M0 scale.
+__device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32_t* w) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (i < nvalid) amax = fmaxf(amax, fabsf(v[i]));
+  // fmaxf drops NaN; a NaN anywhere in the block makes the block NaN
+  bool has_nan = false;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (i < nvalid && v[i] != v[i]) has_nan = true;
+  int E = has_nan ? 128 : mx_scale_exponent(amax);
+  if (E == 128) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0x7F7F7F7Fu;
+    return 0xFF;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t q = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q |= f32_to_e4m3(ldexpf(v[4 * i + j], -E)) << (8 * j);
+    w[i] = q;
+  }
+  return e8m0_byte(E);
+}
+
+// MXFP8 of a staged bf16 tile: stg[r][c] (row stride ld elements) holds rows
+// [0, rows_valid) x cols [0, ncols) of the output, whose global position is
+// grouped row grow0 + r, column col0 + c.  row-wise: blocks along the row;
+// col-wise: blocks of 32 rows starting at the tile's first row (a tile always
+// starts a block because tiles start at group row multiples of 256), scale
+// column scol0 + r / 32.
+__device__ void mx_from_stage(const uint16_t* stg, int ld, int rows_valid, int ncols, int grow0,
+                              int col0, const GemmArgs& p, int scol0) {
+  const int t = threadIdx.x;
+  if (p.row_q) {
+    const int nb = ncols >> 5;
+    for (int it = t; it < GM_BM * nb; it += GM_NT) {
+      int r = it / nb, cb = it - r * nb;
+      if (r >= rows_valid) continue;
+      float v[32];
+      const uint4* s = reinterpret_cast<const uint4*>(stg + r * ld + cb * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint4 x = s[q];
+        uint32_t ww[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * q + 2 * j] = __uint_as_float(ww[j] << 16);
+          v[8 * q + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+        }
+      }
+      uint32_t w[8];
+      uint8_t sb = mx_quant32(v, 32, w);
+      long long grow = grow0 + r;
+      int gc = col0 + cb * 32;
+      store_bytes(p.row_q + grow * p.mx_cols + gc, w, 32);
+      p.row_s[grow * (p.mx_cols >> 5) + (gc >> 5)] = sb;
+    }
+  }
+  if (p.col_q) {
+    const int nrb = (rows_valid + 31) >> 5;
+    for (int it = t; it < ncols * 8; it += GM_NT) {
+      int c = it % ncols, rb = it / ncols;
+      if (rb >= nrb) continue;
+      int nvalid = rows_valid - rb * 32;
+      if (nvalid > 32) nvalid = 32;
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(stg[(rb * 32 + i) * ld + c]);
+      uint32_t w[8];
+      uint8_t sb = mx_quant32(v, nvalid, w);
+      long long gc = col0 + c;
+      store_bytes(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
+      p.col_s[gc * p.col_s_ld + scol0 + rb] = sb;
+    }
+  }
+}
+
+// Coalesced store of a staged bf16 tile (ncols % 8 == 0 assumed per 8-chunk validity).
+__device__ __forceinline__ void store_stage(const uint16_t* stg, int ld, int rows_valid,
+                                            int ncols_valid, int ncols_tile, uint16_t* dst,
+                                            long long dst_ld) {
+  const int t = threadIdx.x;
+  const int cpr = ncols_tile >> 3;  // 16-byte chunks per row
+  for (int it = t; it < GM_BM * cpr; it += GM_NT) {
+    int r = it / cpr, ch = it - r * cpr;
+    if (r < rows_valid && ch * 8 < ncols_valid) {
+      uint4 v = *reinterpret_cast<const uint4*>(stg + r * ld + ch * 8);
+      *reinterpret_cast<uint4*>(dst + r * dst_ld + ch * 8) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- the kernel
+template <int EPI, int BLAY>
+__global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[GM_SMEM_BYTES];
+  __shared__ GroupScan gs;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  build_group_scan<GM_NT>(gs, p.counts, p.E, p.M_cap, GM_BM, p.offsets_out, p.status_out,
+                          blockIdx.x == 0);
+  const int total_tiles = gs.tile_off[p.E] * p.ntiles_n;
+
+  // XCD-aware slot: consecutive workgroups land on different XCDs (round
+  // robin over 8), so give each XCD a contiguous run of tile ids per round.
+  const int P = gridDim.x;
+  const int slot = (P % 8 == 0) ? ((blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3)) : blockIdx.x;
+  const int nk = p.K / GM_BK;
+
+  for (int tile = slot; tile < total_tiles; tile += P) {
+    // ---- decode (expert, m-tile, n-tile); expert e owns tiles
+    // [tile_off[e] * ntiles_n, tile_off[e+1] * ntiles_n), numbered m-fastest
+    int e, mt, nt;
+    {
+      int lo = 0, hi = p.E;  // invariant: tile_off[lo]*ntiles_n <= tile < tile_off[hi]*ntiles_n
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (gs.tile_off[mid] * p.ntiles_n <= tile) lo = mid; else hi = mid;
+      }
+      e = lo;
+      int local = tile - gs.tile_off[e] * p.ntiles_n;
+      int mtiles = gs.tile_off[e + 1] - gs.tile_off[e];
+      nt = local / mtiles;
+      mt = local - nt * mtiles;
+    }
+    const int g_row0 = gs.row_off[e];
+    const int m_e = gs.row_off[e + 1] - g_row0;
+    const int row0 = g_row0 + mt * GM_BM;            // first grouped row of the tile
+    const int rows_valid = min(GM_BM, m_e - mt * GM_BM);
+    const int n0 = nt * GM_BN;
+
+    const uint16_t* __restrict__ Ab = p.A + (long long)row0 * p.K;
+    const uint16_t* __restrict__ Bb = p.B + (long long)e * p.b_estride;
+
+    // ---- per-thread global load coordinates
+    // A and K-contiguous B: 8 rows (tid/8 + 32 i), one 16-byte chunk (tid % 8)
+    const int ld_r = tid >> 3, ld_c = tid & 7;
+    const uint16_t* a_src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int r = ld_r + 32 * i;
+      r = r < rows_valid ? r : rows_valid - 1;
+      a_src[i] = Ab + (long long)r * p.K + ld_c * 8;
+    }
+    const uint16_t* b_src[8];
+    // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (8 rows)
+    const int kn_c = tid & 31, kn_g = tid >> 5;
+    if (BLAY == BL_NK) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int n = n0 + ld_r + 32 * i;
+        n = n < p.N ? n : p.N - 1;
+        b_src[i] = Bb + (long long)n * p.ldb + ld_c * 8;
+      }
+    } else {
+      int ncol = n0 + kn_c * 8;
+      ncol = ncol < p.N ? ncol : p.N - 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b_src[i] = Bb + (long long)(kn_g * 8 + i) * p.ldb + ncol;
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    uint4 ra[8], rb[8];
+    auto gload = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + kt * GM_BK);
+      if (BLAY == BL_NK) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + kt * GM_BK);
+      } else {
+        long long krow;
+        if (BLAY == BL_KN) {
+          krow = (long long)kt * GM_BK;
+        } else {  // packed W1 read as W1^T: plain K tile -> packed row block
+          int j0 = kt * GM_BK;
+          krow = j0 < p.I ? 2LL * j0 : 2LL * (j0 - p.I) + 64;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + krow * p.ldb);
+      }
+    };
+    auto lstore = [&](int stage) {
+      uint8_t* sa = smem + stage * GM_STAGE_BYTES;
+      uint8_t* sb = sa + GM_TILE_BYTES;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint4*>(sa + swz_off(ld_r + 32 * i, ld_c)) = ra[i];
+      if (BLAY == BL_NK) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<uint4*>(sb + swz_off(ld_r + 32 * i, ld_c)) = rb[i];
+      } else {
+        // rb[i] holds 8 columns at k = 8*kn_g + i; transpose to 8 k-values per column
+        uint32_t w[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          w[i][0] = rb[i].x; w[i][1] = rb[i].y; w[i][2] = rb[i].z; w[i][3] = rb[i].w;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t lo = w[2 * q][j >> 1], hi = w[2 * q + 1][j >> 1];
+            o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+          }
+          *reinterpret_cast<uint4*>(sb + swz_off(kn_c * 8 + j, kn_g)) =
+              make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      const uint8_t* sa = smem + cur * GM_STAGE_BYTES;
+      const uint8_t* sb = sa + GM_TILE_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ch = ks * 2 + (lane >> 5);
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int r = wm * 128 + i * 32 + (lane & 31);
+          af[i] = *reinterpret_cast<const bf16x8*>(sa + swz_off(r, ch));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int r = wn * 128 + j * 32 + (lane & 31);
+          bfr[j] = *reinterpret_cast<const bf16x8*>(sb + swz_off(r, ch));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      if (kt + 1 < nk) lstore(cur ^ 1);
+      __syncthreads();
+    }
+
+    // ================================================================ epilogues
+    // Accumulator element r of block (i, j): tile row wm*128 + 32 i + 8 (r/4)
+    // + 4 (lane/32) + r%4, tile column wn*128 + 32 j + lane%32.
+    uint16_t* stg = reinterpret_cast<uint16_t*>(smem);
+    const int lrow = 4 * (lane >> 5);
+    const int lcol = lane & 31;
+
+    if (EPI == EPI_GLU) {
+      // packed pair wn of this tile: gate = blocks j = 0, 1; up = j = 2, 3
+      const int ld = GM_STG_LD_128;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int ycol = wn * 64 + jj * 32 + lcol;          // y column within the tile
+        const int c = nt * 128 + ycol;                      // global gate column / y column
+        const bool cvalid = c < p.I;
+        float bg = 0.0f, bu = 0.0f;
+        if (p.ep.bias && cvalid) {
+          bg = bf16_to_f32(p.ep.bias[(long long)e * 2 * p.I + c]);
+          bu = bf16_to_f32(p.ep.bias[(long long)e * 2 * p.I + p.I + c]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int trow = wm * 128 + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
+            float g = acc[i][jj][r] + bg;
+            float u = acc[i][jj + 2][r] + bu;
+            const bool rvalid = trow < rows_valid;
+            if (p.preact && rvalid && cvalid) {
+              uint16_t* pr = p.preact + (long long)(row0 + trow) * 2 * p.I;
+              pr[c] = f32_to_bf16(g);
+              pr[p.I + c] = f32_to_bf16(u);
+            }
+            float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
+            float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
+            float y = act_fwd(p.ep.act, gc, p.ep.alpha) * uc;
+            if (p.ep.row_scale && rvalid) y *= p.ep.row_scale[row0 + trow];
+            stg[trow * ld + ycol] = f32_to_bf16(y);
+          }
+        }
+      }
+      __syncthreads();
+      const int cvalid_n = min(128, p.I - nt * 128);
+      if (p.C)
+        store_stage(stg, ld, rows_valid, cvalid_n, 128, p.C + (long long)row0 * p.I + nt * 128, p.I);
+      if (p.row_q || p.col_q)
+        mx_from_stage(stg, ld, rows_valid, cvalid_n, row0, nt * 128, p, gs.mxs_off[e] + mt * 8);
+      __syncthreads();
+    } else if (EPI == EPI_STORE) {
+      const int ld = GM_STG_LD_256;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int trow = wm * 128 + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
+            const int tcol = wn * 128 + j * 32 + lcol;
+            stg[trow * ld + tcol] = f32_to_bf16(acc[i][j][r]);
+          }
+      __syncthreads();
+      const int cvalid_n = min(GM_BN, p.N - n0);
+      if (p.C)
+        store_stage(stg, ld, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
+      if (p.row_q || p.col_q)
+        mx_from_stage(stg, ld, rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
+      __syncthreads();
+    } else {  // EPI_DGLU: acc = G = dL/dy for columns n0 .. n0+255 of I
+      const int ld = GM_STG_LD_256;
+      const long long ld2 = 2LL * p.I;
+      // pass 0 stages dg, pass 1 stages du
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tcol = wn * 128 + j * 32 + lcol;
+          const int c = n0 + tcol;
+          const bool cvalid = c < p.I;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int trow = wm * 128 + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
+              float out = 0.0f;
+              if (trow < rows_valid && cvalid) {
+                const uint16_t* pr = p.preact + (long long)(row0 + trow) * ld2;
+                float g = bf16_to_f32(pr[c]);
+                float u = bf16_to_f32(pr[p.I + c]);
+                float G = acc[i][j][r];
+                if (p.ep.row_scale) G *= p.ep.row_scale[row0 + trow];
+                float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
+                float a, da;
+                act_fwd_bwd(p.ep.act, gc, p.ep.alpha, a, da);
+                if (pass == 0) {
+                  float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
+                  bool gin = (g >= p.ep.gate_lo) && (g <= p.ep.gate_hi);
+                  out = gin ? G * uc * da : 0.0f;
+                } else {
+                  bool uin = (u >= p.ep.up_lo) && (u <= p.ep.up_hi);
+                  out = uin ? G * a : 0.0f;
+                }
+              }
+              stg[trow * ld + tcol] = f32_to_bf16(out);
+            }
+          }
+        }
+        __syncthreads();
+        const int cvalid_n = min(GM_BN, p.I - n0);
+        const int ccol0 = (pass == 0 ? 0 : p.I) + n0;
+        if (p.C)
+          store_stage(stg, ld, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * ld2 + ccol0, ld2);
+        if (p.row_q || p.col_q)
+          mx_from_stage(stg, ld, rows_valid, cvalid_n, row0, ccol0, p, gs.mxs_off[e] + mt * 8);
+        __syncthreads();
+      }
+    }
+  }
+}
+
+}  // namespace moe

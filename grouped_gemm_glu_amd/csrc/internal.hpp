@@ -1,0 +1,18 @@
+// Host-side declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "group_gemm.hpp"
+#include "moe_glu.h"
+
+namespace moe {
+
+// Launch one persistent grouped-GEMM kernel instantiation; each returns
+// MOE_ERR_UNSUPPORTED for a combination its translation unit does not hold.
+moe_status_t launch_group_gemm_fwd(int epi, int blay, const GemmArgs& args, int grid,
+                                   hipStream_t stream);
+moe_status_t launch_group_gemm_bwd(int epi, int blay, const GemmArgs& args, int grid,
+                                   hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,233 @@
+/*
+ * moe_glu.h -- C ABI of the sync-free MoE expert-MLP library for AMD MI355X
+ * (CDNA4, gfx950): grouped GEMM over per-expert token groups whose sizes live
+ * only in device memory, with the GLU activation, its backward and an MXFP8
+ * quantize/transpose fused into the GEMM epilogues.
+ *
+ * Sources ("the pages"):
+ *   [BLOG] "Boosting MoE Training Throughput with Advanced Fusion Kernels"
+ *          (Spanish translation).  Its kernel family: GroupGemm + Quantize,
+ *          GroupGemm + Activation + Quantize/Transpose, GroupGemm +
+ *          dActivation + Quantize/Transpose; activations SwiGLU, GeGLU,
+ *          sReLU with clamping and scaling.
+ *   [MEGA] DeepSeek MegaMoE / DeepGEMM walkthrough (hnwysp.cn), §2.1 routing,
+ *          §4.3 grouped GEMM over contiguous per-expert rows, §5.3 tail tiles.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  bf16 tensors are
+ *     passed as 16-bit storage, e4m3fn elements and E8M0 scales as bytes.
+ *     Every device pointer must be 16-byte aligned, except the MX outputs.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call allocates, synchronises, or reads device data back to
+ *     the host, so each is legal inside hipStreamBeginCapture.
+ *   - The caller owns every buffer.  The library keeps no per-call state.
+ *   - Errors a host can see (null required pointer, bad shape, misalignment,
+ *     unsupported option) return a nonzero status BEFORE anything launches.
+ *     A failed launch returns MOE_ERR_LAUNCH.  Errors only the device can see
+ *     (a negative count, counts summing past M_cap) set bits in
+ *     groups->status_out and the work is clamped to M_cap rows; nothing is
+ *     read or written out of bounds and no kernel traps.
+ *   - Grouped rows: expert e owns rows [o_e, o_e + m_e) of every [M_cap][*]
+ *     operand, o_e = sum_{j<e} m_j ([MEGA] §4.3).  Rows >= sum m_e, and all
+ *     rows of a zero-row expert, are never written.
+ *   - Calls on different streams are independent and re-entrant.
+ */
+#ifndef MOE_GLU_H
+#define MOE_GLU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,        /* a size is out of range or not a supported multiple */
+  MOE_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned */
+  MOE_ERR_UNSUPPORTED = 4,  /* an option combination the library does not implement */
+  MOE_ERR_LAUNCH = 5,       /* the HIP runtime rejected a launch */
+  MOE_ERR_DEVICE = 6        /* no usable gfx950 device */
+} moe_status_t;
+
+typedef enum {
+  MOE_ACT_SWIGLU = 0,       /* a(g) = g * sigmoid(alpha * g) */
+  MOE_ACT_GEGLU = 1,        /* a(g) = g * Phi(g), exact erf form */
+  MOE_ACT_GEGLU_TANH = 2,   /* a(g) = tanh approximation of g * Phi(g) */
+  MOE_ACT_SRELU = 3         /* a(g) = max(g, 0)^2 */
+} moe_act_t;
+
+/* GLU epilogue ([BLOG] "Optimizando GLU vía epílogos GEMM fusionados": the
+ * GLU splits FC1's output into an input (up) half and a gate half; the fused
+ * epilogue also does feature scaling, clamping and bias addition).
+ * With z = FC1 output + bias, g = z[:, :I] (gate), u = z[:, I:] (up):
+ *     y = a(clamp(g, gate_lo, gate_hi)) * (clamp(u, up_lo, up_hi) + up_offset)
+ *         * row_scale[row]
+ * rounded to bf16 (round-to-nearest-even).  (host struct) */
+typedef struct {
+  int32_t act;              /* moe_act_t */
+  int32_t gated;            /* must be 1: the gated (GLU) form */
+  float alpha;              /* SwiGLU gate scale inside the sigmoid; 1 = plain SiLU */
+  float gate_lo, gate_hi;   /* clamp bounds on g; -inf/+inf = off */
+  float up_lo, up_hi;       /* clamp bounds on u; -inf/+inf = off */
+  float up_offset;          /* added to the clamped up value; 0 = off */
+  const void* bias;         /* nullable: bf16 [E][2I] in PLAIN order (gate | up) */
+  const float* row_scale;   /* nullable: fp32 [M_cap], multiplies y per row */
+} moe_epilogue_t;
+
+/* MXFP8 outputs ([BLOG] "Fusionando cuantización MXFP8 y NVFP4": the
+ * quantised activation plus a transposed copy for back prop).  Blocks of 32
+ * values share one E8M0 scale X = 2^E, E the smallest integer with
+ * amax/X <= 448; elements are e4m3fn(v / X), round-to-nearest-even.
+ * For an output of R = M_cap rows and C columns:
+ *   row_q [R][C], row_s [R][C/32]          blocks along a row
+ *   col_q [C][R], col_s [C][ceil(R/32)+E]  blocks of 32 rows of one column
+ *                                          that restart at each group's first
+ *                                          row; group e's scales start at column
+ *                                          sum_{j<e} ceil(m_j/32)
+ * Any pointer may be NULL (that copy is skipped); row_q/row_s and col_q/col_s
+ * go in pairs.  No alignment requirement.  (host struct) */
+typedef struct {
+  uint8_t* row_q;
+  uint8_t* row_s;
+  uint8_t* col_q;
+  uint8_t* col_s;
+} moe_mx_out_t;
+
+/* Expert groups.  The counts are the ONLY copy of the group sizes and stay in
+ * device memory ([BLOG] "Eliminando la sincronización host-device": tokens
+ * per group are tracked in GPU memory, so no host sync is needed and a whole
+ * iteration can be captured in a graph).  (host struct) */
+typedef struct {
+  const int32_t* counts;    /* device [E] */
+  int32_t E;                /* 1 <= E <= 1024 */
+  int32_t M_cap;            /* static row capacity of every grouped operand */
+  int32_t* offsets_out;     /* nullable device [E+1]: exclusive scan of the clamped counts */
+  int32_t* status_out;      /* nullable device word, OR-ed: bit0 a count < 0, bit1 sum > M_cap */
+} moe_groups_t;
+
+/* Operand descriptor of moe_group_gemm_quant. */
+typedef enum {
+  MOE_DT_BF16 = 0,
+  MOE_DT_MXFP8 = 1          /* e4m3fn bytes + E8M0 scales, 32-blocks along K */
+} moe_dtype_t;
+
+typedef enum {
+  MOE_B_KN = 0,             /* B_e is [K][N] row-major (N contiguous), e.g. W2 [E][I][H] for FC2 */
+  MOE_B_NK = 1,             /* B_e is stored [N][K] (K contiguous), i.e. used transposed:
+                               out = A . B_e^T, e.g. W2 [E][I][H] in the dgrad dY2 . W2^T */
+  MOE_B_W1_PACKED_T = 2     /* B_e = W1_e^T read from the packed W1 of moe_repack_gate_up:
+                               out = A . W1_e^T with A's K = 2I in PLAIN order (dX) */
+} moe_b_layout_t;
+
+typedef struct {
+  int32_t dtype;            /* moe_dtype_t */
+  int32_t layout;           /* A: ignored (always [M_cap][K] row-major); B: moe_b_layout_t */
+  const void* data;         /* bf16 or e4m3 elements */
+  const uint8_t* scales;    /* MXFP8 only: A [M_cap][K/32]; B [E][N][K/32] */
+} moe_operand_t;
+
+/* Reads the device's compute-unit count once; call before graph capture.
+ * Every other call initialises lazily on first use. */
+moe_status_t moe_init(int device);
+
+const char* moe_status_string(moe_status_t s);
+
+/* Bytes of the packed W1 for E experts, hidden H, intermediate I (= E*2I*H*2). */
+size_t moe_packed_w1_bytes(int E, int H, int I);
+
+/* Offline gate/up repack ([BLOG] "Optimizando GLU…" and its Figure 2: W1's
+ * columns are repacked into interleaved gate and input (up) blocks so that one
+ * GEMM tile holds half a tile width of each; done once at checkpoint load).
+ * w1:        bf16 [E][H][2I], plain: columns [0,I) gate, [I,2I) up.
+ * w1_packed: bf16 [E][2I][H] (K-contiguous).  Packed column 128p + s holds
+ *            gate column 64p + s for s < 64 and up column I + 64p + (s-64)
+ *            for s >= 64.  Requires I % 64 == 0, H % 8 == 0.  Bit-exact. */
+moe_status_t moe_repack_gate_up(const void* w1, int E, int H, int I, void* w1_packed,
+                                void* stream);
+
+/* Inverse of moe_repack_gate_up (checkpoint save, tests).  Bit-exact. */
+moe_status_t moe_unpack_gate_up(const void* w1_packed, int E, int H, int I, void* w1,
+                                void* stream);
+
+/* Device routing and grouping ([MEGA] §2.1: each token's k experts are the
+ * k largest router logits; §4.3: rows of one expert laid out contiguously).
+ * Exactly one of logits (fp32 [T][E]) / topk_ids (int32 [T][k]) is non-NULL.
+ * Ties go to the lower expert id.  Outputs (all device, all required except
+ * xg): topk_ids_out [T][k]; counts [E]; offsets [E+1]; dst [T][k], the grouped
+ * row of pair (t, j); src [T*k], the token of each grouped row.  Within an
+ * expert the pairs keep ascending (t, j) order, so the result is unique and
+ * deterministic.  If x (bf16 [T][H]) and xg (bf16 [T*k][H]) are given, xg
+ * receives the gathered rows xg[r] = x[src[r]].  Requires k <= E <= 1024,
+ * k <= 16, T*k < 2^31, H % 8 == 0. */
+moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T, int E, int k,
+                             int32_t* topk_ids_out, int32_t* counts, int32_t* offsets,
+                             int32_t* dst, int32_t* src, const void* x, int H, void* xg,
+                             void* stream);
+
+/* GroupGemm + Activation (+ Quantize/Transpose), the fused FC1 ([BLOG] kernel
+ * family, second kernel).  For each expert e, with A_e = xg rows of group e:
+ *     z = A_e . W1_e (+ bias_e)          fp32 accumulate, W1 from moe_repack_gate_up
+ *     preact = bf16(z)                   optional, [M_cap][2I] in PLAIN order
+ *     y = bf16(GLU epilogue of z)        optional, [M_cap][I]
+ *     mx = MXFP8 copies of y             optional (row-wise and/or transposed)
+ * xg: bf16 [M_cap][H].  Requires H % 64 == 0, I % 64 == 0, ep->gated == 1.
+ * One persistent launch; tiles are scheduled from the device counts.
+ * cu_margin: compute units left free for concurrent kernels (0 = use all). */
+moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
+                                    const void* w1_packed, int H, int I,
+                                    const moe_epilogue_t* ep, void* y, void* preact,
+                                    const moe_mx_out_t* mx, int cu_margin, void* stream);
+
+/* GroupGemm + dActivation (+ Quantize/Transpose), the fused backward of FC1's
+ * activation ([BLOG] "Optimizando GLU…": in back prop the epilogue reads the
+ * GEMM output, computes the dGLU and writes it out).  Per expert:
+ *     G = dy2_e . W2_e^T                 fp32 accumulate; dy2 bf16 [M_cap][H],
+ *                                        w2 bf16 [E][I][H] (FC2's weight)
+ *     with g, u from preact (bf16 [M_cap][2I] plain, post-bias, pre-clamp),
+ *     gc = clamp(g), uc = clamp(u) + up_offset, rs = row_scale or 1:
+ *     du = G * a(gc) * rs * [up_lo <= u <= up_hi]
+ *     dg = G * uc * rs * a'(gc) * [gate_lo <= g <= gate_hi]
+ *     dgu = bf16([dg | du])              [M_cap][2I] plain order
+ *     mx = MXFP8 copies of dgu           optional
+ * ep->bias is ignored (already inside preact).  Requires H % 64 == 0,
+ * I % 64 == 0. */
+moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const void* w2, int H, int I,
+                                     const moe_groups_t* groups, const void* preact,
+                                     const moe_epilogue_t* ep, void* dgu,
+                                     const moe_mx_out_t* mx, int cu_margin, void* stream);
+
+/* GroupGemm + Quantize ([BLOG] kernel family, first kernel): out_e = A_e . B_e
+ * with bf16 and/or MXFP8 output.  A: [M_cap][K] grouped rows; B per the
+ * layout in b->layout.  c_bf16: nullable bf16 [M_cap][N].
+ * bf16 x bf16 on every B layout; MXFP8 x MXFP8 (both dtypes MXFP8) requires
+ * layout MOE_B_NK (B stored [E][N][K] e4m3 with scales [E][N][K/32]).
+ * Requires K % 64 == 0 (K % 128 == 0 for MXFP8), N % 64 == 0. */
+moe_status_t moe_group_gemm_quant(const moe_operand_t* a, const moe_operand_t* b, int N, int K,
+                                  const moe_groups_t* groups, void* c_bf16,
+                                  const moe_mx_out_t* mx, int cu_margin, void* stream);
+
+/* Unfused GLU pass (baseline and fallback): y = GLU epilogue of z, where z is
+ * the plain-order bf16 [M_cap][2I] FC1 output WITHOUT bias (bias, if any, is
+ * added here).  Same arithmetic as the fused epilogue, as its own kernel. */
+moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
+                             const moe_epilogue_t* ep, void* y, void* stream);
+
+/* Standalone MXFP8 quantize/transpose (baseline, and offline weight prep) of
+ * a bf16 [R][C] matrix.  Row-wise blocks run along C.  Column-wise blocks run
+ * down 32 rows; with groups (counts over the first rows, M_cap = R) they
+ * restart at each group's first row exactly as in the fused epilogues and
+ * col_s is [C][ceil(R/32)+E]; without groups the whole matrix is one group
+ * and col_s is [C][ceil(R/32)].  So quantising one expert's W2_e [I][H]
+ * column-wise yields exactly the [H][I] e4m3 + [H][I/32] scale operand that
+ * MOE_B_NK expects.  Requires C % 32 == 0. */
+moe_status_t moe_mxfp8_quantize(const void* v, int R, int C, const moe_groups_t* groups,
+                                const moe_mx_out_t* mx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GLU_H */

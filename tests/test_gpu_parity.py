@@ -1,0 +1,406 @@
+"""GPU parity of every entry point against the CPU oracle on small seeded
+inputs (several tiles, ragged group tails, empty experts), through the C ABI.
+
+Integer, index and byte results are compared bit-exactly; bf16 results within
+|gpu - ref| <= 2e-2 (1 + |ref|).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import formats as F
+from oracle import moe as O
+from tests.gpu_util import (BF16_NAN_SENTINEL, BYTE_SENTINEL, assert_bf16_close, dev_bits, dev_i32,
+                            empty_bits, empty_bytes, host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_gemm_glu_amd as G
+    G.moe_init(0)
+    return G
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- repack
+@pytest.mark.parametrize("E,H,I", [(3, 64, 192), (4, 256, 512), (2, 72, 64)])
+def test_repack_bit_exact_and_roundtrip(G, E, H, I):
+    rng = np.random.default_rng(E * 1000 + H + I)
+    w1 = rng.integers(0, 2 ** 16, size=(E, H, 2 * I)).astype(np.uint16)
+    want, _ = O.repack_gate_up(w1)
+    d_w1 = dev_bits(w1)
+    d_p = empty_bits((E, 2 * I, H))
+    G.moe_repack_gate_up(d_w1, E, H, I, d_p)
+    d_back = empty_bits((E, H, 2 * I))
+    G.moe_unpack_gate_up(d_p, E, H, I, d_back)
+    _sync()
+    assert np.array_equal(host_bits(d_p), want)
+    assert np.array_equal(host_bits(d_back), w1)
+
+
+# ---------------------------------------------------------------- routing / grouping
+def _route_case(G, logits, k, x=None):
+    import torch
+    T, E = logits.shape
+    d_logits = torch.from_numpy(logits).cuda()
+    ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offs = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    dst = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    src = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    xg = None
+    H = 0
+    if x is not None:
+        H = x.shape[1]
+        xg = empty_bits((T * k, H))
+    G.moe_route_group(d_logits, None, T, E, k, ids, counts, offs, dst, src,
+                      None if x is None else dev_bits(x), H, xg)
+    _sync()
+    return (ids.cpu().numpy(), counts.cpu().numpy(), offs.cpu().numpy(), dst.cpu().numpy(),
+            src.cpu().numpy(), None if xg is None else host_bits(xg))
+
+
+@pytest.mark.parametrize("case", ["tiny", "tiny_empty", "gptoss", "ties"])
+def test_route_group_bit_exact(G, case):
+    if case == "ties":
+        rng = np.random.default_rng(5)
+        logits = rng.integers(-2, 3, size=(300, 9)).astype(np.float32)
+        x, k = None, 3
+    elif case == "gptoss":
+        d = W.gptoss(with_weights=False)
+        logits, x, k = d["logits"], d["x"], d["k"]
+    else:
+        d = W.tiny(empty_expert=(case == "tiny_empty"))
+        logits, x, k = d["logits"], d["x"], d["k"]
+    ids, counts, offs, dst, src, xg = _route_case(G, logits, k, x)
+    rids, rcounts, roffs, rdst, rsrc = O.route_topk(logits, k)
+    assert np.array_equal(ids, rids)
+    assert np.array_equal(counts, rcounts) and np.array_equal(offs, roffs)
+    assert np.array_equal(dst, rdst) and np.array_equal(src, rsrc)
+    if x is not None:
+        assert np.array_equal(xg, O.gather_rows(x, rsrc))
+
+
+# ---------------------------------------------------------------- FC1 + GLU
+def _fc1_gpu(G, x, counts, w1, I, ep_kw, m_cap=None, preact=True, mx=False, bias=None,
+             row_scale=None, cu_margin=0):
+    import torch
+    E, H, _ = w1.shape
+    M = int(np.sum(counts))
+    m_cap = m_cap or x.shape[0]
+    d_w1 = dev_bits(w1)
+    d_w1p = empty_bits((E, 2 * I, H))
+    G.moe_repack_gate_up(d_w1, E, H, I, d_w1p)
+    d_x = dev_bits(x)
+    d_counts = dev_i32(counts)
+    d_off = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = empty_bits((m_cap, I))
+    pre = empty_bits((m_cap, 2 * I)) if preact else None
+    d_bias = dev_bits(bias) if bias is not None else None
+    d_rs = torch.from_numpy(row_scale).cuda() if row_scale is not None else None
+    ep = G.epilogue(bias=d_bias, row_scale=d_rs, **ep_kw)
+    grp = G.groups(d_counts, m_cap, d_off, d_status)
+    mxo, bufs = None, None
+    if mx:
+        bufs = dict(row_q=empty_bytes((m_cap, I)), row_s=empty_bytes((m_cap, I // 32)),
+                    col_q=empty_bytes((I, m_cap)), col_s=empty_bytes((I, (m_cap + 31) // 32 + E)))
+        mxo = G.mx_out(**bufs)
+    G.moe_group_gemm_glu_fwd(d_x, grp, d_w1p, H, I, ep, y, pre, mxo, cu_margin)
+    _sync()
+    out = dict(y=host_bits(y), off=d_off.cpu().numpy(), status=int(d_status.item()))
+    if preact:
+        out["preact"] = host_bits(pre)
+    if mx:
+        out.update({k: v.cpu().numpy() for k, v in bufs.items()})
+    return out
+
+
+def _check_fc1(out, x, counts, w1, ep_o, m_cap, what):
+    M = int(np.sum(counts))
+    rp, ry = O.fc1_glu(x[:M], counts, w1, ep_o)
+    assert np.array_equal(out["off"], O.exclusive_offsets(counts).astype(np.int32))
+    assert out["status"] == 0
+    assert_bf16_close(out["y"][:M], ry, what=what + " y")
+    if "preact" in out:
+        assert_bf16_close(out["preact"][:M], rp, what=what + " preact")
+        assert np.all(out["preact"][M:] == BF16_NAN_SENTINEL)
+    assert np.all(out["y"][M:] == BF16_NAN_SENTINEL)
+    return rp, ry
+
+
+@pytest.mark.parametrize("empty", [False, True])
+def test_fc1_tiny_workload(G, empty):
+    d = W.tiny(empty_expert=empty)
+    _, counts, _, _, src = O.route_topk(d["logits"], d["k"])
+    xg = O.gather_rows(d["x"], src)
+    out = _fc1_gpu(G, xg, counts, d["w1"], d["I"], {})
+    _check_fc1(out, xg, counts, d["w1"], O.Epilogue(), xg.shape[0], d["name"])
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu", "geglu_tanh", "srelu"])
+def test_fc1_ragged_all_activations(G, act):
+    counts = np.array([300, 0, 1, 257, 64, 0, 513])
+    E, H, I = len(counts), 128, 320          # 2I = 640: 2.5 n-tiles (half-tile tail)
+    m_cap = int(counts.sum()) + 37
+    d = W.small_grouped(10, counts, H, I, bias=True, m_cap=m_cap)
+    rs = (np.random.default_rng(3).uniform(0.5, 1.5, m_cap)).astype(np.float32)
+    ep_kw = dict(act=act, alpha=1.702 if act == "swiglu" else 1.0, gate_lo=-1.5, gate_hi=1.0,
+                 up_lo=-1.2, up_hi=2.0, up_offset=0.5)
+    out = _fc1_gpu(G, d["x"], counts, d["w1"], I, ep_kw, m_cap=m_cap, bias=d["b1"], row_scale=rs)
+    ep_o = O.Epilogue(bias=d["b1"], row_scale=rs, **ep_kw)
+    _check_fc1(out, d["x"], counts, d["w1"], ep_o, m_cap, act)
+
+
+def test_fc1_integer_exact_preact_bit_exact(G):
+    """Ternary inputs with K = 256: every partial sum is a small integer, so the
+    pre-activation has exactly one correct bf16 value whatever the order."""
+    counts = np.array([5, 260, 0, 77])
+    E, H, I = 4, 256, 192
+    M = int(counts.sum())
+    x = W.ternary_bf16(1, (M, H))
+    w1 = W.ternary_bf16(2, (E, H, 2 * I))
+    out = _fc1_gpu(G, x, counts, w1, I, {})
+    rp, ry = O.fc1_glu(x, counts, w1, O.Epilogue())
+    assert np.array_equal(out["preact"], rp)
+    assert_bf16_close(out["y"], ry, what="ternary y")
+
+
+def test_fc1_row_permutation_within_group_bit_exact(G):
+    counts = np.array([200, 300])
+    E, H, I = 2, 192, 128
+    d = W.small_grouped(11, counts, H, I)
+    rng = np.random.default_rng(0)
+    perm = np.concatenate([rng.permutation(200), 200 + rng.permutation(300)])
+    a = _fc1_gpu(G, d["x"], counts, d["w1"], I, {}, mx=True)
+    b = _fc1_gpu(G, d["x"][perm], counts, d["w1"], I, {}, mx=True)
+    assert np.array_equal(a["y"][perm], b["y"]) and np.array_equal(a["preact"][perm], b["preact"])
+    assert np.array_equal(a["row_q"][perm], b["row_q"]) and np.array_equal(a["row_s"][perm], b["row_s"])
+
+
+def test_fc1_mx_epilogue_matches_oracle_quantisation(G):
+    """The fused MXFP8 row-wise and transposed copies equal the oracle's
+    quantisation of the GPU's own bf16 y byte for byte, and y itself is within
+    tolerance of the oracle."""
+    counts = np.array([70, 0, 33, 256, 1, 300])
+    E, H, I = len(counts), 128, 256
+    m_cap = int(counts.sum()) + 5
+    d = W.small_grouped(12, counts, H, I, m_cap=m_cap)
+    x = W.student_t_rows_bf16(12, m_cap, H)
+    out = _fc1_gpu(G, x, counts, d["w1"], I, {}, m_cap=m_cap, mx=True)
+    M = int(counts.sum())
+    _check_fc1(out, x, counts, d["w1"], O.Epilogue(), m_cap, "mx")
+    q, s = O.mx_quantize_rows(out["y"][:M])
+    assert np.array_equal(out["row_q"][:M], q) and np.array_equal(out["row_s"][:M], s)
+    assert np.all(out["row_q"][M:] == BYTE_SENTINEL)
+    cq, cs = O.mx_quantize_cols(out["y"][:M], counts, m_cap=m_cap)
+    assert np.array_equal(out["col_q"][:, :M], cq[:, :M])
+    used = O.mx_scale_col_offsets(counts)[-1]
+    assert np.array_equal(out["col_s"][:, :used], cs[:, :used])
+    assert np.all(out["col_s"][:, used:] == BYTE_SENTINEL)
+    assert np.all(out["col_q"][:, M:] == BYTE_SENTINEL)
+
+
+def test_fc1_device_status_bits_and_clamp(G):
+    import torch
+    E, H, I = 3, 64, 64
+    m_cap = 100
+    d = W.small_grouped(13, [40, 40, 40], H, I, m_cap=m_cap)
+    counts = np.array([-5, 70, 50])    # negative count and a sum past M_cap
+    out = _fc1_gpu(G, d["x"], counts, d["w1"], I, {}, m_cap=m_cap)
+    assert out["status"] == 3
+    # clamped groups: expert 0 -> 0 rows, expert 1 -> 70, expert 2 -> 30
+    assert out["off"].tolist() == [0, 0, 70, 100]
+    clamped = np.array([0, 70, 30])
+    rp, ry = O.fc1_glu(d["x"], clamped, d["w1"], O.Epilogue())
+    assert_bf16_close(out["y"], ry, what="clamped y")
+
+
+# ---------------------------------------------------------------- GroupGemm (+Quantize)
+def _quant_gpu(G, a_bits, counts, b_bits, layout, N, K, m_cap, mx=False):
+    import torch
+    E = len(counts)
+    d_counts = dev_i32(counts)
+    c = empty_bits((m_cap, N))
+    bufs, mxo = None, None
+    if mx:
+        bufs = dict(row_q=empty_bytes((m_cap, N)), row_s=empty_bytes((m_cap, N // 32)),
+                    col_q=empty_bytes((N, m_cap)), col_s=empty_bytes((N, (m_cap + 31) // 32 + E)))
+        mxo = G.mx_out(**bufs)
+    d_a = dev_bits(a_bits)
+    G.moe_group_gemm_quant(G.operand(d_a), G.operand(b_bits, layout=layout), N, K,
+                           G.groups(d_counts, m_cap), c, mxo)
+    _sync()
+    out = dict(c=host_bits(c))
+    if mx:
+        out.update({k: v.cpu().numpy() for k, v in bufs.items()})
+    return out
+
+
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+def test_group_gemm_quant_bf16(G, layout):
+    counts = np.array([129, 0, 400, 3, 256])
+    E, K, N = len(counts), 320, 448
+    m_cap = int(counts.sum()) + 3
+    rng = np.random.default_rng(21)
+    a = W.to_bf16_bits(rng.standard_normal((m_cap, K)).astype(np.float32))
+    b = W.to_bf16_bits((rng.standard_normal((E, K, N)) * 0.05).astype(np.float32))
+    if layout == "KN":
+        d_b = dev_bits(b)
+        lay = G.B_KN
+    else:
+        d_b = dev_bits(np.ascontiguousarray(np.transpose(b, (0, 2, 1))))
+        lay = G.B_NK
+    out = _quant_gpu(G, a, counts, d_b, lay, N, K, m_cap, mx=True)
+    M = int(counts.sum())
+    ref = O.group_gemm(a[:M], counts, b)
+    assert_bf16_close(out["c"][:M], ref, what="group_gemm " + layout)
+    assert np.all(out["c"][M:] == BF16_NAN_SENTINEL)
+    q, s = O.mx_quantize_rows(out["c"][:M])
+    assert np.array_equal(out["row_q"][:M], q) and np.array_equal(out["row_s"][:M], s)
+    cq, cs = O.mx_quantize_cols(out["c"][:M], counts, m_cap=m_cap)
+    used = O.mx_scale_col_offsets(counts)[-1]
+    assert np.array_equal(out["col_q"][:, :M], cq[:, :M])
+    assert np.array_equal(out["col_s"][:, :used], cs[:, :used])
+
+
+def test_group_gemm_quant_integer_exact(G):
+    counts = np.array([300, 17, 0, 260])
+    E, K, N = 4, 256, 320
+    M = int(counts.sum())
+    a = W.ternary_bf16(3, (M, K))
+    b = W.ternary_bf16(4, (E, K, N))
+    out = _quant_gpu(G, a, counts, dev_bits(b), G.B_KN, N, K, M)
+    assert np.array_equal(out["c"], O.group_gemm(a, counts, b))
+
+
+def test_dx_through_packed_w1(G):
+    counts = np.array([100, 0, 300, 257])
+    E, H, I = len(counts), 192, 192
+    M = int(counts.sum())
+    rng = np.random.default_rng(22)
+    dgu = W.to_bf16_bits(rng.standard_normal((M, 2 * I)).astype(np.float32))
+    w1 = W.to_bf16_bits((rng.standard_normal((E, H, 2 * I)) * 0.05).astype(np.float32))
+    d_w1p = empty_bits((E, 2 * I, H))
+    G.moe_repack_gate_up(dev_bits(w1), E, H, I, d_w1p)
+    out = _quant_gpu(G, dgu, counts, d_w1p, G.B_W1_PACKED_T, H, 2 * I, M)
+    assert_bf16_close(out["c"], O.dx(dgu, counts, w1), what="dX")
+    # integer-exact variant: bit-exact
+    dgu_t = W.ternary_bf16(5, (M, 2 * I))
+    w1_t = W.ternary_bf16(6, (E, H, 2 * I), density=0.5)
+    G.moe_repack_gate_up(dev_bits(w1_t), E, H, I, d_w1p)
+    out = _quant_gpu(G, dgu_t, counts, d_w1p, G.B_W1_PACKED_T, H, 2 * I, M)
+    assert np.array_equal(out["c"], O.dx(dgu_t, counts, w1_t))
+
+
+# ---------------------------------------------------------------- dgrad + dGLU
+@pytest.mark.parametrize("act,clamp", [("swiglu", False), ("swiglu", True), ("geglu", False),
+                                       ("geglu_tanh", False), ("srelu", False)])
+def test_dglu_bwd(G, act, clamp):
+    import torch
+    counts = np.array([64, 0, 300, 1, 270])
+    E, H, I = len(counts), 256, 320
+    m_cap = int(counts.sum()) + 9
+    M = int(counts.sum())
+    rng = np.random.default_rng(31)
+    dy2 = W.to_bf16_bits((rng.standard_normal((m_cap, H)) * 0.1).astype(np.float32))
+    w2 = W.to_bf16_bits((rng.standard_normal((E, I, H)) * 0.05).astype(np.float32))
+    pre = W.to_bf16_bits((rng.standard_normal((m_cap, 2 * I)) * 2).astype(np.float32))
+    rs = rng.uniform(0.5, 1.5, m_cap).astype(np.float32)
+    kw = dict(act=act, alpha=1.702 if act == "swiglu" else 1.0)
+    if clamp:
+        kw.update(gate_lo=-1.0, gate_hi=1.0, up_lo=-1.5, up_hi=1.5, up_offset=1.0)
+    d_counts = dev_i32(counts)
+    dgu = empty_bits((m_cap, 2 * I))
+    bufs = dict(row_q=empty_bytes((m_cap, 2 * I)), row_s=empty_bytes((m_cap, 2 * I // 32)),
+                col_q=empty_bytes((2 * I, m_cap)), col_s=empty_bytes((2 * I, (m_cap + 31) // 32 + E)))
+    d_rs = torch.from_numpy(rs).cuda()
+    G.moe_group_gemm_dglu_bwd(dev_bits(dy2), dev_bits(w2), H, I, G.groups(d_counts, m_cap),
+                              dev_bits(pre), G.epilogue(row_scale=d_rs, **kw), dgu,
+                              G.mx_out(**bufs))
+    _sync()
+    got = host_bits(dgu)
+    ref = O.dgrad_dglu(dy2[:M], counts, w2, pre[:M], O.Epilogue(row_scale=rs, **kw))
+    assert_bf16_close(got[:M], ref, what=f"dgu {act}", normwise=2e-2)
+    assert np.all(got[M:] == BF16_NAN_SENTINEL)
+    q, s = O.mx_quantize_rows(got[:M])
+    assert np.array_equal(bufs["row_q"].cpu().numpy()[:M], q)
+    assert np.array_equal(bufs["row_s"].cpu().numpy()[:M], s)
+    cq, cs = O.mx_quantize_cols(got[:M], counts, m_cap=m_cap)
+    used = O.mx_scale_col_offsets(counts)[-1]
+    assert np.array_equal(bufs["col_q"].cpu().numpy()[:, :M], cq[:, :M])
+    assert np.array_equal(bufs["col_s"].cpu().numpy()[:, :used], cs[:, :used])
+
+
+# ---------------------------------------------------------------- unfused baseline kernels
+def test_glu_unfused_and_mx_quantize_match_fused_on_exact_inputs(G):
+    """On integer-exact inputs the fused epilogue and the unfused chain
+    (GEMM -> GLU pass -> quantize pass) give identical bytes."""
+    import torch
+    counts = np.array([96, 0, 130, 33])
+    E, H, I = 4, 256, 128
+    M = int(counts.sum())
+    x = W.ternary_bf16(7, (M, H))
+    w1 = W.ternary_bf16(8, (E, H, 2 * I), density=0.3)
+    fused = _fc1_gpu(G, x, counts, w1, I, {}, mx=True)
+    d_counts = dev_i32(counts)
+    grp = G.groups(d_counts, M)
+    z = dev_bits(fused["preact"])
+    y = empty_bits((M, I))
+    G.moe_glu_unfused(z, grp, I, G.epilogue(), y)
+    bufs = dict(row_q=empty_bytes((M, I)), row_s=empty_bytes((M, I // 32)),
+                col_q=empty_bytes((I, M)), col_s=empty_bytes((I, (M + 31) // 32 + E)))
+    G.moe_mxfp8_quantize(y, M, I, grp, G.mx_out(**bufs))
+    _sync()
+    assert np.array_equal(host_bits(y), fused["y"])
+    for k in ("row_q", "row_s", "col_q", "col_s"):
+        assert np.array_equal(bufs[k].cpu().numpy(), fused[k]), k
+
+
+def test_glu_unfused_with_bias_against_oracle(G):
+    counts = np.array([50, 0, 77])
+    E, I = 3, 192
+    M = int(counts.sum())
+    rng = np.random.default_rng(41)
+    z = W.to_bf16_bits(rng.standard_normal((M, 2 * I)).astype(np.float32))
+    b = W.to_bf16_bits((rng.standard_normal((E, 2 * I)) * 0.1).astype(np.float32))
+    y = empty_bits((M, I))
+    G.moe_glu_unfused(dev_bits(z), G.groups(dev_i32(counts), M), I,
+                      G.epilogue(alpha=1.702, gate_lo=-7, gate_hi=7, up_lo=-7, up_hi=7,
+                                 bias=dev_bits(b)), y)
+    _sync()
+    zz = F.bf16_bits_to_f64(z)
+    off = [0, 50, 50, 127]
+    for e in range(E):
+        zz[off[e]:off[e + 1]] += F.bf16_bits_to_f64(b[e])[None, :]
+    ref = F.f64_to_bf16_bits(O.glu_from_preact(zz, O.Epilogue(alpha=1.702, gate_lo=-7, gate_hi=7,
+                                                              up_lo=-7, up_hi=7)))
+    assert_bf16_close(host_bits(y), ref, what="glu_unfused")
+
+
+def test_mxfp8_quantize_standalone_bit_exact(G):
+    rng = np.random.default_rng(51)
+    R, C = 77, 96
+    v = W.to_bf16_bits((rng.standard_t(3, size=(R, C)) * np.exp2(rng.integers(-20, 20, (R, 1))))
+                       .astype(np.float32))
+    bufs = dict(row_q=empty_bytes((R, C)), row_s=empty_bytes((R, C // 32)),
+                col_q=empty_bytes((C, R)), col_s=empty_bytes((C, (R + 31) // 32)))
+    G.moe_mxfp8_quantize(dev_bits(v), R, C, None, G.mx_out(**bufs))
+    _sync()
+    q, s = O.mx_quantize_rows(v)
+    assert np.array_equal(bufs["row_q"].cpu().numpy(), q)
+    assert np.array_equal(bufs["row_s"].cpu().numpy(), s)
+    cq, cs = O.mx_quantize_cols(v, [R], m_cap=R)
+    assert np.array_equal(bufs["col_q"].cpu().numpy(), cq)
+    assert np.array_equal(bufs["col_s"].cpu().numpy(), cs[:, :(R + 31) // 32])
