@@ -1,0 +1,278 @@
+"""Benchmark of the sync-free MoE expert MLP step on one MI355X.
+
+Workload: the DeepSeek-V3-like one-GPU expert share -- 32 experts, 16384
+routed rows with Zipf(1.1) counts (device-resident), hidden 7168, expert
+intermediate 2048, bf16 weights and activations, fp32 accumulation.  One step
+is the whole hot path:
+
+    FC1 + SwiGLU  (GroupGemm + Activation, packed W1, saves the pre-activation)
+    FC2           (GroupGemm, W2 [E][I][H])
+    dgrad + dSwiGLU (GroupGemm + dActivation: dY2 . W2^T, reads the pre-activation)
+    dX            (GroupGemm: d(gate|up) . W1^T through the packed W1)
+
+Inputs are synthetic and seeded (workloads.py) and already resident in HBM
+when the timed region starts.  `value` is the step's algorithmic TFLOP/s
+(sum over experts of 2 m_e K N for the four GEMMs) divided by the measured
+step time.  The dominant kernel (FC1) is also timed on its own with HIP events
+on the launch stream, for the roofline entry.  The CPU oracle is timed on a
+bounded sample of the same step for `cpu_baseline`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true", help="skip the unfused B1 timing")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON with HBM bytes per FC1 launch measured by rocprofv3 counters")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import grouped_gemm_glu_amd as G
+
+    torch.cuda.set_device(0)
+    G.moe_init(0)
+    dev = "cuda"
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    t0 = time.time()
+    d = W.dsv3(with_w2=True)
+    dy2_h = W.dsv3_dy2()
+    counts_h = d["counts"]
+    E, M, H, I = d["E"], d["M"], d["H"], d["I"]
+    log(f"inputs generated in {time.time() - t0:.1f}s; counts max {counts_h.max()} min {counts_h.min()}")
+
+    x = up(d["x"])
+    w1 = up(d["w1"])
+    w2 = up(d["w2"])
+    dy2 = up(dy2_h)
+    counts = torch.from_numpy(counts_h.astype(np.int32)).to(dev)
+    w1p = torch.empty((E, 2 * I, H), dtype=torch.int16, device=dev)
+    G.moe_repack_gate_up(w1, E, H, I, w1p)
+    y = torch.empty((M, I), dtype=torch.int16, device=dev)
+    pre = torch.empty((M, 2 * I), dtype=torch.int16, device=dev)
+    out2 = torch.empty((M, H), dtype=torch.int16, device=dev)
+    dgu = torch.empty((M, 2 * I), dtype=torch.int16, device=dev)
+    dx = torch.empty((M, H), dtype=torch.int16, device=dev)
+    grp = G.groups(counts, M)
+    ep = G.epilogue("swiglu")
+    op_y = G.operand(y)
+    op_w2 = G.operand(w2, layout=G.B_KN)
+    op_dgu = G.operand(dgu)
+    op_w1p = G.operand(w1p, layout=G.B_W1_PACKED_T)
+    torch.cuda.synchronize()
+
+    def fc1():
+        G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, y, pre)
+
+    def fc2():
+        G.moe_group_gemm_quant(op_y, op_w2, H, I, grp, out2)
+
+    def dglu():
+        G.moe_group_gemm_dglu_bwd(dy2, w2, H, I, grp, pre, ep, dgu)
+
+    def dxk():
+        G.moe_group_gemm_quant(op_dgu, op_w1p, H, 2 * I, grp, dx)
+
+    def step():
+        fc1()
+        fc2()
+        dglu()
+        dxk()
+
+    flop_row = 2 * H * 2 * I + 2 * I * H + 2 * H * I + 2 * 2 * I * H
+    step_flops = float(M) * flop_row
+    fc1_flops = 2.0 * M * H * 2 * I
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K eager steps; HIP events bracket every FC1 launch on
+    # the launch stream (torch's current stream, which the binding uses)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        fc1()
+        evs[i][1].record(stream)
+        fc2()
+        dglu()
+        dxk()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # ---- per-kernel times (events around each kernel alone), for the record
+    def time_kernel(fn, n=10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    kern_ms = {"fc1_glu": time_kernel(fc1), "fc2": time_kernel(fc2),
+               "dgrad_dglu": time_kernel(dglu), "dx": time_kernel(dxk)}
+
+    # ---- the same step as one hipGraph replay (no host sync inside)
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / args.steps
+    except Exception as exc:  # reported, never hides the eager number
+        log(f"graph capture failed: {exc!r}")
+
+    # ---- B1: the unfused chain on the same main loop (GEMM -> HBM -> GLU)
+    b1 = None
+    if not args.no_baselines:
+        w1t_plain = torch.empty((E, 2 * I, H), dtype=torch.int16, device=dev)
+        w1t_plain.copy_(w1.transpose(1, 2))
+        z = torch.empty((M, 2 * I), dtype=torch.int16, device=dev)
+        op_x = G.operand(x)
+        op_w1t = G.operand(w1t_plain, layout=G.B_NK)
+
+        def b1_chain():
+            G.moe_group_gemm_quant(op_x, op_w1t, 2 * I, H, grp, z)
+            G.moe_glu_unfused(z, grp, I, ep, y)
+
+        b1_ms = time_kernel(b1_chain)
+        b1 = {"fc1_unfused_ms": b1_ms, "fused_speedup": b1_ms / kern_ms["fc1_glu"]}
+        del w1t_plain, z
+
+    fc1_tflops = fc1_flops / (fc1_ms * 1e-3) / 1e12
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("fc1_hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, dy2_h)
+
+    rec = {
+        "metric": "fused MoE GroupGEMM+GLU TFLOP/s fwd & bwd and % MFMA peak, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Zipf(1.1) expert counts, N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": "DeepSeek-V3-like one-GPU expert share: FC1+SwiGLU, FC2, "
+                               "dgrad+dSwiGLU, dX",
+                   "experts": E, "routed_rows": M, "hidden": H, "intermediate": I,
+                   "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "moe_group_gemm_glu_fwd (FC1 + SwiGLU)",
+                     "achieved": round(fc1_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fc1_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(fc1_ms, 4),
+                     "algorithmic_flops_per_launch": fc1_flops},
+        "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "unfused_b1": b1,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(d, dy2_h):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    first 256 rows of 3 experts through FC1+SwiGLU, FC2, dgrad+dSwiGLU and dX
+    in float64 (numpy/BLAS), timed on this host's cores."""
+    from oracle import moe as O
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))       # BLAS threads actually used
+    counts = d["counts"]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    experts = [int(e) for e in np.argsort(-counts)[:3]]
+    rows = 256
+    H, I = d["H"], d["I"]
+    xs = np.concatenate([d["x"][off[e]:off[e] + rows] for e in experts])
+    dys = np.concatenate([dy2_h[off[e]:off[e] + rows] for e in experts])
+    c = np.array([rows] * 3)
+    w1 = d["w1"][experts]
+    w2 = d["w2"][experts]
+    ep = O.Epilogue()
+    t = time.perf_counter()
+    pre, y = O.fc1_glu(xs, c, w1, ep)
+    O.group_gemm(y, c, w2)
+    dgu = O.dgrad_dglu(dys, c, w2, pre, ep)
+    O.dx(dgu, c, w1)
+    dt = time.perf_counter() - t
+    flops = 3.0 * rows * (2 * H * 2 * I + 2 * I * H + 2 * H * I + 2 * 2 * I * H)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "first 256 rows of the 3 largest experts through the full step "
+                      "(FC1+SwiGLU, FC2, dgrad+dSwiGLU, dX), float64"}
+
+
+if __name__ == "__main__":
+    main()

@@ -67,9 +67,37 @@ struct GemmArgs {
   int ntiles_n;
 };
 
-__device__ __forceinline__ int swz_off(int r, int c) {
-  return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+// Physical 16-byte chunk of logical chunk c in operand-tile row r.  The XOR
+// key uses only row bits 0..4, so rows r and r + 32 share it and the four
+// 32-row MFMA blocks of a wave are immediate offsets from one address.  Eight
+// consecutive rows get eight different keys (bank-conflict free with 32 or 64
+// LDS banks for the 16-byte fragment reads).
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+__device__ __forceinline__ int swz_off(int r, int c) { return r * 128 + ((c ^ swz_key(r)) << 4); }
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes) (bytes clamped to 2^32 - 1).
+// gfx9 descriptor word 3: 32-bit data format, no swizzle, no stride.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0xFFFFFFFFll) bytes = 0xFFFFFFFFll;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(uint32_t)bytes, 0x00020000);
 }
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes lds_wave_base + 16 l (the LDS base is wave-uniform, held in M0).
+__device__ __forceinline__ void lds_dma16(const rsrc_t& rs, uint8_t* lds_wave_base,
+                                          uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+// Wait until every vector memory operation of this wave has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------- MX helpers
 __device__ __forceinline__ void store_bytes(uint8_t* dst, const uint32_t* w, int nvalid) {
@@ -190,7 +218,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
 
   build_group_scan<GM_NT>(gs, p.counts, p.E, p.M_cap, GM_BM, p.offsets_out, p.status_out,
@@ -202,22 +230,33 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   const int P = gridDim.x;
   const int slot = (P % 8 == 0) ? ((blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3)) : blockIdx.x;
   const int nk = p.K / GM_BK;
+  const int NT = p.ntiles_n;
+  // LDS-DMA lane coordinates: a wave instruction fills 8 rows x 128 B
+  const int rl = lane >> 3, pc = lane & 7;
 
   for (int tile = slot; tile < total_tiles; tile += P) {
-    // ---- decode (expert, m-tile, n-tile); expert e owns tiles
-    // [tile_off[e] * ntiles_n, tile_off[e+1] * ntiles_n), numbered m-fastest
+    // ---- decode (expert, m-tile, n-tile).  Expert e owns tiles
+    // [tile_off[e] * NT, tile_off[e+1] * NT).  Within an expert, tiles run in
+    // blocks of 4 m-tiles x 8 n-tiles (m fastest), so the run of consecutive
+    // ids an XCD takes per round shares few A panels and few B panels.
     int e, mt, nt;
     {
-      int lo = 0, hi = p.E;  // invariant: tile_off[lo]*ntiles_n <= tile < tile_off[hi]*ntiles_n
+      int lo = 0, hi = p.E;  // invariant: tile_off[lo]*NT <= tile < tile_off[hi]*NT
       while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
-        if (gs.tile_off[mid] * p.ntiles_n <= tile) lo = mid; else hi = mid;
+        if (gs.tile_off[mid] * NT <= tile) lo = mid; else hi = mid;
       }
       e = lo;
-      int local = tile - gs.tile_off[e] * p.ntiles_n;
-      int mtiles = gs.tile_off[e + 1] - gs.tile_off[e];
-      nt = local / mtiles;
-      mt = local - nt * mtiles;
+      const int local = tile - gs.tile_off[e] * NT;
+      const int MT = gs.tile_off[e + 1] - gs.tile_off[e];
+      constexpr int BHT = 4, BWT = 8;
+      const int band = local / (BHT * NT);
+      const int bh = min(BHT, MT - band * BHT);
+      const int l2 = local - band * BHT * NT;
+      const int nb = l2 / (bh * BWT);
+      const int l3 = l2 - nb * bh * BWT;
+      mt = band * BHT + l3 % bh;
+      nt = nb * BWT + l3 / bh;
     }
     const int g_row0 = gs.row_off[e];
     const int m_e = gs.row_off[e + 1] - g_row0;
@@ -225,35 +264,24 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     const int rows_valid = min(GM_BM, m_e - mt * GM_BM);
     const int n0 = nt * GM_BN;
 
-    const uint16_t* __restrict__ Ab = p.A + (long long)row0 * p.K;
-    const uint16_t* __restrict__ Bb = p.B + (long long)e * p.b_estride;
+    // ---- buffer descriptors: loads past the record count return zero, so
+    // rows past M_cap (A) or past N (K-contiguous B) need no clamping.
+    const uint32_t a_stride = (uint32_t)p.K * 2u;
+    const long long a_bytes = (long long)(p.M_cap - row0) * a_stride;
+    const rsrc_t rsA = make_rsrc(p.A + (long long)row0 * p.K, a_bytes);
+    const uint16_t* Bb = p.B + (long long)e * p.b_estride;
+    const uint32_t b_stride = (uint32_t)p.ldb * 2u;
+    rsrc_t rsB;
+    if (BLAY == BL_NK)
+      rsB = make_rsrc(Bb + (long long)n0 * p.ldb, (long long)(p.N - n0) * b_stride);
+    else
+      rsB = make_rsrc(Bb, p.b_estride * 2);
 
-    // ---- per-thread global load coordinates
-    // A and K-contiguous B: 8 rows (tid/8 + 32 i), one 16-byte chunk (tid % 8)
-    const int ld_r = tid >> 3, ld_c = tid & 7;
-    const uint16_t* a_src[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = ld_r + 32 * i;
-      r = r < rows_valid ? r : rows_valid - 1;
-      a_src[i] = Ab + (long long)r * p.K + ld_c * 8;
-    }
-    const uint16_t* b_src[8];
-    // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (8 rows)
+    // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (8 rows);
+    // the column chunk is clamped inside the row so no load leaves the matrix.
     const int kn_c = tid & 31, kn_g = tid >> 5;
-    if (BLAY == BL_NK) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int n = n0 + ld_r + 32 * i;
-        n = n < p.N ? n : p.N - 1;
-        b_src[i] = Bb + (long long)n * p.ldb + ld_c * 8;
-      }
-    } else {
-      int ncol = n0 + kn_c * 8;
-      ncol = ncol < p.N ? ncol : p.N - 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) b_src[i] = Bb + (long long)(kn_g * 8 + i) * p.ldb + ncol;
-    }
+    const uint32_t kn_voff =
+        (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -263,66 +291,68 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    uint4 ra[8], rb[8];
-    auto gload = [&](int kt) {
+    // direct global -> LDS of one 256 x 64 operand tile (swizzled layout).
+    // Instruction j of wave w fills rows 8 (8w + j) .. + 7; lane (rl, pc)
+    // lands on row 8 (8w + j) + rl, physical chunk pc, so it fetches logical
+    // chunk pc ^ key(row), key = rl ^ (j & 3).
+    auto issue_tile = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t stride, uint32_t koff) {
+      const uint32_t vrow = (uint32_t)(wave * 64 + rl) * stride;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + kt * GM_BK);
-      if (BLAY == BL_NK) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + kt * GM_BK);
-      } else {
-        long long krow;
-        if (BLAY == BL_KN) {
-          krow = (long long)kt * GM_BK;
-        } else {  // packed W1 read as W1^T: plain K tile -> packed row block
-          int j0 = kt * GM_BK;
-          krow = j0 < p.I ? 2LL * j0 : 2LL * (j0 - p.I) + 64;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + krow * p.ldb);
+      for (int j = 0; j < 8; ++j) {
+        const int c = pc ^ (rl ^ (j & 3));
+        const uint32_t voff = vrow + (uint32_t)(j * 8) * stride + (uint32_t)(c << 4);
+        lds_dma16(rs, lds_tile + (wave * 8 + j) * 1024, voff, koff);
       }
     };
-    auto lstore = [&](int stage) {
+    auto issue_direct = [&](int kt, int stage) {
       uint8_t* sa = smem + stage * GM_STAGE_BYTES;
-      uint8_t* sb = sa + GM_TILE_BYTES;
+      issue_tile(rsA, sa, a_stride, (uint32_t)kt * (GM_BK * 2));
+      if (BLAY == BL_NK) issue_tile(rsB, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * (GM_BK * 2));
+    };
+    u32x4 rb[8];
+    auto kn_load = [&](int kt) {
+      long long krow;
+      if (BLAY == BL_KN) {
+        krow = (long long)kt * GM_BK;
+      } else {  // packed W1 read as W1^T: plain K tile -> packed row block
+        const int j0 = kt * GM_BK;
+        krow = j0 < p.I ? 2LL * j0 : 2LL * (j0 - p.I) + 64;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint4*>(sa + swz_off(ld_r + 32 * i, ld_c)) = ra[i];
-      if (BLAY == BL_NK) {
+        rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rsB, kn_voff,
+                                                      (uint32_t)((krow + i) * b_stride), 0);
+    };
+    auto kn_store = [&](int stage) {
+      uint8_t* sb = smem + stage * GM_STAGE_BYTES + GM_TILE_BYTES;
+      // rb[i] holds 8 columns at k = 8*kn_g + i; transpose to 8 k-values per column
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint4*>(sb + swz_off(ld_r + 32 * i, ld_c)) = rb[i];
-      } else {
-        // rb[i] holds 8 columns at k = 8*kn_g + i; transpose to 8 k-values per column
-        uint32_t w[8][4];
+      for (int j = 0; j < 8; ++j) {
+        uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          w[i][0] = rb[i].x; w[i][1] = rb[i].y; w[i][2] = rb[i].z; w[i][3] = rb[i].w;
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = rb[2 * q][j >> 1], hi = rb[2 * q + 1][j >> 1];
+          o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          uint32_t o[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t lo = w[2 * q][j >> 1], hi = w[2 * q + 1][j >> 1];
-            o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-          }
-          *reinterpret_cast<uint4*>(sb + swz_off(kn_c * 8 + j, kn_g)) =
-              make_uint4(o[0], o[1], o[2], o[3]);
-        }
+        *reinterpret_cast<uint4*>(sb + swz_off(kn_c * 8 + j, kn_g)) =
+            make_uint4(o[0], o[1], o[2], o[3]);
       }
     };
 
-    gload(0);
-    lstore(0);
+    issue_direct(0, 0);
+    if (BLAY != BL_NK) {
+      kn_load(0);
+      kn_store(0);
+    }
+    wait_vmem_all();
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
+      if (kt + 1 < nk) {
+        issue_direct(kt + 1, cur ^ 1);
+        if (BLAY != BL_NK) kn_load(kt + 1);
+      }
       const uint8_t* sa = smem + cur * GM_STAGE_BYTES;
       const uint8_t* sb = sa + GM_TILE_BYTES;
 #pragma unroll
@@ -345,7 +375,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) lstore(cur ^ 1);
+      if (kt + 1 < nk && BLAY != BL_NK) kn_store(cur ^ 1);
+      wait_vmem_all();
       __syncthreads();
     }
 
