@@ -38,8 +38,21 @@ constexpr int GM_STAGE_BYTES = 2 * GM_TILE_BYTES;             // A + B
 constexpr int GM_MAIN_BYTES = 2 * GM_STAGE_BYTES;             // two stages: 128 KB
 constexpr int GM_STG_LD_256 = 264;                            // staged row, 256 cols (+16 B pad)
 constexpr int GM_STG_LD_128 = 136;                            // staged row, 128 cols (+16 B pad)
-constexpr int GM_STG_BYTES = GM_BM * GM_STG_LD_256 * 2;       // 132 KB
-constexpr int GM_SMEM_BYTES = GM_STG_BYTES > GM_MAIN_BYTES ? GM_STG_BYTES : GM_MAIN_BYTES;
+// Each of the two LDS stage arrays also holds one 128-row half of the staged
+// output tile in the epilogue (rows 0..127 in array 0, 128..255 in array 1).
+constexpr int GM_HALF_STG_BYTES = (GM_BM / 2) * GM_STG_LD_256 * 2;   // 66 KB
+constexpr int GM_STAGE_ALLOC =
+    GM_HALF_STG_BYTES > GM_STAGE_BYTES ? GM_HALF_STG_BYTES : GM_STAGE_BYTES;
+
+// Staged output tile split over the two stage arrays by row halves.
+struct Stg {
+  uint16_t* h0;
+  uint16_t* h1;
+  int ld;
+  __device__ __forceinline__ uint16_t* row(int r) const {
+    return (r < 128 ? h0 : h1) + (r & 127) * ld;
+  }
+};
 
 enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2 };
 enum { BL_NK = 0, BL_KN = 1, BL_W1T = 2 };
@@ -95,6 +108,15 @@ __device__ __forceinline__ void lds_dma16(const rsrc_t& rs, uint8_t* lds_wave_ba
       rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff, 0, 0);
 }
 
+// A zero the compiler cannot see through.  Epilogue addressing is derived
+// from it so that none of it is hoisted out of the tile loop, where it would
+// stay live across the main loop and push loop values into scratch.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
 // Wait until every vector memory operation of this wave has completed
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -148,16 +170,16 @@ __device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32
 // col-wise: blocks of 32 rows starting at the tile's first row (a tile always
 // starts a block because tiles start at group row multiples of 256), scale
 // column scol0 + r / 32.
-__device__ void mx_from_stage(const uint16_t* stg, int ld, int rows_valid, int ncols, int grow0,
+__device__ void mx_from_stage(const Stg& stg, int rows_valid, int ncols, int grow0,
                               int col0, const GemmArgs& p, int scol0) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x + opaque_zero();
   if (p.row_q) {
     const int nb = ncols >> 5;
     for (int it = t; it < GM_BM * nb; it += GM_NT) {
       int r = it / nb, cb = it - r * nb;
       if (r >= rows_valid) continue;
       float v[32];
-      const uint4* s = reinterpret_cast<const uint4*>(stg + r * ld + cb * 32);
+      const uint4* s = reinterpret_cast<const uint4*>(stg.row(r) + cb * 32);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint4 x = s[q];
@@ -185,7 +207,7 @@ __device__ void mx_from_stage(const uint16_t* stg, int ld, int rows_valid, int n
       if (nvalid > 32) nvalid = 32;
       float v[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(stg[(rb * 32 + i) * ld + c]);
+      for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(stg.row(rb * 32 + i)[c]);
       uint32_t w[8];
       uint8_t sb = mx_quant32(v, nvalid, w);
       long long gc = col0 + c;
@@ -196,15 +218,15 @@ __device__ void mx_from_stage(const uint16_t* stg, int ld, int rows_valid, int n
 }
 
 // Coalesced store of a staged bf16 tile (ncols % 8 == 0 assumed per 8-chunk validity).
-__device__ __forceinline__ void store_stage(const uint16_t* stg, int ld, int rows_valid,
+__device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
                                             int ncols_valid, int ncols_tile, uint16_t* dst,
                                             long long dst_ld) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x + opaque_zero();
   const int cpr = ncols_tile >> 3;  // 16-byte chunks per row
   for (int it = t; it < GM_BM * cpr; it += GM_NT) {
     int r = it / cpr, ch = it - r * cpr;
     if (r < rows_valid && ch * 8 < ncols_valid) {
-      uint4 v = *reinterpret_cast<const uint4*>(stg + r * ld + ch * 8);
+      uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
       *reinterpret_cast<uint4*>(dst + r * dst_ld + ch * 8) = v;
     }
   }
@@ -213,7 +235,11 @@ __device__ __forceinline__ void store_stage(const uint16_t* stg, int ld, int row
 // ---------------------------------------------------------------- the kernel
 template <int EPI, int BLAY>
 __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[GM_SMEM_BYTES];
+  // Two distinct stage arrays: the compiler can then see that the LDS-DMA
+  // writes of the next stage never alias the fragment reads of the current
+  // one, and does not wait for the prefetch before computing.
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[GM_STAGE_ALLOC];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[GM_STAGE_ALLOC];
   __shared__ GroupScan gs;
 
   const int tid = threadIdx.x;
@@ -264,6 +290,11 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     const int rows_valid = min(GM_BM, m_e - mt * GM_BM);
     const int n0 = nt * GM_BN;
 
+    // Per-tile opaque zero: main-loop addressing is recomputed for each tile,
+    // so it is not live across the epilogue.
+    const int zt = opaque_zero();
+    const int lane_t = lane + zt;
+
     // ---- buffer descriptors: loads past the record count return zero, so
     // rows past M_cap (A) or past N (K-contiguous B) need no clamping.
     const uint32_t a_stride = (uint32_t)p.K * 2u;
@@ -279,7 +310,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 
     // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (8 rows);
     // the column chunk is clamped inside the row so no load leaves the matrix.
-    const int kn_c = tid & 31, kn_g = tid >> 5;
+    const int kn_c = (tid + zt) & 31, kn_g = (tid + zt) >> 5;
     const uint32_t kn_voff =
         (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
 
@@ -295,36 +326,43 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // Instruction j of wave w fills rows 8 (8w + j) .. + 7; lane (rl, pc)
     // lands on row 8 (8w + j) + rl, physical chunk pc, so it fetches logical
     // chunk pc ^ key(row), key = rl ^ (j & 3).
+    const int rl_t = lane_t >> 3, pc_t = lane_t & 7;
     auto issue_tile = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t stride, uint32_t koff) {
-      const uint32_t vrow = (uint32_t)(wave * 64 + rl) * stride;
+      const uint32_t vrow = (uint32_t)(wave * 64 + rl_t) * stride;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int c = pc ^ (rl ^ (j & 3));
+        const int c = pc_t ^ (rl_t ^ (j & 3));
         const uint32_t voff = vrow + (uint32_t)(j * 8) * stride + (uint32_t)(c << 4);
         lds_dma16(rs, lds_tile + (wave * 8 + j) * 1024, voff, koff);
       }
     };
-    auto issue_direct = [&](int kt, int stage) {
-      uint8_t* sa = smem + stage * GM_STAGE_BYTES;
-      issue_tile(rsA, sa, a_stride, (uint32_t)kt * (GM_BK * 2));
-      if (BLAY == BL_NK) issue_tile(rsB, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * (GM_BK * 2));
+    // K-tiles past the end are fetched through a descriptor with no records:
+    // the loads return zeros, so the main loop needs no tail branch.
+    const rsrc_t rsZ = make_rsrc(p.A, 0);
+    auto issue_direct = [&](int kt, uint8_t* sa) {
+      const bool in = kt < nk;
+      issue_tile(in ? rsA : rsZ, sa, a_stride, (uint32_t)kt * (GM_BK * 2));
+      if (BLAY == BL_NK)
+        issue_tile(in ? rsB : rsZ, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * (GM_BK * 2));
     };
     u32x4 rb[8];
     auto kn_load = [&](int kt) {
+      const bool in = kt < nk;
+      const int ktc = in ? kt : 0;
       long long krow;
       if (BLAY == BL_KN) {
-        krow = (long long)kt * GM_BK;
+        krow = (long long)ktc * GM_BK;
       } else {  // packed W1 read as W1^T: plain K tile -> packed row block
-        const int j0 = kt * GM_BK;
+        const int j0 = ktc * GM_BK;
         krow = j0 < p.I ? 2LL * j0 : 2LL * (j0 - p.I) + 64;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rsB, kn_voff,
+        rb[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsB : rsZ, kn_voff,
                                                       (uint32_t)((krow + i) * b_stride), 0);
     };
-    auto kn_store = [&](int stage) {
-      uint8_t* sb = smem + stage * GM_STAGE_BYTES + GM_TILE_BYTES;
+    auto kn_store = [&](uint8_t* stage) {
+      uint8_t* sb = stage + GM_TILE_BYTES;
       // rb[i] holds 8 columns at k = 8*kn_g + i; transpose to 8 k-values per column
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -339,160 +377,231 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       }
     };
 
-    issue_direct(0, 0);
-    if (BLAY != BL_NK) {
-      kn_load(0);
-      kn_store(0);
-    }
-    wait_vmem_all();
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        issue_direct(kt + 1, cur ^ 1);
-        if (BLAY != BL_NK) kn_load(kt + 1);
-      }
-      const uint8_t* sa = smem + cur * GM_STAGE_BYTES;
+    // Fragments are double-buffered one k-step ahead; the scheduling barriers
+    // keep the compiler from hoisting a whole K-tile of LDS reads (which
+    // would need ~128 more VGPRs than the loop has).
+    auto compute = [&](const uint8_t* sa) {
       const uint8_t* sb = sa + GM_TILE_BYTES;
+      bf16x8 af[2][4], bfr[2][4];
+      auto frag_load = [&](int ks, int buf) {
+        const int ch = ks * 2 + (lane_t >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[buf][i] = *reinterpret_cast<const bf16x8*>(
+              sa + swz_off(wm * 128 + i * 32 + (lane_t & 31), ch));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bfr[buf][j] = *reinterpret_cast<const bf16x8*>(
+              sb + swz_off(wn * 128 + j * 32 + (lane_t & 31), ch));
+      };
+      frag_load(0, 0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int ch = ks * 2 + (lane >> 5);
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int r = wm * 128 + i * 32 + (lane & 31);
-          af[i] = *reinterpret_cast<const bf16x8*>(sa + swz_off(r, ch));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int r = wn * 128 + j * 32 + (lane & 31);
-          bfr[j] = *reinterpret_cast<const bf16x8*>(sb + swz_off(r, ch));
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks < 3) frag_load(ks + 1, (ks + 1) & 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][j], af[ks & 1][i],
+                                                                acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk && BLAY != BL_NK) kn_store(cur ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Two K-tiles per iteration, stage arrays used in a fixed order so every
+    // LDS access names its array directly.  With an odd tile count the last
+    // step computes a zero tile.
+    issue_direct(0, lds0);
+    if (BLAY != BL_NK) {
+      kn_load(0);
+      kn_store(lds0);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      issue_direct(kt + 1, lds1);
+      if (BLAY != BL_NK) kn_load(kt + 1);
+      compute(lds0);
+      if (BLAY != BL_NK) kn_store(lds1);
+      wait_vmem_all();
+      __syncthreads();
+      issue_direct(kt + 2, lds0);
+      if (BLAY != BL_NK) kn_load(kt + 2);
+      compute(lds1);
+      if (BLAY != BL_NK) kn_store(lds0);
       wait_vmem_all();
       __syncthreads();
     }
 
     // ================================================================ epilogues
-    // Accumulator element r of block (i, j): tile row wm*128 + 32 i + 8 (r/4)
-    // + 4 (lane/32) + r%4, tile column wn*128 + 32 j + lane%32.
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem);
-    const int lrow = 4 * (lane >> 5);
-    const int lcol = lane & 31;
+    // The MFMAs compute D = W X^T per 32 x 32 block, so accumulator element r
+    // of block (i, j) is
+    //   tile row    m = wm*128 + 32 i + lane%32
+    //   tile column n = wn*128 + 32 j + 8 (r/4) + 4 (lane/32) + r%4,
+    // i.e. each lane holds runs of 4 consecutive columns of one row.
+    const int z0 = opaque_zero();
+    // this wave's rows (wm*128 ..) live in stage array wm
+    uint16_t* wstg = reinterpret_cast<uint16_t*>(wm ? lds1 : lds0) + z0;
+    const int lm = (lane & 31) + z0;
+    const int ln = 4 * (lane >> 5) + z0;
+    float rsc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wm * 128 + 32 * i + lm;
+      rsc[i] = (p.ep.row_scale && m < rows_valid) ? p.ep.row_scale[row0 + m] : 1.0f;
+    }
 
     if (EPI == EPI_GLU) {
-      // packed pair wn of this tile: gate = blocks j = 0, 1; up = j = 2, 3
+      // pair wn of this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3
       const int ld = GM_STG_LD_128;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int ycol = wn * 64 + jj * 32 + lcol;          // y column within the tile
-        const int c = nt * 128 + ycol;                      // global gate column / y column
-        const bool cvalid = c < p.I;
-        float bg = 0.0f, bu = 0.0f;
-        if (p.ep.bias && cvalid) {
-          bg = bf16_to_f32(p.ep.bias[(long long)e * 2 * p.I + c]);
-          bu = bf16_to_f32(p.ep.bias[(long long)e * 2 * p.I + p.I + c]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int trow = wm * 128 + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-            float g = acc[i][jj][r] + bg;
-            float u = acc[i][jj + 2][r] + bu;
-            const bool rvalid = trow < rows_valid;
-            if (p.preact && rvalid && cvalid) {
-              uint16_t* pr = p.preact + (long long)(row0 + trow) * 2 * p.I;
-              pr[c] = f32_to_bf16(g);
-              pr[p.I + c] = f32_to_bf16(u);
-            }
-            float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
-            float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
-            float y = act_fwd(p.ep.act, gc, p.ep.alpha) * uc;
-            if (p.ep.row_scale && rvalid) y *= p.ep.row_scale[row0 + trow];
-            stg[trow * ld + ycol] = f32_to_bf16(y);
-          }
-        }
-      }
-      __syncthreads();
       const int cvalid_n = min(128, p.I - nt * 128);
-      if (p.C)
-        store_stage(stg, ld, rows_valid, cvalid_n, 128, p.C + (long long)row0 * p.I + nt * 128, p.I);
-      if (p.row_q || p.col_q)
-        mx_from_stage(stg, ld, rows_valid, cvalid_n, row0, nt * 128, p, gs.mxs_off[e] + mt * 8);
-      __syncthreads();
-    } else if (EPI == EPI_STORE) {
-      const int ld = GM_STG_LD_256;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int trow = wm * 128 + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-            const int tcol = wn * 128 + j * 32 + lcol;
-            stg[trow * ld + tcol] = f32_to_bf16(acc[i][j][r]);
-          }
-      __syncthreads();
-      const int cvalid_n = min(GM_BN, p.N - n0);
-      if (p.C)
-        store_stage(stg, ld, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
-      if (p.row_q || p.col_q)
-        mx_from_stage(stg, ld, rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
-      __syncthreads();
-    } else {  // EPI_DGLU: acc = G = dL/dy for columns n0 .. n0+255 of I
-      const int ld = GM_STG_LD_256;
       const long long ld2 = 2LL * p.I;
-      // pass 0 stages dg, pass 1 stages du
+      const uint16_t* bias_e = p.ep.bias ? p.ep.bias + (long long)e * ld2 : nullptr;
+      // round 0: y; round 1: gate pre-activation; round 2: up pre-activation
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
+      for (int round = 0; round < 3; ++round) {
+        if (round > 0 && !p.preact) break;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tcol = wn * 128 + j * 32 + lcol;
-          const int c = n0 + tcol;
-          const bool cvalid = c < p.I;
+        for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int ycol = wn * 64 + 32 * jj + 8 * q + ln;   // 4 consecutive y columns
+            const int c = nt * 128 + ycol;                    // global gate column
+            float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias_e && c < p.I) {
+              const uint2 vg = *reinterpret_cast<const uint2*>(bias_e + c);
+              const uint2 vu = *reinterpret_cast<const uint2*>(bias_e + p.I + c);
+              bg[0] = __uint_as_float(vg.x << 16); bg[1] = __uint_as_float(vg.x & 0xFFFF0000u);
+              bg[2] = __uint_as_float(vg.y << 16); bg[3] = __uint_as_float(vg.y & 0xFFFF0000u);
+              bu[0] = __uint_as_float(vu.x << 16); bu[1] = __uint_as_float(vu.x & 0xFFFF0000u);
+              bu[2] = __uint_as_float(vu.y << 16); bu[3] = __uint_as_float(vu.y & 0xFFFF0000u);
+            }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int trow = wm * 128 + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-              float out = 0.0f;
-              if (trow < rows_valid && cvalid) {
-                const uint16_t* pr = p.preact + (long long)(row0 + trow) * ld2;
-                float g = bf16_to_f32(pr[c]);
-                float u = bf16_to_f32(pr[p.I + c]);
-                float G = acc[i][j][r];
-                if (p.ep.row_scale) G *= p.ep.row_scale[row0 + trow];
-                float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
-                float a, da;
-                act_fwd_bwd(p.ep.act, gc, p.ep.alpha, a, da);
-                if (pass == 0) {
-                  float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
-                  bool gin = (g >= p.ep.gate_lo) && (g <= p.ep.gate_hi);
-                  out = gin ? G * uc * da : 0.0f;
+            for (int i = 0; i < 4; ++i) {
+              const int m = wm * 128 + 32 * i + lm;
+              float o[4];
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) {
+                const float g = acc[i][jj][4 * q + s2] + bg[s2];
+                const float u = acc[i][jj + 2][4 * q + s2] + bu[s2];
+                if (round == 0) {
+                  const float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
+                  const float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
+                  o[s2] = act_fwd(p.ep.act, gc, p.ep.alpha) * uc * rsc[i];
                 } else {
-                  bool uin = (u >= p.ep.up_lo) && (u <= p.ep.up_hi);
-                  out = uin ? G * a : 0.0f;
+                  o[s2] = round == 1 ? g : u;
                 }
               }
-              stg[trow * ld + tcol] = f32_to_bf16(out);
+              *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + ycol) =
+                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
           }
         }
         __syncthreads();
-        const int cvalid_n = min(GM_BN, p.I - n0);
-        const int ccol0 = (pass == 0 ? 0 : p.I) + n0;
+        if (round == 0) {
+          if (p.C)
+            store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, 128, p.C + (long long)row0 * p.I + nt * 128,
+                        p.I);
+          if (p.row_q || p.col_q)
+            mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, row0, nt * 128, p, gs.mxs_off[e] + mt * 8);
+        } else {
+          const int col0 = (round == 1 ? 0 : p.I) + nt * 128;
+          store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, 128, p.preact + (long long)row0 * ld2 + col0,
+                      ld2);
+        }
+        __syncthreads();
+      }
+    } else if (EPI == EPI_STORE) {
+      const int ld = GM_STG_LD_256;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 128 + 32 * i + lm;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int n = wn * 128 + 32 * j + 8 * q + ln;
+            *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + n) =
+                make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                           pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          }
+      }
+      __syncthreads();
+      const int cvalid_n = min(GM_BN, p.N - n0);
+      if (p.C)
+        store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
+      if (p.row_q || p.col_q)
+        mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
+      __syncthreads();
+    } else {  // EPI_DGLU: acc = G = dL/dy for columns n0 .. n0+255 of I
+      const int ld = GM_STG_LD_256;
+      const long long ld2 = 2LL * p.I;
+      const int cvalid_n = min(GM_BN, p.I - n0);
+      // round 0: dg staged, du kept as packed bf16 in registers; round 1: du staged
+      uint32_t dupk[4][4][4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int n = wn * 128 + 32 * j + 8 * q + ln;
+          const int c = n0 + n;                        // column of I (4 consecutive)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = wm * 128 + 32 * i + lm;
+            float dg[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
+            if (m < rows_valid && c < p.I) {
+              const uint16_t* pr = p.preact + (long long)(row0 + m) * ld2 + c;
+              const uint2 vg = *reinterpret_cast<const uint2*>(pr);
+              const uint2 vu = *reinterpret_cast<const uint2*>(pr + p.I);
+              const float gv[4] = {__uint_as_float(vg.x << 16), __uint_as_float(vg.x & 0xFFFF0000u),
+                                   __uint_as_float(vg.y << 16), __uint_as_float(vg.y & 0xFFFF0000u)};
+              const float uv[4] = {__uint_as_float(vu.x << 16), __uint_as_float(vu.x & 0xFFFF0000u),
+                                   __uint_as_float(vu.y << 16), __uint_as_float(vu.y & 0xFFFF0000u)};
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) {
+                const float G = acc[i][j][4 * q + s2] * rsc[i];
+                const float g = gv[s2], u = uv[s2];
+                const float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
+                const float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
+                float a, da;
+                act_fwd_bwd(p.ep.act, gc, p.ep.alpha, a, da);
+                const bool gin = (g >= p.ep.gate_lo) && (g <= p.ep.gate_hi);
+                const bool uin = (u >= p.ep.up_lo) && (u <= p.ep.up_hi);
+                dg[s2] = gin ? G * uc * da : 0.0f;
+                du[s2] = uin ? G * a : 0.0f;
+              }
+            }
+            *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + n) =
+                make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            dupk[i][j][q][0] = pack_bf16x2(du[0], du[1]);
+            dupk[i][j][q][1] = pack_bf16x2(du[2], du[3]);
+          }
+        }
+#pragma unroll
+      for (int round = 0; round < 2; ++round) {
+        if (round == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = wm * 128 + 32 * i + lm;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int n = wn * 128 + 32 * j + 8 * q + ln;
+                *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + n) =
+                    make_uint2(dupk[i][j][q][0], dupk[i][j][q][1]);
+              }
+          }
+        }
+        __syncthreads();
+        const int ccol0 = (round == 0 ? 0 : p.I) + n0;
         if (p.C)
-          store_stage(stg, ld, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * ld2 + ccol0, ld2);
+          store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * ld2 + ccol0, ld2);
         if (p.row_q || p.col_q)
-          mx_from_stage(stg, ld, rows_valid, cvalid_n, row0, ccol0, p, gs.mxs_off[e] + mt * 8);
+          mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, row0, ccol0, p, gs.mxs_off[e] + mt * 8);
         __syncthreads();
       }
     }

@@ -194,7 +194,7 @@ def test_fc1_mx_epilogue_matches_oracle_quantisation(G):
     quantisation of the GPU's own bf16 y byte for byte, and y itself is within
     tolerance of the oracle."""
     counts = np.array([70, 0, 33, 256, 1, 300])
-    E, H, I = len(counts), 128, 256
+    E, H, I = len(counts), 192, 256          # K = 192: an odd number of 64-deep K-tiles
     m_cap = int(counts.sum()) + 5
     d = W.small_grouped(12, counts, H, I, m_cap=m_cap)
     x = W.student_t_rows_bf16(12, m_cap, H)
