@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true", help="skip the unfused B1 timing")
     ap.add_argument("--traffic", type=str, default=None,
                     help="JSON with HBM bytes per FC1 launch measured by rocprofv3 counters")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 3 times (a known-size "
+                         "reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -202,6 +205,17 @@ def main():
     if args.traffic and os.path.exists(args.traffic):
         with open(args.traffic) as f:
             traffic = json.load(f).get("fc1_hbm_bytes_per_launch")
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 2
+        src_c = torch.empty(n, dtype=torch.int16, device=dev).fill_(1)
+        dst_c = torch.empty_like(src_c)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.calibrate_copy_mib} MiB device copies")
+        del src_c, dst_c
 
     cpu = None
     if not args.no_cpu_baseline:

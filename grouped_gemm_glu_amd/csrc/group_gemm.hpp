@@ -383,16 +383,20 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     auto compute = [&](const uint8_t* sa) {
       const uint8_t* sb = sa + GM_TILE_BYTES;
       bf16x8 af[2][4], bfr[2][4];
+      // reads in order of first use by the MFMA sequence (i outer, j inner)
       auto frag_load = [&](int ks, int buf) {
         const int ch = ks * 2 + (lane_t >> 5);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+        auto rd_a = [&](int i) {
           af[buf][i] = *reinterpret_cast<const bf16x8*>(
               sa + swz_off(wm * 128 + i * 32 + (lane_t & 31), ch));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        };
+        auto rd_b = [&](int j) {
           bfr[buf][j] = *reinterpret_cast<const bf16x8*>(
               sb + swz_off(wn * 128 + j * 32 + (lane_t & 31), ch));
+        };
+        rd_a(0);
+        rd_b(0); rd_b(1); rd_b(2); rd_b(3);
+        rd_a(1); rd_a(2); rd_a(3);
       };
       frag_load(0, 0);
 #pragma unroll
@@ -405,6 +409,16 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][j], af[ks & 1][i],
                                                                 acc[i][j], 0, 0, 0);
+        // issue order: the next k-step's 8 LDS reads one per MFMA over the
+        // first 8 MFMAs, so each has at least 8 MFMAs of cover before use
+        if (ks < 3) {
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMA
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
