@@ -40,8 +40,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true", help="skip the unfused B1 timing")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON with HBM bytes per FC1 launch measured by rocprofv3 counters")
+    ap.add_argument("--traffic", type=str,
+                    default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                         "fc1_glu_dsv3_traffic.json"),
+                    help="JSON with HBM bytes per FC1 launch measured by rocprofv3 counters "
+                         "(used only while the kernel source still matches its recorded hash)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a known-size "
                          "reference for the HBM byte counters)")
@@ -201,10 +204,7 @@ def main():
     fc1_tflops = fc1_flops / (fc1_ms * 1e-3) / 1e12
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("fc1_hbm_bytes_per_launch")
+    traffic = read_traffic(args.traffic)
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 2
@@ -252,10 +252,30 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(d, dy2_h):
+def read_traffic(path):
+    """HBM bytes per FC1 launch from the committed counter record, or None when
+    the record is missing or the GEMM kernel source changed since it was taken."""
+    import hashlib
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    root = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(root, rec.get("kernel_source", ""))
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    if h != rec.get("source_sha256_16"):
+        return None
+    return rec.get("fc1_hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, dy2_h, rows_per_expert=768):
     """The oracle, as it stands, on a bounded sample of the same step: the
-    first 256 rows of 3 experts through FC1+SwiGLU, FC2, dgrad+dSwiGLU and dX
-    in float64 (numpy/BLAS), timed on this host's cores."""
+    first min(m_e, 768) rows of every expert through FC1+SwiGLU, FC2,
+    dgrad+dSwiGLU and dX in float64 (numpy/BLAS), timed on this host's cores
+    (about 10-20 s of CPU work)."""
     from oracle import moe as O
     try:
         cores = len(os.sched_getaffinity(0))
@@ -266,25 +286,22 @@ def cpu_baseline(d, dy2_h):
         cores = min(cores, int(omp))       # BLAS threads actually used
     counts = d["counts"]
     off = np.concatenate([[0], np.cumsum(counts)])
-    experts = [int(e) for e in np.argsort(-counts)[:3]]
-    rows = 256
     H, I = d["H"], d["I"]
-    xs = np.concatenate([d["x"][off[e]:off[e] + rows] for e in experts])
-    dys = np.concatenate([dy2_h[off[e]:off[e] + rows] for e in experts])
-    c = np.array([rows] * 3)
-    w1 = d["w1"][experts]
-    w2 = d["w2"][experts]
+    c = np.minimum(counts, rows_per_expert).astype(np.int64)
+    sel = np.concatenate([np.arange(off[e], off[e] + c[e]) for e in range(len(counts))])
+    xs, dys = d["x"][sel], dy2_h[sel]
     ep = O.Epilogue()
     t = time.perf_counter()
-    pre, y = O.fc1_glu(xs, c, w1, ep)
-    O.group_gemm(y, c, w2)
-    dgu = O.dgrad_dglu(dys, c, w2, pre, ep)
-    O.dx(dgu, c, w1)
+    pre, y = O.fc1_glu(xs, c, d["w1"], ep)
+    O.group_gemm(y, c, d["w2"])
+    dgu = O.dgrad_dglu(dys, c, d["w2"], pre, ep)
+    O.dx(dgu, c, d["w1"])
     dt = time.perf_counter() - t
-    flops = 3.0 * rows * (2 * H * 2 * I + 2 * I * H + 2 * H * I + 2 * 2 * I * H)
+    flops = float(c.sum()) * (2 * H * 2 * I + 2 * I * H + 2 * H * I + 2 * 2 * I * H)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "first 256 rows of the 3 largest experts through the full step "
+            "sample": f"first min(m_e, {rows_per_expert}) rows of each of the 32 experts "
+                      f"({int(c.sum())} of {int(counts.sum())} rows) through the full step "
                       "(FC1+SwiGLU, FC2, dgrad+dSwiGLU, dX), float64"}
 
 
