@@ -85,8 +85,18 @@ def main():
     w2 = up(d["w2"])
     dy2 = up(dy2_h)
     counts = torch.from_numpy(counts_h.astype(np.int32)).to(dev)
-    w1p = torch.empty((E, 2 * I, H), dtype=torch.int16, device=dev)
+    # offline weight preparation (not timed): the gate/up-repacked W1 for FC1 and
+    # tile-blocked copies of W1 (dX) and W2 (FC2, dgrad)
+    def packed(n_bytes):
+        return torch.empty(n_bytes // 2, dtype=torch.int16, device=dev)
+    w1p = packed(G.moe_packed_w1_bytes(E, H, I))
     G.moe_repack_gate_up(w1, E, H, I, w1p)
+    w1x = packed(G.moe_packed_weight_bytes(E, H, 2 * I))
+    G.moe_pack_weight(w1, E, H, 2 * I, G.B_NK, w1x)
+    w2f = packed(G.moe_packed_weight_bytes(E, H, I))
+    G.moe_pack_weight(w2, E, H, I, G.B_KN, w2f)
+    w2d = packed(G.moe_packed_weight_bytes(E, I, H))
+    G.moe_pack_weight(w2, E, I, H, G.B_NK, w2d)
     y = torch.empty((M, I), dtype=torch.int16, device=dev)
     pre = torch.empty((M, 2 * I), dtype=torch.int16, device=dev)
     out2 = torch.empty((M, H), dtype=torch.int16, device=dev)
@@ -95,9 +105,10 @@ def main():
     grp = G.groups(counts, M)
     ep = G.epilogue("swiglu")
     op_y = G.operand(y)
-    op_w2 = G.operand(w2, layout=G.B_KN)
+    op_w2 = G.operand(w2f, layout=G.B_PACKED)
+    op_w2d = G.operand(w2d, layout=G.B_PACKED)
     op_dgu = G.operand(dgu)
-    op_w1p = G.operand(w1p, layout=G.B_W1_PACKED_T)
+    op_w1x = G.operand(w1x, layout=G.B_PACKED)
     torch.cuda.synchronize()
 
     def fc1():
@@ -107,10 +118,10 @@ def main():
         G.moe_group_gemm_quant(op_y, op_w2, H, I, grp, out2)
 
     def dglu():
-        G.moe_group_gemm_dglu_bwd(dy2, w2, H, I, grp, pre, ep, dgu)
+        G.moe_group_gemm_dglu_bwd(dy2, op_w2d, H, I, grp, pre, ep, dgu)
 
     def dxk():
-        G.moe_group_gemm_quant(op_dgu, op_w1p, H, 2 * I, grp, dx)
+        G.moe_group_gemm_quant(op_dgu, op_w1x, H, 2 * I, grp, dx)
 
     def step():
         fc1()
@@ -187,11 +198,13 @@ def main():
     # ---- B1: the unfused chain on the same main loop (GEMM -> HBM -> GLU)
     b1 = None
     if not args.no_baselines:
-        w1t_plain = torch.empty((E, 2 * I, H), dtype=torch.int16, device=dev)
-        w1t_plain.copy_(w1.transpose(1, 2))
+        # same main loop on a tile-blocked W1 in PLAIN column order (N = 2I, K = H),
+        # writing the bf16 pre-activation, then the unfused GLU kernel
+        w1t_plain = packed(G.moe_packed_weight_bytes(E, 2 * I, H))
+        G.moe_pack_weight(w1, E, 2 * I, H, G.B_KN, w1t_plain)
         z = torch.empty((M, 2 * I), dtype=torch.int16, device=dev)
         op_x = G.operand(x)
-        op_w1t = G.operand(w1t_plain, layout=G.B_NK)
+        op_w1t = G.operand(w1t_plain, layout=G.B_PACKED)
 
         def b1_chain():
             G.moe_group_gemm_quant(op_x, op_w1t, 2 * I, H, grp, z)

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoeglu.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m grouped_gemm_glu_amd.build` (needs hipcc)")
+        f"{LIB_PATH} is not built; run `python grouped_gemm_glu_amd/build.py` (needs hipcc)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOE_OK = 0
 ACT = {"swiglu": 0, "geglu": 1, "geglu_tanh": 2, "srelu": 3}
 DT_BF16, DT_MXFP8 = 0, 1
-B_KN, B_NK, B_W1_PACKED_T = 0, 1, 2
+B_KN, B_NK, B_PACKED = 0, 1, 2
 
 
 class EpilogueT(ctypes.Structure):
@@ -58,12 +58,14 @@ _SIGS = {
     "moe_init": ([_I], _I),
     "moe_status_string": ([_I], ctypes.c_char_p),
     "moe_packed_w1_bytes": ([_I, _I, _I], ctypes.c_size_t),
+    "moe_packed_weight_bytes": ([_I, _I, _I], ctypes.c_size_t),
+    "moe_pack_weight": ([_P, _I, _I, _I, _I, _P, _P], _I),
     "moe_repack_gate_up": ([_P, _I, _I, _I, _P, _P], _I),
     "moe_unpack_gate_up": ([_P, _I, _I, _I, _P, _P], _I),
     "moe_route_group": ([_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P], _I),
     "moe_group_gemm_glu_fwd": ([_P, ctypes.POINTER(GroupsT), _P, _I, _I,
                                 ctypes.POINTER(EpilogueT), _P, _P, ctypes.POINTER(MxOutT), _I, _P], _I),
-    "moe_group_gemm_dglu_bwd": ([_P, _P, _I, _I, ctypes.POINTER(GroupsT), _P,
+    "moe_group_gemm_dglu_bwd": ([_P, ctypes.POINTER(OperandT), _I, _I, ctypes.POINTER(GroupsT), _P,
                                  ctypes.POINTER(EpilogueT), _P, ctypes.POINTER(MxOutT), _I, _P], _I),
     "moe_group_gemm_quant": ([ctypes.POINTER(OperandT), ctypes.POINTER(OperandT), _I, _I,
                               ctypes.POINTER(GroupsT), _P, ctypes.POINTER(MxOutT), _I, _P], _I),
@@ -151,6 +153,15 @@ def moe_packed_w1_bytes(E: int, H: int, I: int) -> int:
     return _lib.moe_packed_w1_bytes(E, H, I)
 
 
+def moe_packed_weight_bytes(E: int, N: int, K: int) -> int:
+    return _lib.moe_packed_weight_bytes(E, N, K)
+
+
+def moe_pack_weight(src, E, N, K, src_layout, dst, stream=None):
+    _check("moe_pack_weight",
+           _lib.moe_pack_weight(_ptr(src), E, N, K, src_layout, _ptr(dst), _stream(stream)))
+
+
 def moe_repack_gate_up(w1, E, H, I, w1_packed, stream=None):
     _check("moe_repack_gate_up",
            _lib.moe_repack_gate_up(_ptr(w1), E, H, I, _ptr(w1_packed), _stream(stream)))
@@ -177,10 +188,10 @@ def moe_group_gemm_glu_fwd(xg, grp: GroupsT, w1_packed, H, I, ep: EpilogueT, y=N
                                        cu_margin, _stream(stream)))
 
 
-def moe_group_gemm_dglu_bwd(dy2, w2, H, I, grp: GroupsT, preact, ep: EpilogueT, dgu=None,
+def moe_group_gemm_dglu_bwd(dy2, w2: OperandT, H, I, grp: GroupsT, preact, ep: EpilogueT, dgu=None,
                             mx: Optional[MxOutT] = None, cu_margin: int = 0, stream=None):
     _check("moe_group_gemm_dglu_bwd",
-           _lib.moe_group_gemm_dglu_bwd(_ptr(dy2), _ptr(w2), H, I, ctypes.byref(grp),
+           _lib.moe_group_gemm_dglu_bwd(_ptr(dy2), ctypes.byref(w2), H, I, ctypes.byref(grp),
                                         _ptr(preact), ctypes.byref(ep), _ptr(dgu), _ref(mx),
                                         cu_margin, _stream(stream)))
 

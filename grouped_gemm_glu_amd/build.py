@@ -1,6 +1,6 @@
 """Build libmoeglu.so (the HIP library) in-tree for gfx950 with hipcc.
 
-Usage:  python -m grouped_gemm_glu_amd.build [--jobs N] [--verbose]
+Usage:  python grouped_gemm_glu_amd/build.py [--jobs N] [--verbose]
 
 Each .hip translation unit is compiled to an object in parallel, then linked
 into grouped_gemm_glu_amd/libmoeglu.so.  Every HIP compile disables the

@@ -119,33 +119,50 @@ const char* moe_status_string(moe_status_t s) {
   return "unknown status";
 }
 
-size_t moe_packed_w1_bytes(int E, int H, int I) {
-  if (E <= 0 || H <= 0 || I <= 0) return 0;
-  return (size_t)E * 2 * (size_t)I * (size_t)H * 2;
+size_t moe_packed_weight_bytes(int E, int N, int K) {
+  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  return (size_t)E * (size_t)((N + 255) / 256) * 256 * (size_t)K * 2;
 }
 
-static moe_status_t repack_common(const void* src, int E, int H, int I, void* dst, void* stream,
-                                  int unpack) {
-  if (!src || !dst) return MOE_ERR_NULL;
-  if (E < 1 || H < 1 || I < 64 || I % 64 != 0 || H % 8 != 0) return MOE_ERR_SHAPE;
-  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+size_t moe_packed_w1_bytes(int E, int H, int I) {
+  if (I <= 0) return 0;
+  return moe_packed_weight_bytes(E, 2 * I, H);
+}
+
+static moe_status_t launch_pack(const void* src, void* dst, int E, int N, int K, int mode, int I,
+                                void* stream) {
   int cus;
   moe_status_t st = ensure_init(&cus);
   if (st != MOE_OK) return st;
-  dim3 grid(2 * I / 64, (H + 63) / 64, E);
-  hipLaunchKernelGGL(repack_kernel, grid, dim3(256), 0, (hipStream_t)stream,
-                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), H, I, unpack);
+  dim3 grid(K / 64, (N + 255) / 256, E);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), N, K, mode, I);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status_t moe_pack_weight(const void* src, int E, int N, int K, int src_layout, void* dst,
+                             void* stream) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (E < 1 || N < 64 || N % 64 != 0 || K < 64 || K % 64 != 0) return MOE_ERR_SHAPE;
+  if (src_layout != MOE_B_NK && src_layout != MOE_B_KN) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  return launch_pack(src, dst, E, N, K, src_layout == MOE_B_NK ? PACK_NK : PACK_KN, 0, stream);
 }
 
 moe_status_t moe_repack_gate_up(const void* w1, int E, int H, int I, void* w1_packed,
                                 void* stream) {
-  return repack_common(w1, E, H, I, w1_packed, stream, 0);
+  if (!w1 || !w1_packed) return MOE_ERR_NULL;
+  if (E < 1 || H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(w1) || !aligned16(w1_packed)) return MOE_ERR_ALIGN;
+  return launch_pack(w1, w1_packed, E, 2 * I, H, PACK_GATEUP, I, stream);
 }
 
 moe_status_t moe_unpack_gate_up(const void* w1_packed, int E, int H, int I, void* w1,
                                 void* stream) {
-  return repack_common(w1_packed, E, H, I, w1, stream, 1);
+  if (!w1 || !w1_packed) return MOE_ERR_NULL;
+  if (E < 1 || H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(w1) || !aligned16(w1_packed)) return MOE_ERR_ALIGN;
+  return launch_pack(w1_packed, w1, E, 2 * I, H, UNPACK_GATEUP, I, stream);
 }
 
 moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T, int E, int k,
@@ -206,7 +223,7 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
   fill_groups(&a, groups);
   a.A = static_cast<const uint16_t*>(xg);
   a.B = static_cast<const uint16_t*>(w1_packed);
-  a.b_estride = 2LL * I * H;
+  a.b_estride = (long long)moe_packed_w1_bytes(1, H, I) / 2;
   a.ldb = H;
   a.N = 2 * I;
   a.K = H;
@@ -216,20 +233,21 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
   fill_mx(&a, mx, I, groups);
   a.ntiles_n = (2 * I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  return launch_group_gemm_fwd(EPI_GLU, BL_NK, a, grid, (hipStream_t)stream);
+  return launch_group_gemm_fwd(EPI_GLU, BL_PACKED, a, grid, (hipStream_t)stream);
 }
 
-moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const void* w2, int H, int I,
+moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, int H, int I,
                                      const moe_groups_t* groups, const void* preact,
                                      const moe_epilogue_t* ep, void* dgu,
                                      const moe_mx_out_t* mx, int cu_margin, void* stream) {
   moe_status_t st = check_groups(groups);
   if (st != MOE_OK) return st;
-  if (!dy2 || !w2 || !preact || !ep) return MOE_ERR_NULL;
+  if (!dy2 || !w2 || !w2->data || !preact || !ep) return MOE_ERR_NULL;
   if ((st = check_mx(mx)) != MOE_OK) return st;
   if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
-  if (ep->gated != 1) return MOE_ERR_UNSUPPORTED;
-  if (!aligned16(dy2) || !aligned16(w2) || !aligned16(preact) || (dgu && !aligned16(dgu)))
+  if (ep->gated != 1 || w2->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (w2->layout != MOE_B_NK && w2->layout != MOE_B_PACKED) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(dy2) || !aligned16(w2->data) || !aligned16(preact) || (dgu && !aligned16(dgu)))
     return MOE_ERR_ALIGN;
   GemmArgs a;
   memset(&a, 0, sizeof(a));
@@ -239,8 +257,9 @@ moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const void* w2, int H, int
   if ((st = ensure_init(&cus)) != MOE_OK) return st;
   fill_groups(&a, groups);
   a.A = static_cast<const uint16_t*>(dy2);
-  a.B = static_cast<const uint16_t*>(w2);  // W2_e [I][H] = (W2_e^T stored [N=I][K=H])
-  a.b_estride = (long long)I * H;
+  a.B = static_cast<const uint16_t*>(w2->data);  // W2_e [I][H] = W2_e^T stored [N=I][K=H]
+  const bool w2_packed = w2->layout == MOE_B_PACKED;
+  a.b_estride = w2_packed ? (long long)moe_packed_weight_bytes(1, I, H) / 2 : (long long)I * H;
   a.ldb = H;
   a.N = I;
   a.K = H;
@@ -250,7 +269,8 @@ moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const void* w2, int H, int
   fill_mx(&a, mx, 2 * I, groups);
   a.ntiles_n = (I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  return launch_group_gemm_bwd(EPI_DGLU, BL_NK, a, grid, (hipStream_t)stream);
+  return launch_group_gemm_bwd(EPI_DGLU, w2_packed ? BL_PACKED : BL_NK, a, grid,
+                               (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t* b_op, int N,
@@ -280,13 +300,13 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t
   switch (b_op->layout) {
     case MOE_B_KN: blay = BL_KN; a.ldb = N; a.b_estride = (long long)K * N; break;
     case MOE_B_NK: blay = BL_NK; a.ldb = K; a.b_estride = (long long)N * K; break;
-    case MOE_B_W1_PACKED_T:
-      if (K % 128 != 0) return MOE_ERR_SHAPE;
-      blay = BL_W1T; a.ldb = N; a.I = K / 2; a.b_estride = (long long)K * N; break;
+    case MOE_B_PACKED:
+      blay = BL_PACKED; a.ldb = K; a.b_estride = (long long)moe_packed_weight_bytes(1, N, K) / 2;
+      break;
     default: return MOE_ERR_UNSUPPORTED;
   }
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  if (blay == BL_W1T) return launch_group_gemm_bwd(EPI_STORE, blay, a, grid, (hipStream_t)stream);
+  if (blay == BL_PACKED) return launch_group_gemm_bwd(EPI_STORE, blay, a, grid, (hipStream_t)stream);
   return launch_group_gemm_fwd(EPI_STORE, blay, a, grid, (hipStream_t)stream);
 }
 

@@ -8,65 +8,81 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------- repack
+// ---------------------------------------------------------------- weight packing
 // Packed row of plain FC1 column j ("Boosting MoE Training Throughput…",
 // section "Optimizando GLU…", Figure 2: one tile holds half a tile width of the
 // gate and of the input/up columns).  128-row block p = gate columns 64p..64p+63
-// then up columns I+64p..I+64p+63.
-__device__ __forceinline__ int packed_row_of(int j, int I) {
-  int up = j >= I;
-  int c = up ? j - I : j;
-  return (c >> 6) * 128 + (up ? 64 : 0) + (c & 63);
+// then up columns I+64p..I+64p+63; this is the inverse map (packed row -> j).
+__device__ __forceinline__ int plain_col_of_packed(int pr, int I) {
+  const int pair = pr >> 7, s = pr & 127;
+  return s < 64 ? pair * 64 + s : I + pair * 64 + (s - 64);
 }
 
-// W1 [E][H][2I] -> W1p [E][2I][H].  Block = 64 (h) x 64 (j) transpose through
-// LDS; grid (2I/64, ceil(H/64), E), 256 threads.
-__global__ __launch_bounds__(256) void repack_kernel(const uint16_t* __restrict__ w1,
-                                                     uint16_t* __restrict__ w1p, int H, int I,
-                                                     int unpack) {
-  __shared__ uint16_t tile[64][66];
-  const int N2 = 2 * I;
-  const int j0 = blockIdx.x * 64, h0 = blockIdx.y * 64, e = blockIdx.z;
-  const uint16_t* src = w1 + (long long)e * H * N2;
-  uint16_t* dst = w1p + (long long)e * H * N2;
+// 16-byte chunk key of the tile-blocked layout (include/moe_glu.h): the same
+// XOR the GEMM uses for its LDS operand tiles.
+__device__ __forceinline__ int pack_key(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+
+enum { PACK_NK = 0, PACK_KN = 1, PACK_GATEUP = 2, UNPACK_GATEUP = 3 };
+
+// One workgroup per 256 x 64 destination block (grid: K/64, ceil(N/256), E).
+// The block is assembled as tile[n][k] in LDS and then written in the
+// blocked, swizzled order (or, for UNPACK_GATEUP, read in that order and
+// scattered back to the plain [E][H][2I] layout).
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ src,
+                                                   uint16_t* __restrict__ dst, int N, int K,
+                                                   int mode, int I) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[256][72];
+  const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
   const int t = threadIdx.x;
-  if (!unpack) {
-    // read 64 rows h x 64 plain columns j (128 B per row), write 64 packed rows x 64 h
-    for (int i = t; i < 64 * 8; i += 256) {
-      int r = i >> 3, ch = i & 7;
-      int h = h0 + r;
-      if (h < H) {
-        uint4 v = *reinterpret_cast<const uint4*>(src + (long long)h * N2 + j0 + ch * 8);
-        const uint16_t* pv = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) tile[r][ch * 8 + q] = pv[q];
-      }
+  const int KB = K >> 6;
+  const long long pe = (long long)((N + 255) / 256) * 256 * K;       // packed expert stride
+  uint16_t* pblk = (mode == UNPACK_GATEUP ? const_cast<uint16_t*>(src) : dst) + (long long)e * pe +
+                   ((long long)nb * KB + kb) * 16384;
+  if (mode == UNPACK_GATEUP) {
+    for (int it = t; it < 2048; it += 256) {
+      const int r = it >> 3, pc = it & 7, c = pc ^ pack_key(r);
+      *reinterpret_cast<uint4*>(&tile[r][c * 8]) = reinterpret_cast<const uint4*>(pblk)[it];
     }
     __syncthreads();
-    for (int i = t; i < 64 * 64; i += 256) {
-      int jj = i >> 6, hh = i & 63;
-      int h = h0 + hh;
-      if (h < H) dst[(long long)packed_row_of(j0 + jj, I) * H + h] = tile[hh][jj];
-    }
-  } else {
-    // read 64 packed rows (of plain columns j0..j0+63) x 64 h, write plain [h][j]
-    for (int i = t; i < 64 * 64; i += 256) {
-      int jj = i >> 6, hh = i & 63;
-      int h = h0 + hh;
-      if (h < H) tile[hh][jj] = src[(long long)packed_row_of(j0 + jj, I) * H + h];
-    }
-    __syncthreads();
-    for (int i = t; i < 64 * 8; i += 256) {
-      int r = i >> 3, ch = i & 7;
-      int h = h0 + r;
-      if (h < H) {
-        uint4 v;
-        uint16_t* pv = reinterpret_cast<uint16_t*>(&v);
+    // plain W1 [E][H][2I]: row k = 64 kb + kk, 8 packed rows -> 8 consecutive plain columns
+    uint16_t* w = dst + (long long)e * K * N;
+    for (int it = t; it < 2048; it += 256) {
+      const int kk = it >> 5, cc = it & 31, r0 = cc * 8, pr = nb * 256 + r0;
+      if (pr >= N) continue;
+      uint4 v;
+      uint16_t* pv = reinterpret_cast<uint16_t*>(&v);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) pv[q] = tile[r][ch * 8 + q];
-        *reinterpret_cast<uint4*>(dst + (long long)h * N2 + j0 + ch * 8) = v;
-      }
+      for (int q = 0; q < 8; ++q) pv[q] = tile[r0 + q][kk];
+      *reinterpret_cast<uint4*>(w + (long long)(kb * 64 + kk) * N + plain_col_of_packed(pr, I)) = v;
     }
+    return;
+  }
+  if (mode == PACK_NK) {
+    const uint16_t* w = src + (long long)e * N * K;
+    for (int it = t; it < 2048; it += 256) {
+      const int r = it >> 3, c = it & 7, n = nb * 256 + r;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < N) v = *reinterpret_cast<const uint4*>(w + (long long)n * K + kb * 64 + c * 8);
+      *reinterpret_cast<uint4*>(&tile[r][c * 8]) = v;
+    }
+  } else {  // PACK_KN and PACK_GATEUP: source [K][N]-major rows, 8 consecutive n per chunk
+    const uint16_t* w = src + (long long)e * K * N;
+    for (int it = t; it < 2048; it += 256) {
+      const int kk = it >> 5, cc = it & 31, r0 = cc * 8, pr = nb * 256 + r0;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (pr < N) {
+        const int col = mode == PACK_GATEUP ? plain_col_of_packed(pr, I) : pr;
+        v = *reinterpret_cast<const uint4*>(w + (long long)(kb * 64 + kk) * N + col);
+      }
+      const uint16_t* pv = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tile[r0 + q][kk] = pv[q];
+    }
+  }
+  __syncthreads();
+  for (int it = t; it < 2048; it += 256) {
+    const int r = it >> 3, pc = it & 7, c = pc ^ pack_key(r);
+    reinterpret_cast<uint4*>(pblk)[it] = *reinterpret_cast<const uint4*>(&tile[r][c * 8]);
   }
 }
 

@@ -1,6 +1,7 @@
-// Instantiations of the persistent grouped GEMM used by the backward pass:
-// dgrad + dGLU (W2 [I][H] read as the K-contiguous W2^T) and dX (packed W1
-// read transposed, N-contiguous, with the gate/up K remap).
+// Instantiations of the persistent grouped GEMM used by the backward pass and
+// by every packed-weight GEMM: dgrad + dGLU (W2 read as W2^T, packed or as the
+// K-contiguous [I][H]) and the plain GroupGemm on a tile-blocked packed weight
+// (FC2, dX).
 #include "internal.hpp"
 
 namespace moe {
@@ -12,8 +13,9 @@ static moe_status_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
 }
 
 moe_status_t launch_group_gemm_bwd(int epi, int blay, const GemmArgs& a, int grid, hipStream_t s) {
+  if (epi == EPI_DGLU && blay == BL_PACKED) return launch_one<EPI_DGLU, BL_PACKED>(a, grid, s);
   if (epi == EPI_DGLU && blay == BL_NK) return launch_one<EPI_DGLU, BL_NK>(a, grid, s);
-  if (epi == EPI_STORE && blay == BL_W1T) return launch_one<EPI_STORE, BL_W1T>(a, grid, s);
+  if (epi == EPI_STORE && blay == BL_PACKED) return launch_one<EPI_STORE, BL_PACKED>(a, grid, s);
   return MOE_ERR_UNSUPPORTED;
 }
 

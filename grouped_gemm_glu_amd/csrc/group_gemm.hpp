@@ -55,7 +55,7 @@ struct Stg {
 };
 
 enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2 };
-enum { BL_NK = 0, BL_KN = 1, BL_W1T = 2 };
+enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 
 struct GemmArgs {
   const uint16_t* A;        // [M_cap][K] grouped rows, K contiguous
@@ -305,6 +305,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     rsrc_t rsB;
     if (BLAY == BL_NK)
       rsB = make_rsrc(Bb + (long long)n0 * p.ldb, (long long)(p.N - n0) * b_stride);
+    else if (BLAY == BL_PACKED)   // the n-tile's K/64 contiguous 32 KB blocks
+      rsB = make_rsrc(Bb + (long long)nt * nk * (GM_BN * GM_BK), (long long)nk * GM_TILE_BYTES);
     else
       rsB = make_rsrc(Bb, p.b_estride * 2);
 
@@ -339,23 +341,28 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // K-tiles past the end are fetched through a descriptor with no records:
     // the loads return zeros, so the main loop needs no tail branch.
     const rsrc_t rsZ = make_rsrc(p.A, 0);
+    // a packed 32 KB block is already in LDS order: each wave instruction
+    // streams 1 KB contiguously
+    auto issue_block = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t koff) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int blk = wave * 8 + j;
+        lds_dma16(rs, lds_tile + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16), koff);
+      }
+    };
     auto issue_direct = [&](int kt, uint8_t* sa) {
       const bool in = kt < nk;
       issue_tile(in ? rsA : rsZ, sa, a_stride, (uint32_t)kt * (GM_BK * 2));
       if (BLAY == BL_NK)
         issue_tile(in ? rsB : rsZ, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * (GM_BK * 2));
+      if (BLAY == BL_PACKED)
+        issue_block(in ? rsB : rsZ, sa + GM_TILE_BYTES, (uint32_t)kt * GM_TILE_BYTES);
     };
     u32x4 rb[8];
     auto kn_load = [&](int kt) {
       const bool in = kt < nk;
       const int ktc = in ? kt : 0;
-      long long krow;
-      if (BLAY == BL_KN) {
-        krow = (long long)ktc * GM_BK;
-      } else {  // packed W1 read as W1^T: plain K tile -> packed row block
-        const int j0 = ktc * GM_BK;
-        krow = j0 < p.I ? 2LL * j0 : 2LL * (j0 - p.I) + 64;
-      }
+      const long long krow = (long long)ktc * GM_BK;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         rb[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsB : rsZ, kn_voff,
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // LDS access names its array directly.  With an odd tile count the last
     // step computes a zero tile.
     issue_direct(0, lds0);
-    if (BLAY != BL_NK) {
+    if (BLAY == BL_KN) {
       kn_load(0);
       kn_store(lds0);
     }
@@ -434,15 +441,15 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     __syncthreads();
     for (int kt = 0; kt < nk; kt += 2) {
       issue_direct(kt + 1, lds1);
-      if (BLAY != BL_NK) kn_load(kt + 1);
+      if (BLAY == BL_KN) kn_load(kt + 1);
       compute(lds0);
-      if (BLAY != BL_NK) kn_store(lds1);
+      if (BLAY == BL_KN) kn_store(lds1);
       wait_vmem_all();
       __syncthreads();
       issue_direct(kt + 2, lds0);
-      if (BLAY != BL_NK) kn_load(kt + 2);
+      if (BLAY == BL_KN) kn_load(kt + 2);
       compute(lds1);
-      if (BLAY != BL_NK) kn_store(lds0);
+      if (BLAY == BL_KN) kn_store(lds0);
       wait_vmem_all();
       __syncthreads();
     }

@@ -118,8 +118,7 @@ typedef enum {
   MOE_B_KN = 0,             /* B_e is [K][N] row-major (N contiguous), e.g. W2 [E][I][H] for FC2 */
   MOE_B_NK = 1,             /* B_e is stored [N][K] (K contiguous), i.e. used transposed:
                                out = A . B_e^T, e.g. W2 [E][I][H] in the dgrad dY2 . W2^T */
-  MOE_B_W1_PACKED_T = 2     /* B_e = W1_e^T read from the packed W1 of moe_repack_gate_up:
-                               out = A . W1_e^T with A's K = 2I in PLAIN order (dX) */
+  MOE_B_PACKED = 2          /* B_e in the tile-blocked layout of moe_pack_weight (see there) */
 } moe_b_layout_t;
 
 typedef struct {
@@ -135,16 +134,39 @@ moe_status_t moe_init(int device);
 
 const char* moe_status_string(moe_status_t s);
 
-/* Bytes of the packed W1 for E experts, hidden H, intermediate I (= E*2I*H*2). */
+/* Tile-blocked weight layout ("packed"), shared by moe_repack_gate_up and
+ * moe_pack_weight.  A weight used as the B operand of out = A . B_e^T is
+ * viewed per expert as [N][K] (K contiguous).  It is stored as blocks of 256
+ * rows (n) by 64 columns (k) = 32 KiB each; block (nb, kb) starts at element
+ * (nb * K/64 + kb) * 16384 of the expert, and experts are ceil(N/256) * 256 * K
+ * elements apart.  Inside a block, the 16-byte chunk c (0..7, k = 64 kb + 8c
+ * .. +7) of row r (n = 256 nb + r) sits at byte r * 128 + 16 * (c XOR s(r)),
+ * s(r) = (r mod 8) XOR ((r / 8) mod 4): the order in which the kernels stage
+ * it in LDS, so each block streams from memory contiguously.  Rows n >= N are
+ * zero.  Requires K % 64 == 0. */
+size_t moe_packed_weight_bytes(int E, int N, int K);
+
+/* Packs per-expert weights into the tile-blocked layout above.
+ * src_layout MOE_B_NK: src is [E][N][K]; MOE_B_KN: src is [E][K][N] (transposed
+ * while packing).  Uses: FC2's W2 [E][I][H] as MOE_B_KN with N = H, K = I;
+ * dgrad's W2 [E][I][H] as MOE_B_NK with N = I, K = H; dX's plain W1 [E][H][2I]
+ * as MOE_B_NK with N = H, K = 2I.  Bit-exact (a permutation plus zero padding). */
+moe_status_t moe_pack_weight(const void* src, int E, int N, int K, int src_layout, void* dst,
+                             void* stream);
+
+/* Bytes of the packed W1 for E experts, hidden H, intermediate I:
+ * moe_packed_weight_bytes(E, 2I, H). */
 size_t moe_packed_w1_bytes(int E, int H, int I);
 
 /* Offline gate/up repack ([BLOG] "Optimizando GLU…" and its Figure 2: W1's
  * columns are repacked into interleaved gate and input (up) blocks so that one
  * GEMM tile holds half a tile width of each; done once at checkpoint load).
  * w1:        bf16 [E][H][2I], plain: columns [0,I) gate, [I,2I) up.
- * w1_packed: bf16 [E][2I][H] (K-contiguous).  Packed column 128p + s holds
- *            gate column 64p + s for s < 64 and up column I + 64p + (s-64)
- *            for s >= 64.  Requires I % 64 == 0, H % 8 == 0.  Bit-exact. */
+ * w1_packed: the tile-blocked layout above with N = 2I (packed order), K = H,
+ *            where packed row 128p + s is gate column 64p + s for s < 64 and up
+ *            column I + 64p + (s-64) for s >= 64.  Each 256-row block therefore
+ *            holds two (64 gate | 64 up) pairs.  Requires I % 64 == 0,
+ *            H % 64 == 0.  Bit-exact. */
 moe_status_t moe_repack_gate_up(const void* w1, int E, int H, int I, void* w1_packed,
                                 void* stream);
 
@@ -173,7 +195,8 @@ moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T
  *     preact = bf16(z)                   optional, [M_cap][2I] in PLAIN order
  *     y = bf16(GLU epilogue of z)        optional, [M_cap][I]
  *     mx = MXFP8 copies of y             optional (row-wise and/or transposed)
- * xg: bf16 [M_cap][H].  Requires H % 64 == 0, I % 64 == 0, ep->gated == 1.
+ * xg: bf16 [M_cap][H]; w1_packed from moe_repack_gate_up.
+ * Requires H % 64 == 0, I % 64 == 0, ep->gated == 1.
  * One persistent launch; tiles are scheduled from the device counts.
  * cu_margin: compute units left free for concurrent kernels (0 = use all). */
 moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
@@ -184,8 +207,11 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
 /* GroupGemm + dActivation (+ Quantize/Transpose), the fused backward of FC1's
  * activation ([BLOG] "Optimizando GLU…": in back prop the epilogue reads the
  * GEMM output, computes the dGLU and writes it out).  Per expert:
- *     G = dy2_e . W2_e^T                 fp32 accumulate; dy2 bf16 [M_cap][H],
- *                                        w2 bf16 [E][I][H] (FC2's weight)
+ *     G = dy2_e . W2_e^T                 fp32 accumulate; dy2 bf16 [M_cap][H];
+ *                                        w2: FC2's weight [E][I][H] bf16 as
+ *                                        MOE_B_NK, or moe_pack_weight of it
+ *                                        (MOE_B_NK source, N = I, K = H) as
+ *                                        MOE_B_PACKED
  *     with g, u from preact (bf16 [M_cap][2I] plain, post-bias, pre-clamp),
  *     gc = clamp(g), uc = clamp(u) + up_offset, rs = row_scale or 1:
  *     du = G * a(gc) * rs * [up_lo <= u <= up_hi]
@@ -194,17 +220,16 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
  *     mx = MXFP8 copies of dgu           optional
  * ep->bias is ignored (already inside preact).  Requires H % 64 == 0,
  * I % 64 == 0. */
-moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const void* w2, int H, int I,
+moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, int H, int I,
                                      const moe_groups_t* groups, const void* preact,
                                      const moe_epilogue_t* ep, void* dgu,
                                      const moe_mx_out_t* mx, int cu_margin, void* stream);
 
 /* GroupGemm + Quantize ([BLOG] kernel family, first kernel): out_e = A_e . B_e
  * with bf16 and/or MXFP8 output.  A: [M_cap][K] grouped rows; B per the
- * layout in b->layout.  c_bf16: nullable bf16 [M_cap][N].
- * bf16 x bf16 on every B layout; MXFP8 x MXFP8 (both dtypes MXFP8) requires
- * layout MOE_B_NK (B stored [E][N][K] e4m3 with scales [E][N][K/32]).
- * Requires K % 64 == 0 (K % 128 == 0 for MXFP8), N % 64 == 0. */
+ * layout in b->layout (MOE_B_PACKED is the fast path).  c_bf16: nullable bf16
+ * [M_cap][N].  bf16 x bf16 on every B layout.
+ * Requires K % 64 == 0, N % 64 == 0. */
 moe_status_t moe_group_gemm_quant(const moe_operand_t* a, const moe_operand_t* b, int N, int K,
                                   const moe_groups_t* groups, void* c_bf16,
                                   const moe_mx_out_t* mx, int cu_margin, void* stream);

@@ -88,3 +88,23 @@ def sample_rows(counts, per_group=2, seed=0, max_rows=64):
 def expert_of_rows(counts, rows):
     off = np.concatenate([[0], np.cumsum(counts)])
     return np.searchsorted(off, rows, side="right") - 1
+
+
+def packed_layout(w_nk: np.ndarray) -> np.ndarray:
+    """The tile-blocked weight format documented in include/moe_glu.h, written
+    out in numpy from its definition: per expert [N][K] -> blocks of 256 rows x
+    64 columns, block (nb, kb) at (nb * K/64 + kb) * 16384, chunk c of row r at
+    16 * (c ^ s(r)) bytes into the row, s(r) = (r % 8) ^ ((r // 8) % 4); rows
+    past N are zero.  Returns uint16 [E * ceil(N/256)*256 * K]."""
+    E, N, K = w_nk.shape
+    NB, KB = (N + 255) // 256, K // 64
+    pad = np.zeros((E, NB * 256, K), dtype=np.uint16)
+    pad[:, :N] = w_nk
+    out = np.zeros((E, NB, KB, 256, 8, 8), dtype=np.uint16)
+    blocks = pad.reshape(E, NB, 256, KB, 8, 8).transpose(0, 1, 3, 2, 4, 5)  # e nb kb r c q
+    r = np.arange(256)
+    key = (r % 8) ^ ((r // 8) % 4)
+    for c in range(8):
+        out[:, :, :, r, c ^ key, :] = blocks[:, :, :, r, c, :]
+    return out.reshape(-1)
+

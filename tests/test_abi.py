@@ -85,8 +85,22 @@ def test_host_argument_errors_return_before_launch():
     assert G.raw_call("moe_route_group", fake, NULL, 8, 4, 5, fake, fake, fake, fake, fake,
                       NULL, 0, NULL, NULL) == 2
     # dgrad needs the saved pre-activation
-    assert G.raw_call("moe_group_gemm_dglu_bwd", fake, fake, 256, 512, ctypes.byref(grp), NULL,
-                      ctypes.byref(ep), fake, NULL, 0, NULL) == 1
+    w2op = G.operand(fake, layout=G.B_PACKED)
+    assert G.raw_call("moe_group_gemm_dglu_bwd", fake, ctypes.byref(w2op), 256, 512,
+                      ctypes.byref(grp), NULL, ctypes.byref(ep), fake, NULL, 0, NULL) == 1
+    # dgrad's W2 may be plain [N][K] or packed, not [K][N]
+    w2kn = G.operand(fake, layout=G.B_KN)
+    assert G.raw_call("moe_group_gemm_dglu_bwd", fake, ctypes.byref(w2kn), 256, 512,
+                      ctypes.byref(grp), fake, ctypes.byref(ep), fake, NULL, 0, NULL) == 4
+    # weight packing: K and N multiples of 64, source layout plain
+    assert G.raw_call("moe_pack_weight", fake, 2, 256, 96, G.B_NK, fake, NULL) == 2
+    assert G.raw_call("moe_pack_weight", fake, 2, 100, 128, G.B_NK, fake, NULL) == 2
+    assert G.raw_call("moe_pack_weight", fake, 2, 256, 128, G.B_PACKED, fake, NULL) == 4
+    assert G.raw_call("moe_pack_weight", fake + 2, 2, 256, 128, G.B_KN, fake, NULL) == 3
+    # packed sizes: experts padded to 256 rows
+    assert G.moe_packed_weight_bytes(3, 300, 128) == 3 * 512 * 128 * 2
+    assert G.moe_packed_w1_bytes(2, 192, 64) == 2 * 256 * 192 * 2
+    assert G.moe_packed_weight_bytes(0, 256, 64) == 0
     # MXFP8 quantize: C not a multiple of 32
     mx2 = G.mx_out(row_q=fake, row_s=fake)
     assert G.raw_call("moe_mxfp8_quantize", fake, 64, 48, NULL, ctypes.byref(mx2), NULL) == 2

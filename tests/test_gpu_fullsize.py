@@ -43,20 +43,26 @@ def dsv3_run(G):
     x, w1, w2, dy2 = dev_bits(d["x"]), dev_bits(d["w1"]), dev_bits(d["w2"]), dev_bits(dy2_h)
     cnt = dev_i32(counts)
     off = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
-    w1p = empty_bits((E, 2 * I, H))
+    w1p = empty_bits((G.moe_packed_w1_bytes(E, H, I) // 2,))
     G.moe_repack_gate_up(w1, E, H, I, w1p)
+    w1x = empty_bits((G.moe_packed_weight_bytes(E, H, 2 * I) // 2,))   # dX: N = H, K = 2I
+    G.moe_pack_weight(w1, E, H, 2 * I, G.B_NK, w1x)
+    w2f = empty_bits((G.moe_packed_weight_bytes(E, H, I) // 2,))       # FC2: N = H, K = I
+    G.moe_pack_weight(w2, E, H, I, G.B_KN, w2f)
+    w2d = empty_bits((G.moe_packed_weight_bytes(E, I, H) // 2,))       # dgrad: N = I, K = H
+    G.moe_pack_weight(w2, E, I, H, G.B_NK, w2d)
     y, pre = empty_bits((M, I)), empty_bits((M, 2 * I))
     out2, dgu, dx = empty_bits((M, H)), empty_bits((M, 2 * I)), empty_bits((M, H))
     grp = G.groups(cnt, M, off)
     ep = G.epilogue("swiglu")
     G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, y, pre)
-    G.moe_group_gemm_quant(G.operand(y), G.operand(w2, layout=G.B_KN), H, I, grp, out2)
-    G.moe_group_gemm_dglu_bwd(dy2, w2, H, I, grp, pre, ep, dgu)
-    G.moe_group_gemm_quant(G.operand(dgu), G.operand(w1p, layout=G.B_W1_PACKED_T), H, 2 * I, grp, dx)
+    G.moe_group_gemm_quant(G.operand(y), G.operand(w2f, layout=G.B_PACKED), H, I, grp, out2)
+    G.moe_group_gemm_dglu_bwd(dy2, G.operand(w2d, layout=G.B_PACKED), H, I, grp, pre, ep, dgu)
+    G.moe_group_gemm_quant(G.operand(dgu), G.operand(w1x, layout=G.B_PACKED), H, 2 * I, grp, dx)
     _sync()
     res = dict(d=d, dy2=dy2_h, off=off.cpu().numpy(), y=host_bits(y), pre=host_bits(pre),
                out2=host_bits(out2), dgu=host_bits(dgu), dx=host_bits(dx))
-    del x, w1, w2, dy2, w1p
+    del x, w1, w2, dy2, w1p, w1x, w2f, w2d
     return res
 
 
@@ -128,7 +134,7 @@ def test_gptoss_route_and_fc1_sampled_rows(G):
     x = dev_bits(d["x"])
     xg = empty_bits((TK, H))
     G.moe_route_group(logits, None, T, E, k, ids, cnt, off, dst, src, x, H, xg)
-    w1p = empty_bits((E, 2 * I, H))
+    w1p = empty_bits((G.moe_packed_w1_bytes(E, H, I) // 2,))
     G.moe_repack_gate_up(dev_bits(d["w1"]), E, H, I, w1p)
     b1 = dev_bits(d["b1"])
     y, pre = empty_bits((TK, I)), empty_bits((TK, 2 * I))

@@ -37,8 +37,14 @@ def test_full_step_graph_replay_with_new_routing(G):
 
     logits = torch.zeros((T, E), dtype=torch.float32, device="cuda")
     x, w1, w2, dy2 = dev_bits(x_h), dev_bits(w1_h), dev_bits(w2_h), dev_bits(dy2_h)
-    w1p = empty_bits((E, 2 * I, H))
+    w1p = empty_bits((G.moe_packed_w1_bytes(E, H, I) // 2,))
     G.moe_repack_gate_up(w1, E, H, I, w1p)
+    w1x = empty_bits((G.moe_packed_weight_bytes(E, H, 2 * I) // 2,))
+    G.moe_pack_weight(w1, E, H, 2 * I, G.B_NK, w1x)
+    w2f = empty_bits((G.moe_packed_weight_bytes(E, H, I) // 2,))
+    G.moe_pack_weight(w2, E, H, I, G.B_KN, w2f)
+    w2d = empty_bits((G.moe_packed_weight_bytes(E, I, H) // 2,))
+    G.moe_pack_weight(w2, E, I, H, G.B_NK, w2d)
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     cnt = torch.empty(E, dtype=torch.int32, device="cuda")
     off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
@@ -49,15 +55,16 @@ def test_full_step_graph_replay_with_new_routing(G):
     out2, dgu, dx = empty_bits((TK, H)), empty_bits((TK, 2 * I)), empty_bits((TK, H))
     grp = G.groups(cnt, TK)
     ep = G.epilogue("swiglu")
-    op_y, op_w2 = G.operand(y), G.operand(w2, layout=G.B_KN)
-    op_dgu, op_w1p = G.operand(dgu), G.operand(w1p, layout=G.B_W1_PACKED_T)
+    op_y, op_w2 = G.operand(y), G.operand(w2f, layout=G.B_PACKED)
+    op_dgu, op_w1x = G.operand(dgu), G.operand(w1x, layout=G.B_PACKED)
+    op_w2d = G.operand(w2d, layout=G.B_PACKED)
 
     def step():
         G.moe_route_group(logits, None, T, E, k, ids, cnt, off, dst, src, x, H, xg)
         G.moe_group_gemm_glu_fwd(xg, grp, w1p, H, I, ep, y, pre)
         G.moe_group_gemm_quant(op_y, op_w2, H, I, grp, out2)
-        G.moe_group_gemm_dglu_bwd(dy2, w2, H, I, grp, pre, ep, dgu)
-        G.moe_group_gemm_quant(op_dgu, op_w1p, H, 2 * I, grp, dx)
+        G.moe_group_gemm_dglu_bwd(dy2, op_w2d, H, I, grp, pre, ep, dgu)
+        G.moe_group_gemm_quant(op_dgu, op_w1x, H, 2 * I, grp, dx)
 
     # warm up on a side stream, then capture (the library makes no allocation,
     # synchronisation or host query while capturing)

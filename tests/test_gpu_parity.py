@@ -13,7 +13,7 @@ import workloads as W
 from oracle import formats as F
 from oracle import moe as O
 from tests.gpu_util import (BF16_NAN_SENTINEL, BYTE_SENTINEL, assert_bf16_close, dev_bits, dev_i32,
-                            empty_bits, empty_bytes, host_bits)
+                            empty_bits, empty_bytes, host_bits, packed_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,19 +34,36 @@ def _sync():
 
 
 # ---------------------------------------------------------------- repack
-@pytest.mark.parametrize("E,H,I", [(3, 64, 192), (4, 256, 512), (2, 72, 64)])
+@pytest.mark.parametrize("E,H,I", [(3, 64, 192), (4, 256, 512), (2, 128, 64), (1, 192, 320)])
 def test_repack_bit_exact_and_roundtrip(G, E, H, I):
+    """The gate/up repack equals the oracle's packed row order stored in the
+    documented tile-blocked format (2I not a multiple of 256 in some cases)."""
     rng = np.random.default_rng(E * 1000 + H + I)
     w1 = rng.integers(0, 2 ** 16, size=(E, H, 2 * I)).astype(np.uint16)
-    want, _ = O.repack_gate_up(w1)
+    want = packed_layout(O.repack_gate_up(w1)[0])
     d_w1 = dev_bits(w1)
-    d_p = empty_bits((E, 2 * I, H))
+    n_el = G.moe_packed_w1_bytes(E, H, I) // 2
+    assert n_el == want.size
+    d_p = empty_bits((n_el,))
     G.moe_repack_gate_up(d_w1, E, H, I, d_p)
     d_back = empty_bits((E, H, 2 * I))
     G.moe_unpack_gate_up(d_p, E, H, I, d_back)
     _sync()
     assert np.array_equal(host_bits(d_p), want)
     assert np.array_equal(host_bits(d_back), w1)
+
+
+@pytest.mark.parametrize("layout", ["NK", "KN"])
+@pytest.mark.parametrize("E,N,K", [(2, 320, 128), (3, 256, 64), (1, 64, 192)])
+def test_pack_weight_bit_exact(G, layout, E, N, K):
+    rng = np.random.default_rng(N * 7 + K + E)
+    w_nk = rng.integers(0, 2 ** 16, size=(E, N, K)).astype(np.uint16)
+    src = w_nk if layout == "NK" else np.ascontiguousarray(np.transpose(w_nk, (0, 2, 1)))
+    n_el = G.moe_packed_weight_bytes(E, N, K) // 2
+    d_p = empty_bits((n_el,))
+    G.moe_pack_weight(dev_bits(src), E, N, K, G.B_NK if layout == "NK" else G.B_KN, d_p)
+    _sync()
+    assert np.array_equal(host_bits(d_p), packed_layout(w_nk))
 
 
 # ---------------------------------------------------------------- routing / grouping
@@ -100,7 +117,7 @@ def _fc1_gpu(G, x, counts, w1, I, ep_kw, m_cap=None, preact=True, mx=False, bias
     M = int(np.sum(counts))
     m_cap = m_cap or x.shape[0]
     d_w1 = dev_bits(w1)
-    d_w1p = empty_bits((E, 2 * I, H))
+    d_w1p = empty_bits((G.moe_packed_w1_bytes(E, H, I) // 2,))
     G.moe_repack_gate_up(d_w1, E, H, I, d_w1p)
     d_x = dev_bits(x)
     d_counts = dev_i32(counts)
@@ -248,7 +265,7 @@ def _quant_gpu(G, a_bits, counts, b_bits, layout, N, K, m_cap, mx=False):
     return out
 
 
-@pytest.mark.parametrize("layout", ["KN", "NK"])
+@pytest.mark.parametrize("layout", ["KN", "NK", "PACKED"])
 def test_group_gemm_quant_bf16(G, layout):
     counts = np.array([129, 0, 400, 3, 256])
     E, K, N = len(counts), 320, 448
@@ -259,9 +276,13 @@ def test_group_gemm_quant_bf16(G, layout):
     if layout == "KN":
         d_b = dev_bits(b)
         lay = G.B_KN
-    else:
+    elif layout == "NK":
         d_b = dev_bits(np.ascontiguousarray(np.transpose(b, (0, 2, 1))))
         lay = G.B_NK
+    else:
+        d_b = empty_bits((G.moe_packed_weight_bytes(E, N, K) // 2,))
+        G.moe_pack_weight(dev_bits(b), E, N, K, G.B_KN, d_b)
+        lay = G.B_PACKED
     out = _quant_gpu(G, a, counts, d_b, lay, N, K, m_cap, mx=True)
     M = int(counts.sum())
     ref = O.group_gemm(a[:M], counts, b)
@@ -285,29 +306,33 @@ def test_group_gemm_quant_integer_exact(G):
     assert np.array_equal(out["c"], O.group_gemm(a, counts, b))
 
 
-def test_dx_through_packed_w1(G):
+def test_dx_through_packed_plain_w1(G):
+    """dX = dgu . W1^T with the plain W1 [E][H][2I] packed as a K-contiguous
+    operand (N = H, K = 2I)."""
     counts = np.array([100, 0, 300, 257])
-    E, H, I = len(counts), 192, 192
+    E, H, I = len(counts), 320, 192
     M = int(counts.sum())
     rng = np.random.default_rng(22)
     dgu = W.to_bf16_bits(rng.standard_normal((M, 2 * I)).astype(np.float32))
     w1 = W.to_bf16_bits((rng.standard_normal((E, H, 2 * I)) * 0.05).astype(np.float32))
-    d_w1p = empty_bits((E, 2 * I, H))
-    G.moe_repack_gate_up(dev_bits(w1), E, H, I, d_w1p)
-    out = _quant_gpu(G, dgu, counts, d_w1p, G.B_W1_PACKED_T, H, 2 * I, M)
+    d_p = empty_bits((G.moe_packed_weight_bytes(E, H, 2 * I) // 2,))
+    G.moe_pack_weight(dev_bits(w1), E, H, 2 * I, G.B_NK, d_p)
+    out = _quant_gpu(G, dgu, counts, d_p, G.B_PACKED, H, 2 * I, M)
     assert_bf16_close(out["c"], O.dx(dgu, counts, w1), what="dX")
     # integer-exact variant: bit-exact
     dgu_t = W.ternary_bf16(5, (M, 2 * I))
     w1_t = W.ternary_bf16(6, (E, H, 2 * I), density=0.5)
-    G.moe_repack_gate_up(dev_bits(w1_t), E, H, I, d_w1p)
-    out = _quant_gpu(G, dgu_t, counts, d_w1p, G.B_W1_PACKED_T, H, 2 * I, M)
+    G.moe_pack_weight(dev_bits(w1_t), E, H, 2 * I, G.B_NK, d_p)
+    out = _quant_gpu(G, dgu_t, counts, d_p, G.B_PACKED, H, 2 * I, M)
     assert np.array_equal(out["c"], O.dx(dgu_t, counts, w1_t))
 
 
 # ---------------------------------------------------------------- dgrad + dGLU
-@pytest.mark.parametrize("act,clamp", [("swiglu", False), ("swiglu", True), ("geglu", False),
-                                       ("geglu_tanh", False), ("srelu", False)])
-def test_dglu_bwd(G, act, clamp):
+@pytest.mark.parametrize("act,clamp,w2_layout", [("swiglu", False, "PACKED"), ("swiglu", True, "NK"),
+                                                 ("swiglu", True, "PACKED"), ("geglu", False, "NK"),
+                                                 ("geglu_tanh", False, "PACKED"),
+                                                 ("srelu", False, "PACKED")])
+def test_dglu_bwd(G, act, clamp, w2_layout):
     import torch
     counts = np.array([64, 0, 300, 1, 270])
     E, H, I = len(counts), 256, 320
@@ -326,7 +351,13 @@ def test_dglu_bwd(G, act, clamp):
     bufs = dict(row_q=empty_bytes((m_cap, 2 * I)), row_s=empty_bytes((m_cap, 2 * I // 32)),
                 col_q=empty_bytes((2 * I, m_cap)), col_s=empty_bytes((2 * I, (m_cap + 31) // 32 + E)))
     d_rs = torch.from_numpy(rs).cuda()
-    G.moe_group_gemm_dglu_bwd(dev_bits(dy2), dev_bits(w2), H, I, G.groups(d_counts, m_cap),
+    if w2_layout == "NK":
+        w2_op = G.operand(dev_bits(w2), layout=G.B_NK)
+    else:
+        d_w2p = empty_bits((G.moe_packed_weight_bytes(E, I, H) // 2,))
+        G.moe_pack_weight(dev_bits(w2), E, I, H, G.B_NK, d_w2p)
+        w2_op = G.operand(d_w2p, layout=G.B_PACKED)
+    G.moe_group_gemm_dglu_bwd(dev_bits(dy2), w2_op, H, I, G.groups(d_counts, m_cap),
                               dev_bits(pre), G.epilogue(row_scale=d_rs, **kw), dgu,
                               G.mx_out(**bufs))
     _sync()
