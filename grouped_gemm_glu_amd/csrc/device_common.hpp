@@ -22,17 +22,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even.  Overflow rounds to +-inf,
-// NaN becomes the quiet NaN 0x7FC0 (sign kept).
+// fp32 -> bf16, round to nearest, ties to even; overflow rounds to +-inf and
+// NaN stays NaN (gfx950 converts in hardware: v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------- MXFP8
@@ -80,7 +79,11 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 // ---------------------------------------------------------------- activations
 enum { ACT_SWIGLU = 0, ACT_GEGLU = 1, ACT_GEGLU_TANH = 2, ACT_SRELU = 3 };
 
-__device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each;
+// the results are rounded to bf16).
+__device__ __forceinline__ float sigmoidf_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 __device__ __forceinline__ float act_fwd(int act, float g, float alpha) {
   switch (act) {

@@ -14,8 +14,11 @@
 // are staged in LDS as [rows][64] bf16, 128 bytes per row, with the 16-byte
 // chunk index XOR-swizzled by ((r ^ (r >> 3)) & 7) so that the fragment reads
 // (8 consecutive rows, one chunk) and the transposed weight writes (rows 8
-// apart) are both free of bank conflicts.  Two LDS stages; the next K-tile is
-// fetched into registers while the current one feeds the MFMAs.
+// apart) are both free of bank conflicts.  Two LDS stages filled by direct
+// global -> LDS loads (buffer_load ... lds): the DMA of K-tile t + 2 is issued
+// right after the barrier that frees its stage, one instruction per MFMA of
+// the last k-step of K-tile t, whose fragments are already in registers, so
+// the barrier does not drain the MFMA pipe.
 //
 // Epilogues (fused; the accumulators never go to HBM in fp32):
 //   EPI_GLU   FC1: bias, clamp, activation * up, row scale -> bf16 y; optional
@@ -384,50 +387,79 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       }
     };
 
-    // Fragments are double-buffered one k-step ahead; the scheduling barriers
-    // keep the compiler from hoisting a whole K-tile of LDS reads (which
-    // would need ~128 more VGPRs than the loop has).
-    auto compute = [&](const uint8_t* sa) {
+    // Fragments are double-buffered one k-step ahead.  A K-tile is 4 k-steps
+    // of 16 MFMAs per wave.  The barrier that hands a stage back to the DMA
+    // sits before the LAST k-step of each K-tile: that k-step's fragments are
+    // already in registers, so its 16 MFMAs keep the pipe busy while the next
+    // stage's first fragments are read and the next DMA is issued.
+    bf16x8 af[2][4], bfr[2][4];
+    // reads in order of first use by the MFMA sequence (i outer, j inner)
+    auto frag_load = [&](const uint8_t* sa, int ks, int buf) {
       const uint8_t* sb = sa + GM_TILE_BYTES;
-      bf16x8 af[2][4], bfr[2][4];
-      // reads in order of first use by the MFMA sequence (i outer, j inner)
-      auto frag_load = [&](int ks, int buf) {
-        const int ch = ks * 2 + (lane_t >> 5);
-        auto rd_a = [&](int i) {
-          af[buf][i] = *reinterpret_cast<const bf16x8*>(
-              sa + swz_off(wm * 128 + i * 32 + (lane_t & 31), ch));
-        };
-        auto rd_b = [&](int j) {
-          bfr[buf][j] = *reinterpret_cast<const bf16x8*>(
-              sb + swz_off(wn * 128 + j * 32 + (lane_t & 31), ch));
-        };
-        rd_a(0);
-        rd_b(0); rd_b(1); rd_b(2); rd_b(3);
-        rd_a(1); rd_a(2); rd_a(3);
+      const int ch = ks * 2 + (lane_t >> 5);
+      auto rd_a = [&](int i) {
+        af[buf][i] = *reinterpret_cast<const bf16x8*>(
+            sa + swz_off(wm * 128 + i * 32 + (lane_t & 31), ch));
       };
-      frag_load(0, 0);
+      auto rd_b = [&](int j) {
+        bfr[buf][j] = *reinterpret_cast<const bf16x8*>(
+            sb + swz_off(wn * 128 + j * 32 + (lane_t & 31), ch));
+      };
+      rd_a(0);
+      rd_b(0); rd_b(1); rd_b(2); rd_b(3);
+      rd_a(1); rd_a(2); rd_a(3);
+    };
+    // 16 MFMAs on fragment buffer buf; the 8 LDS reads issued just before
+    // are spread one per MFMA over the first 8, so each has at least 8 MFMAs
+    // of cover before its first use.
+    auto mfma_step = [&](int buf) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks < 3) frag_load(ks + 1, (ks + 1) & 1);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i],
+                                                              acc[i][j], 0, 0, 0);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][j], af[ks & 1][i],
-                                                                acc[i][j], 0, 0, 0);
-        // issue order: the next k-step's 8 LDS reads one per MFMA over the
-        // first 8 MFMAs, so each has at least 8 MFMAs of cover before use
-        if (ks < 3) {
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMA
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // The same 16 MFMAs with the next stage's DMA (16 VMEM instructions per
+    // wave) spread over them, one per MFMA: issued as a burst right after the
+    // barrier, the four waves' 64 DMA instructions queue at the address unit
+    // and hold up the MFMAs issued behind them.
+    auto mfma_step_dma = [&](int buf) {
 #pragma unroll
-          for (int g = 0; g < 8; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMA
-        }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i],
+                                                              acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        if (g < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);               // 1 VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
       }
       __builtin_amdgcn_sched_barrier(0);
+    };
+    // k-steps 0..2 of the K-tile in stage sa (fragments of k-step 0 requested)
+    auto first_steps = [&](const uint8_t* sa) {
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+        frag_load(sa, ks + 1, (ks + 1) & 1);
+        mfma_step(ks & 1);
+      }
+    };
+    // every wave's reads of a stage done and every wave's DMA into the other
+    // stage landed: s_waitcnt vmcnt(0) lgkmcnt(0), then the barrier
+    auto stage_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __syncthreads();
     };
     // Two K-tiles per iteration, stage arrays used in a fixed order so every
     // LDS access names its array directly.  With an odd tile count the last
@@ -437,22 +469,30 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       kn_load(0);
       kn_store(lds0);
     }
-    wait_vmem_all();
-    __syncthreads();
+    stage_barrier();
+    issue_direct(1, lds1);
+    if (BLAY == BL_KN) kn_load(1);
+    __builtin_amdgcn_sched_barrier(0);
+    frag_load(lds0, 0, 0);
     for (int kt = 0; kt < nk; kt += 2) {
-      issue_direct(kt + 1, lds1);
-      if (BLAY == BL_KN) kn_load(kt + 1);
-      compute(lds0);
+      first_steps(lds0);
       if (BLAY == BL_KN) kn_store(lds1);
-      wait_vmem_all();
-      __syncthreads();
+      stage_barrier();
       issue_direct(kt + 2, lds0);
       if (BLAY == BL_KN) kn_load(kt + 2);
-      compute(lds1);
+      frag_load(lds1, 0, 0);
+      mfma_step_dma(1);                  // k-step 3 of K-tile kt
+      first_steps(lds1);
       if (BLAY == BL_KN) kn_store(lds0);
-      wait_vmem_all();
-      __syncthreads();
+      stage_barrier();
+      issue_direct(kt + 3, lds1);
+      if (BLAY == BL_KN) kn_load(kt + 3);
+      frag_load(lds0, 0, 0);
+      mfma_step_dma(1);                  // k-step 3 of K-tile kt + 1
     }
+    // the loop leaves one DMA (a K-tile past the end: zeros) and one set of
+    // fragment reads in flight; the epilogue reuses both stage arrays
+    stage_barrier();
 
     // ================================================================ epilogues
     // The MFMAs compute D = W X^T per 32 x 32 block, so accumulator element r
