@@ -233,7 +233,8 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
   fill_mx(&a, mx, I, groups);
   a.ntiles_n = (2 * I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  return launch_group_gemm_fwd(EPI_GLU, BL_PACKED, a, grid, (hipStream_t)stream);
+  const int epi = (a.row_q || a.col_q) ? EPI_GLU_MX : EPI_GLU;
+  return launch_group_gemm_fwd(epi, BL_PACKED, a, grid, (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, int H, int I,

@@ -13,6 +13,7 @@ static moe_status_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
 
 moe_status_t launch_group_gemm_fwd(int epi, int blay, const GemmArgs& a, int grid, hipStream_t s) {
   if (epi == EPI_GLU && blay == BL_PACKED) return launch_one<EPI_GLU, BL_PACKED>(a, grid, s);
+  if (epi == EPI_GLU_MX && blay == BL_PACKED) return launch_one<EPI_GLU_MX, BL_PACKED>(a, grid, s);
   if (epi == EPI_STORE && blay == BL_KN) return launch_one<EPI_STORE, BL_KN>(a, grid, s);
   if (epi == EPI_STORE && blay == BL_NK) return launch_one<EPI_STORE, BL_NK>(a, grid, s);
   return MOE_ERR_UNSUPPORTED;

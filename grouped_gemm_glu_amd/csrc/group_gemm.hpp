@@ -57,7 +57,7 @@ struct Stg {
   }
 };
 
-enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2 };
+enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3 };
 enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 
 struct GemmArgs {
@@ -513,6 +513,82 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     }
 
     if (EPI == EPI_GLU) {
+      // Straight from registers to HBM, no LDS and no barrier.  Pair wn of
+      // this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3.  For two
+      // column groups q = 2p, 2p + 1 a lane holds columns 8q + 4 (lane / 32)
+      // .. + 3 of its row; one v_permlane32_swap per dword gives lane l < 32
+      // columns 16p .. 16p + 7 and lane l + 32 columns 16p + 8 .. 16p + 15, so
+      // every lane stores 16 bytes and each row gets 32 contiguous bytes per
+      // store.  Descriptors cover the tile's valid rows only: stores of the
+      // rows past the group are dropped by the buffer range check.
+      const int cvalid_n = min(128, p.I - nt * 128);
+      if (wn * 64 < cvalid_n) {
+        const long long ld2 = 2LL * p.I;
+        const uint16_t* bias_e = p.ep.bias ? p.ep.bias + (long long)e * ld2 : nullptr;
+        const int lh = (lane >> 5) + z0;
+        const rsrc_t rsY = make_rsrc(p.C ? p.C + (long long)row0 * p.I : p.A,
+                                     p.C ? (long long)rows_valid * p.I * 2 : 0);
+        const rsrc_t rsP = make_rsrc(p.preact ? p.preact + (long long)row0 * ld2 : p.A,
+                                     p.preact ? (long long)rows_valid * ld2 * 2 : 0);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            __builtin_amdgcn_sched_barrier(0);
+            float bg[2][4], bu[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int c = nt * 128 + wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) bg[h][s2] = bu[h][s2] = 0.0f;
+              if (bias_e) {
+                const uint2 vg = *reinterpret_cast<const uint2*>(bias_e + c);
+                const uint2 vu = *reinterpret_cast<const uint2*>(bias_e + p.I + c);
+                bg[h][0] = __uint_as_float(vg.x << 16); bg[h][1] = __uint_as_float(vg.x & 0xFFFF0000u);
+                bg[h][2] = __uint_as_float(vg.y << 16); bg[h][3] = __uint_as_float(vg.y & 0xFFFF0000u);
+                bu[h][0] = __uint_as_float(vu.x << 16); bu[h][1] = __uint_as_float(vu.x & 0xFFFF0000u);
+                bu[h][2] = __uint_as_float(vu.y << 16); bu[h][3] = __uint_as_float(vu.y & 0xFFFF0000u);
+              }
+            }
+            // byte offset of this lane's 16 bytes in row 0 of the tile
+            const uint32_t ycol = (uint32_t)(wn * 64 + 32 * jj + 16 * pp + 8 * lh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t m = (uint32_t)(wm * 128 + 32 * i + lm);
+              uint32_t yw[2][2], gw[2][2], uw[2][2];
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int q = 2 * pp + h;
+                float o[4], g[4], u[4];
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                  g[s2] = acc[i][jj][4 * q + s2] + bg[h][s2];
+                  u[s2] = acc[i][jj + 2][4 * q + s2] + bu[h][s2];
+                  const float gc = fminf(fmaxf(g[s2], p.ep.gate_lo), p.ep.gate_hi);
+                  const float uc = fminf(fmaxf(u[s2], p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
+                  o[s2] = act_fwd(p.ep.act, gc, p.ep.alpha) * uc * rsc[i];
+                }
+                yw[h][0] = pack_bf16x2(o[0], o[1]); yw[h][1] = pack_bf16x2(o[2], o[3]);
+                gw[h][0] = pack_bf16x2(g[0], g[1]); gw[h][1] = pack_bf16x2(g[2], g[3]);
+                uw[h][0] = pack_bf16x2(u[0], u[1]); uw[h][1] = pack_bf16x2(u[2], u[3]);
+              }
+              auto put = [&](uint32_t (&w)[2][2], const rsrc_t& rs, uint32_t off) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+                const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+              };
+              put(yw, rsY, (m * (uint32_t)p.I + (uint32_t)nt * 128 + ycol) * 2u);
+              if (p.preact) {
+                const uint32_t prow = m * (uint32_t)ld2 + (uint32_t)nt * 128 + ycol;
+                put(gw, rsP, prow * 2u);
+                put(uw, rsP, (prow + (uint32_t)p.I) * 2u);
+              }
+            }
+          }
+        }
+      }
+    } else if (EPI == EPI_GLU_MX) {
       // pair wn of this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3
       const int ld = GM_STG_LD_128;
       const int cvalid_n = min(128, p.I - nt * 128);
