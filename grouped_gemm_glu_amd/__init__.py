@@ -60,6 +60,9 @@ _SIGS = {
     "moe_packed_w1_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "moe_packed_weight_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "moe_pack_weight": ([_P, _I, _I, _I, _I, _P, _P], _I),
+    "moe_packed_mx_weight_bytes": ([_I, _I, _I], ctypes.c_size_t),
+    "moe_packed_mx_scale_bytes": ([_I, _I, _I], ctypes.c_size_t),
+    "moe_pack_weight_mx": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_repack_gate_up": ([_P, _I, _I, _I, _P, _P], _I),
     "moe_unpack_gate_up": ([_P, _I, _I, _I, _P, _P], _I),
     "moe_route_group": ([_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P], _I),
@@ -160,6 +163,20 @@ def moe_packed_weight_bytes(E: int, N: int, K: int) -> int:
 def moe_pack_weight(src, E, N, K, src_layout, dst, stream=None):
     _check("moe_pack_weight",
            _lib.moe_pack_weight(_ptr(src), E, N, K, src_layout, _ptr(dst), _stream(stream)))
+
+
+def moe_packed_mx_weight_bytes(E: int, N: int, K: int) -> int:
+    return _lib.moe_packed_mx_weight_bytes(E, N, K)
+
+
+def moe_packed_mx_scale_bytes(E: int, N: int, K: int) -> int:
+    return _lib.moe_packed_mx_scale_bytes(E, N, K)
+
+
+def moe_pack_weight_mx(src, E, N, K, src_layout, dst_q, dst_s, stream=None):
+    _check("moe_pack_weight_mx",
+           _lib.moe_pack_weight_mx(_ptr(src), E, N, K, src_layout, _ptr(dst_q), _ptr(dst_s),
+                                   _stream(stream)))
 
 
 def moe_repack_gate_up(w1, E, H, I, w1_packed, stream=None):

@@ -149,6 +149,31 @@ moe_status_t moe_pack_weight(const void* src, int E, int N, int K, int src_layou
   return launch_pack(src, dst, E, N, K, src_layout == MOE_B_NK ? PACK_NK : PACK_KN, 0, stream);
 }
 
+size_t moe_packed_mx_weight_bytes(int E, int N, int K) {
+  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  return (size_t)E * (size_t)((N + 255) / 256) * 256 * (size_t)K;
+}
+
+size_t moe_packed_mx_scale_bytes(int E, int N, int K) {
+  return moe_packed_mx_weight_bytes(E, N, K) / 32;
+}
+
+moe_status_t moe_pack_weight_mx(const void* src, int E, int N, int K, int src_layout, void* dst_q,
+                                void* dst_s, void* stream) {
+  if (!src || !dst_q || !dst_s) return MOE_ERR_NULL;
+  if (E < 1 || N < 64 || N % 64 != 0 || K < 128 || K % 128 != 0) return MOE_ERR_SHAPE;
+  if (src_layout != MOE_B_NK && src_layout != MOE_B_KN) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst_q) || !aligned16(dst_s)) return MOE_ERR_ALIGN;
+  int cus;
+  moe_status_t st = ensure_init(&cus);
+  if (st != MOE_OK) return st;
+  dim3 grid(K / 128, (N + 255) / 256, E);
+  hipLaunchKernelGGL(pack_mx_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(src), static_cast<uint8_t*>(dst_q),
+                     static_cast<uint8_t*>(dst_s), N, K, src_layout == MOE_B_KN ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 moe_status_t moe_repack_gate_up(const void* w1, int E, int H, int I, void* w1_packed,
                                 void* stream) {
   if (!w1 || !w1_packed) return MOE_ERR_NULL;
@@ -282,7 +307,17 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t
   if (!a_op || !b_op || !a_op->data || !b_op->data) return MOE_ERR_NULL;
   if ((st = check_mx(mx)) != MOE_OK) return st;
   if (N < 64 || N % 64 != 0 || K < 64 || K % 64 != 0) return MOE_ERR_SHAPE;
-  if (a_op->dtype != MOE_DT_BF16 || b_op->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool mx_in = a_op->dtype == MOE_DT_MXFP8 || b_op->dtype == MOE_DT_MXFP8;
+  if (mx_in) {   // MXFP8 x MXFP8 only, weight from moe_pack_weight_mx
+    if (a_op->dtype != MOE_DT_MXFP8 || b_op->dtype != MOE_DT_MXFP8 ||
+        b_op->layout != MOE_B_PACKED)
+      return MOE_ERR_UNSUPPORTED;
+    if (!a_op->scales || !b_op->scales) return MOE_ERR_NULL;
+    if (K % 128 != 0) return MOE_ERR_SHAPE;
+    if (!aligned16(a_op->scales) || !aligned16(b_op->scales)) return MOE_ERR_ALIGN;
+  } else if (a_op->dtype != MOE_DT_BF16 || b_op->dtype != MOE_DT_BF16) {
+    return MOE_ERR_UNSUPPORTED;
+  }
   if (!aligned16(a_op->data) || !aligned16(b_op->data) || (c_bf16 && !aligned16(c_bf16)))
     return MOE_ERR_ALIGN;
   GemmArgs a;
@@ -297,6 +332,14 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t
   a.C = static_cast<uint16_t*>(c_bf16);
   fill_mx(&a, mx, N, groups);
   a.ntiles_n = (N + GM_BN - 1) / GM_BN;
+  if (mx_in) {
+    a.a_scales = static_cast<const uint8_t*>(a_op->scales);
+    a.b_scales = static_cast<const uint8_t*>(b_op->scales);
+    a.ldb = K;
+    a.b_estride = (long long)moe_packed_mx_weight_bytes(1, N, K);   // bytes = elements
+    int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
+    return launch_group_gemm_mx(a, grid, (hipStream_t)stream);
+  }
   int blay;
   switch (b_op->layout) {
     case MOE_B_KN: blay = BL_KN; a.ldb = N; a.b_estride = (long long)K * N; break;

@@ -340,4 +340,39 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------- MXFP8 weight pack
+// Offline quantisation of a bf16 weight to MXFP8 along K, written in the
+// tile-blocked order the block-scaled GEMM streams: per expert, blocks of 256
+// rows (output columns n) x 128 K bytes (32 KB), block (nb, kb) at
+// (nb * K/128 + kb) * 32768 bytes, the 16-byte chunk c of row r at
+// 16 * (c ^ key(r)); the four E8M0 scales of row r in block (nb, kb) form the
+// dword at ((nb * K/128 + kb) * 256 + r) * 4 of the scale array (byte b: K
+// values kb * 128 + 32 b .. + 31).  Rows past N are zero with scale byte 0.
+// Grid (K/128, ceil(N/256), E), one thread per row.
+__global__ __launch_bounds__(256) void pack_mx_kernel(const uint16_t* __restrict__ src,
+                                                      uint8_t* __restrict__ q,
+                                                      uint8_t* __restrict__ sc, int N, int K,
+                                                      int src_kn) {
+  const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
+  const int nk = gridDim.x, NB = gridDim.y;
+  const int r = threadIdx.x, n = nb * 256 + r;
+  const uint16_t* W = src + (long long)e * N * K;
+  const long long blk = ((long long)e * NB + nb) * nk + kb;
+  uint8_t* row = q + blk * 32768 + r * 128;
+  uint32_t sword = 0;
+  for (int b = 0; b < 4; ++b) {
+    float v[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const long long k = (long long)kb * 128 + b * 32 + t;
+      v[t] = n < N ? bf16_to_f32(src_kn ? W[k * N + n] : W[(long long)n * K + k]) : 0.0f;
+    }
+    uint32_t w[8];
+    sword |= (uint32_t)mx_block_quant(v, 32, w) << (8 * b);
+    *reinterpret_cast<uint4*>(row + (((2 * b) ^ pack_key(r)) << 4)) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(row + (((2 * b + 1) ^ pack_key(r)) << 4)) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  reinterpret_cast<uint32_t*>(sc)[blk * 256 + r] = sword;
+}
+
 }  // namespace moe

@@ -59,6 +59,9 @@ struct Stg {
 
 enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3 };
 enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
+// operand element type: bf16, or MXFP8 (OCP e4m3 codes with one E8M0 scale
+// per 32 consecutive K values, consumed by the block-scaled MFMA)
+enum { AT_BF16 = 0, AT_MX = 1 };
 
 struct GemmArgs {
   const uint16_t* A;        // [M_cap][K] grouped rows, K contiguous
@@ -81,6 +84,10 @@ struct GemmArgs {
   int mx_cols;              // columns of the quantised output (row length of row_q)
   int col_s_ld;             // ceil(M_cap/32) + E
   int ntiles_n;
+  // MXFP8 operands: A scales [M_cap][K/32]; B scales in the tile-blocked
+  // order [E][ceil(N/256)][K/128][256][4] (4 consecutive K blocks per row)
+  const uint8_t* a_scales;
+  const uint8_t* b_scales;
 };
 
 // Physical 16-byte chunk of logical chunk c in operand-tile row r.  The XOR
@@ -236,8 +243,17 @@ __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
 }
 
 // ---------------------------------------------------------------- the kernel
-template <int EPI, int BLAY>
+template <int EPI, int BLAY, int AT = AT_BF16>
 __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
+  // Operand rows are staged as 128-byte K slices whatever the type: 64 bf16
+  // (4 k-steps of v_mfma_f32_32x32x16_bf16) or 128 e4m3 (2 k-steps of
+  // v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8 stages also carry the tile's
+  // E8M0 scales: 256 rows x 4 bytes for A and for B after the two tiles.
+  constexpr bool MXT = AT == AT_MX;
+  constexpr int ESZ = MXT ? 1 : 2;            // operand element bytes
+  constexpr int KSTEPS = MXT ? 2 : 4;         // k-steps per K-tile
+  static_assert(!MXT || (BLAY == BL_PACKED && EPI == EPI_STORE), "MXFP8: packed B, plain store");
+  static_assert(2 * GM_TILE_BYTES + 2048 <= GM_STAGE_ALLOC, "scale slots");
   // Two distinct stage arrays: the compiler can then see that the LDS-DMA
   // writes of the next stage never alias the fragment reads of the current
   // one, and does not wait for the prefetch before computing.
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   // robin over 8), so give each XCD a contiguous run of tile ids per round.
   const int P = gridDim.x;
   const int slot = (P % 8 == 0) ? ((blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3)) : blockIdx.x;
-  const int nk = p.K / GM_BK;
+  const int nk = p.K * ESZ / 128;             // K-tiles of 128 bytes per row
   const int NT = p.ntiles_n;
   // LDS-DMA lane coordinates: a wave instruction fills 8 rows x 128 B
   const int rl = lane >> 3, pc = lane & 7;
@@ -300,18 +316,29 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 
     // ---- buffer descriptors: loads past the record count return zero, so
     // rows past M_cap (A) or past N (K-contiguous B) need no clamping.
-    const uint32_t a_stride = (uint32_t)p.K * 2u;
+    const uint32_t a_stride = (uint32_t)p.K * ESZ;
     const long long a_bytes = (long long)(p.M_cap - row0) * a_stride;
-    const rsrc_t rsA = make_rsrc(p.A + (long long)row0 * p.K, a_bytes);
-    const uint16_t* Bb = p.B + (long long)e * p.b_estride;
-    const uint32_t b_stride = (uint32_t)p.ldb * 2u;
+    const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A);
+    const rsrc_t rsA = make_rsrc(Ab + (long long)row0 * a_stride, a_bytes);
+    const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (long long)e * p.b_estride * ESZ;
+    const uint32_t b_stride = (uint32_t)p.ldb * ESZ;
     rsrc_t rsB;
     if (BLAY == BL_NK)
-      rsB = make_rsrc(Bb + (long long)n0 * p.ldb, (long long)(p.N - n0) * b_stride);
+      rsB = make_rsrc(Bb + (long long)n0 * b_stride, (long long)(p.N - n0) * b_stride);
     else if (BLAY == BL_PACKED)   // the n-tile's K/64 contiguous 32 KB blocks
-      rsB = make_rsrc(Bb + (long long)nt * nk * (GM_BN * GM_BK), (long long)nk * GM_TILE_BYTES);
+      rsB = make_rsrc(Bb + (long long)nt * nk * GM_TILE_BYTES, (long long)nk * GM_TILE_BYTES);
     else
-      rsB = make_rsrc(Bb, p.b_estride * 2);
+      rsB = make_rsrc(Bb, p.b_estride * ESZ);
+
+    // MXFP8 scales of the tile: A rows row0.. (K/32 bytes each), B's blocked
+    // 1 KB per K-tile
+    const uint32_t sa_stride = (uint32_t)p.K / 32u;
+    rsrc_t rsSA, rsSB;
+    if (MXT) {
+      rsSA = make_rsrc(p.a_scales + (long long)row0 * sa_stride,
+                       (long long)(p.M_cap - row0) * sa_stride);
+      rsSB = make_rsrc(p.b_scales + ((long long)e * NT + nt) * nk * 1024, (long long)nk * 1024);
+    }
 
     // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (8 rows);
     // the column chunk is clamped inside the row so no load leaves the matrix.
@@ -343,7 +370,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     };
     // K-tiles past the end are fetched through a descriptor with no records:
     // the loads return zeros, so the main loop needs no tail branch.
-    const rsrc_t rsZ = make_rsrc(p.A, 0);
+    const rsrc_t rsZ = make_rsrc(Ab, 0);
     // a packed 32 KB block is already in LDS order: each wave instruction
     // streams 1 KB contiguously
     auto issue_block = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t koff) {
@@ -355,17 +382,27 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     };
     auto issue_direct = [&](int kt, uint8_t* sa) {
       const bool in = kt < nk;
-      issue_tile(in ? rsA : rsZ, sa, a_stride, (uint32_t)kt * (GM_BK * 2));
+      issue_tile(in ? rsA : rsZ, sa, a_stride, (uint32_t)kt * 128u);
       if (BLAY == BL_NK)
-        issue_tile(in ? rsB : rsZ, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * (GM_BK * 2));
+        issue_tile(in ? rsB : rsZ, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * 128u);
       if (BLAY == BL_PACKED)
         issue_block(in ? rsB : rsZ, sa + GM_TILE_BYTES, (uint32_t)kt * GM_TILE_BYTES);
+      if (MXT) {   // 4 scale bytes per row: one dword per lane, 64 rows per wave
+        const uint32_t r = (uint32_t)(wave * 64 + lane_t);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            in ? rsSA : rsZ, (__attribute__((address_space(3))) void*)(sa + 2 * GM_TILE_BYTES + wave * 256),
+            4, r * sa_stride, (uint32_t)kt * 4u, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            in ? rsSB : rsZ,
+            (__attribute__((address_space(3))) void*)(sa + 2 * GM_TILE_BYTES + 1024 + wave * 256), 4,
+            r * 4u, (uint32_t)kt * 1024u, 0, 0);
+      }
     };
     u32x4 rb[8];
     auto kn_load = [&](int kt) {
       const bool in = kt < nk;
       const int ktc = in ? kt : 0;
-      const long long krow = (long long)ktc * GM_BK;
+      const long long krow = (long long)ktc * 64;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         rb[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsB : rsZ, kn_voff,
@@ -392,67 +429,114 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // sits before the LAST k-step of each K-tile: that k-step's fragments are
     // already in registers, so its 16 MFMAs keep the pipe busy while the next
     // stage's first fragments are read and the next DMA is issued.
-    bf16x8 af[2][4], bfr[2][4];
-    // reads in order of first use by the MFMA sequence (i outer, j inner)
-    auto frag_load = [&](const uint8_t* sa, int ks, int buf) {
+    bf16x8 af[2][4], bfr[2][4];                 // bf16 fragments
+    i32x8 afx[2][4], bfx[2][4];                 // e4m3 fragments (32 bytes per lane)
+    uint32_t sca[2][4], scb[2][4];              // E8M0 scales per stage set
+    // reads in order of first use by the MFMA sequence (i outer, j inner).
+    // bf16: lane half h = lane / 32 takes 16-byte chunk 2 ks + h of its row
+    // (8 k values).  e4m3: the block-scaled MFMA takes, in lane half h, bytes
+    // 0..15 = k 16 h .. + 15 of the step's first 32-block and bytes 16..31 =
+    // k 32 + 16 h .. + 15 of its second, so chunks 4 ks + h and 4 ks + 2 + h;
+    // the first block's scale comes from the lower-half lane of the row and
+    // the second block's from the upper-half lane.  With k-step 0 an MXFP8
+    // stage also yields its scales: the upper half shifts its dword down by
+    // one byte, so both halves select byte 2 ks in the MFMA (block 2 ks + h).
+    auto frag_load = [&](const uint8_t* sa, int ks, int buf, int sset) {
       const uint8_t* sb = sa + GM_TILE_BYTES;
-      const int ch = ks * 2 + (lane_t >> 5);
-      auto rd_a = [&](int i) {
-        af[buf][i] = *reinterpret_cast<const bf16x8*>(
-            sa + swz_off(wm * 128 + i * 32 + (lane_t & 31), ch));
-      };
-      auto rd_b = [&](int j) {
-        bfr[buf][j] = *reinterpret_cast<const bf16x8*>(
-            sb + swz_off(wn * 128 + j * 32 + (lane_t & 31), ch));
-      };
-      rd_a(0);
-      rd_b(0); rd_b(1); rd_b(2); rd_b(3);
-      rd_a(1); rd_a(2); rd_a(3);
-    };
-    // 16 MFMAs on fragment buffer buf; the 8 LDS reads issued just before
-    // are spread one per MFMA over the first 8, so each has at least 8 MFMAs
-    // of cover before its first use.
-    auto mfma_step = [&](int buf) {
+      const int h = lane_t >> 5;
+      const int ra = wm * 128 + (lane_t & 31), rbw = wn * 128 + (lane_t & 31);
+      if constexpr (!MXT) {
+        const int ch = ks * 2 + h;
+        auto rd_a = [&](int i) {
+          af[buf][i] = *reinterpret_cast<const bf16x8*>(sa + swz_off(ra + i * 32, ch));
+        };
+        auto rd_b = [&](int j) {
+          bfr[buf][j] = *reinterpret_cast<const bf16x8*>(sb + swz_off(rbw + j * 32, ch));
+        };
+        rd_a(0);
+        rd_b(0); rd_b(1); rd_b(2); rd_b(3);
+        rd_a(1); rd_a(2); rd_a(3);
+      } else {
+        const int ch = ks * 4 + h;
+        auto rd32 = [&](const uint8_t* t, int r) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(t + swz_off(r, ch));
+          const uint4 hi = *reinterpret_cast<const uint4*>(t + swz_off(r, ch + 2));
+          i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          return v;
+        };
+        if (ks == 0) {
+          const uint32_t* ssa = reinterpret_cast<const uint32_t*>(sa + 2 * GM_TILE_BYTES);
+          const uint32_t* ssb = reinterpret_cast<const uint32_t*>(sa + 2 * GM_TILE_BYTES + 1024);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) sca[sset][i] = ssa[ra + i * 32];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i],
-                                                              acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) scb[sset][j] = ssb[rbw + j * 32];
+        }
+        afx[buf][0] = rd32(sa, ra);
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        for (int j = 0; j < 4; ++j) bfx[buf][j] = rd32(sb, rbw + j * 32);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) afx[buf][i] = rd32(sa, ra + i * 32);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMA
-      __builtin_amdgcn_sched_barrier(0);
     };
-    // The same 16 MFMAs with the next stage's DMA (16 VMEM instructions per
-    // wave) spread over them, one per MFMA: issued as a burst right after the
-    // barrier, the four waves' 64 DMA instructions queue at the address unit
-    // and hold up the MFMAs issued behind them.
-    auto mfma_step_dma = [&](int buf) {
+    // the 16 MFMAs of one k-step on fragment buffer buf (k-step ks of the
+    // K-tile, scale set sset)
+    auto mfmas = [&](int buf, int sset, int ks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i],
-                                                              acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (!MXT) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i],
+                                                                acc[i][j], 0, 0, 0);
+          } else {
+            const uint32_t sh = 8u * (uint32_t)(lane >> 5);
+            const int sB = (int)(scb[sset][j] >> sh), sA = (int)(sca[sset][i] >> sh);
+            if (ks == 0)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  bfx[buf][j], afx[buf][i], acc[i][j], 0, 0, 0, sB, 0, sA);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  bfx[buf][j], afx[buf][i], acc[i][j], 0, 0, 2, sB, 2, sA);
+          }
+        }
+    };
+    // LDS reads issued by the frag_load just before a k-step
+    constexpr int DS_STEP = MXT ? 16 : 8;
+    // 16 MFMAs; the LDS reads issued just before are spread over them from
+    // the first MFMA on, so each has many MFMAs of cover before its use
+    auto mfma_step = [&](int buf, int sset, int ks) {
+      mfmas(buf, sset, ks);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
-        if (g < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);               // 1 VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
+        if (g < DS_STEP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    // k-steps 0..2 of the K-tile in stage sa (fragments of k-step 0 requested)
-    auto first_steps = [&](const uint8_t* sa) {
+    // The same with the next stage's DMA (16 VMEM instructions per wave, 18
+    // with MXFP8 scales) spread over the MFMAs, one per MFMA: issued as a
+    // burst right after the barrier, the four waves' DMA instructions queue
+    // at the address unit and hold up the MFMAs issued behind them.
+    auto mfma_step_dma = [&](int buf, int sset, int ks) {
+      mfmas(buf, sset, ks);
 #pragma unroll
-      for (int ks = 0; ks < 3; ++ks) {
+      for (int g = 0; g < 16; ++g) {
+        if (g < DS_STEP) __builtin_amdgcn_sched_group_barrier(0x100, MXT ? 2 : 1, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                         // 1 VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // 1 MFMA
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // k-steps 0 .. KSTEPS-2 of the K-tile in stage sa (fragments of k-step 0
+    // requested); the last k-step runs after the stage barrier
+    auto first_steps = [&](const uint8_t* sa, int sset) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS - 1; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
-        frag_load(sa, ks + 1, (ks + 1) & 1);
-        mfma_step(ks & 1);
+        frag_load(sa, ks + 1, (ks + 1) & 1, sset);
+        mfma_step(ks & 1, sset, ks);
       }
     };
     // every wave's reads of a stage done and every wave's DMA into the other
@@ -473,22 +557,22 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     issue_direct(1, lds1);
     if (BLAY == BL_KN) kn_load(1);
     __builtin_amdgcn_sched_barrier(0);
-    frag_load(lds0, 0, 0);
+    frag_load(lds0, 0, 0, 0);
     for (int kt = 0; kt < nk; kt += 2) {
-      first_steps(lds0);
+      first_steps(lds0, 0);
       if (BLAY == BL_KN) kn_store(lds1);
       stage_barrier();
       issue_direct(kt + 2, lds0);
       if (BLAY == BL_KN) kn_load(kt + 2);
-      frag_load(lds1, 0, 0);
-      mfma_step_dma(1);                  // k-step 3 of K-tile kt
-      first_steps(lds1);
+      frag_load(lds1, 0, 0, 1);
+      mfma_step_dma(1, 0, KSTEPS - 1);   // last k-step of K-tile kt
+      first_steps(lds1, 1);
       if (BLAY == BL_KN) kn_store(lds0);
       stage_barrier();
       issue_direct(kt + 3, lds1);
       if (BLAY == BL_KN) kn_load(kt + 3);
-      frag_load(lds0, 0, 0);
-      mfma_step_dma(1);                  // k-step 3 of K-tile kt + 1
+      frag_load(lds0, 0, 0, 0);
+      mfma_step_dma(1, 1, KSTEPS - 1);   // last k-step of K-tile kt + 1
     }
     // the loop leaves one DMA (a K-tile past the end: zeros) and one set of
     // fragment reads in flight; the epilogue reuses both stage arrays

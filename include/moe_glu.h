@@ -125,7 +125,8 @@ typedef struct {
   int32_t dtype;            /* moe_dtype_t */
   int32_t layout;           /* A: ignored (always [M_cap][K] row-major); B: moe_b_layout_t */
   const void* data;         /* bf16 or e4m3 elements */
-  const uint8_t* scales;    /* MXFP8 only: A [M_cap][K/32]; B [E][N][K/32] */
+  const uint8_t* scales;    /* MXFP8 only: A [M_cap][K/32] E8M0 (block b of row r covers K
+                               values 32b..32b+31); B from moe_pack_weight_mx */
 } moe_operand_t;
 
 /* Reads the device's compute-unit count once; call before graph capture.
@@ -153,6 +154,29 @@ size_t moe_packed_weight_bytes(int E, int N, int K);
  * as MOE_B_NK with N = H, K = 2I.  Bit-exact (a permutation plus zero padding). */
 moe_status_t moe_pack_weight(const void* src, int E, int N, int K, int src_layout, void* dst,
                              void* stream);
+
+/* MXFP8 weight for the block-scaled GroupGemm ([BLOG] "Fusionando
+ * cuantización MXFP8…": MXFP8 blocks of 32 values with one E8M0 scale; here a
+ * weight quantised once, offline, along the reduction dimension K).
+ * Element bytes: per expert ceil(N/256) * 256 * K (e4m3fn codes), as blocks
+ * of 256 rows (n) by 128 K values = 32 KiB; block (nb, kb) starts at byte
+ * (nb * K/128 + kb) * 32768 of the expert; the 16-byte chunk c (0..7, k =
+ * 128 kb + 16 c .. +15) of row r sits at byte r * 128 + 16 * (c XOR s(r)),
+ * s(r) as above.  Scale bytes: per expert ceil(N/256) * 256 * K/32; the
+ * dword at byte ((nb * K/128 + kb) * 256 + r) * 4 holds the E8M0 scales of
+ * row r's four 32-blocks of block (nb, kb), block b in byte b.  Rows n >= N
+ * are zero with scale byte 0.  Requires K % 128 == 0. */
+size_t moe_packed_mx_weight_bytes(int E, int N, int K);
+size_t moe_packed_mx_scale_bytes(int E, int N, int K);
+
+/* Quantises a bf16 weight to that MXFP8 layout: for each output column n and
+ * each run of 32 consecutive k, amax gives the E8M0 exponent X (the smallest
+ * power of two with amax / 2^X <= 448; 0xFF if a value is NaN) and every
+ * value becomes e4m3fn(v / 2^X), rounded to nearest even.  src_layout as for
+ * moe_pack_weight (FC2's W2 [E][I][H]: MOE_B_KN with N = H, K = I).
+ * Requires N % 64 == 0, K % 128 == 0; dst_q, dst_s 16-byte aligned. */
+moe_status_t moe_pack_weight_mx(const void* src, int E, int N, int K, int src_layout,
+                                void* dst_q, void* dst_s, void* stream);
 
 /* Bytes of the packed W1 for E experts, hidden H, intermediate I:
  * moe_packed_weight_bytes(E, 2I, H). */
@@ -228,8 +252,14 @@ moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, i
 /* GroupGemm + Quantize ([BLOG] kernel family, first kernel): out_e = A_e . B_e
  * with bf16 and/or MXFP8 output.  A: [M_cap][K] grouped rows; B per the
  * layout in b->layout (MOE_B_PACKED is the fast path).  c_bf16: nullable bf16
- * [M_cap][N].  bf16 x bf16 on every B layout.
- * Requires K % 64 == 0, N % 64 == 0. */
+ * [M_cap][N].  bf16 x bf16 on every B layout, or MXFP8 x MXFP8 ([BLOG]
+ * "GroupGemm + Quantize" with MXFP8 inputs): A = e4m3fn [M_cap][K] with E8M0
+ * row-block scales [M_cap][K/32] (e.g. the row-wise MX output of
+ * moe_group_gemm_glu_fwd), B = MOE_B_PACKED from moe_pack_weight_mx, and
+ *     out_e = sum_k (q_a * 2^(s_a - 127)) (q_b * 2^(s_b - 127))
+ * accumulated in fp32 by the block-scaled MFMA.  Mixed bf16 / MXFP8 inputs
+ * are MOE_ERR_UNSUPPORTED.  Requires K % 64 == 0 (K % 128 == 0 for MXFP8),
+ * N % 64 == 0. */
 moe_status_t moe_group_gemm_quant(const moe_operand_t* a, const moe_operand_t* b, int N, int K,
                                   const moe_groups_t* groups, void* c_bf16,
                                   const moe_mx_out_t* mx, int cu_margin, void* stream);

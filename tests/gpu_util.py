@@ -46,13 +46,17 @@ def empty_bytes(shape, sentinel=BYTE_SENTINEL):
     return t.full(shape, sentinel, dtype=t.uint8, device="cuda")
 
 
-def assert_bf16_close(gpu_bits, ref_bits, rtol=2e-2, what="", normwise=None):
+def assert_bf16_close(gpu_bits, ref_bits, rtol=2e-2, what="", normwise=None, extra=None):
+    """``extra``: an additional element-wise absolute bound (e.g. for sums
+    whose hardware accumulation is not strict fp32)."""
     g = F.bf16_bits_to_f64(gpu_bits)
     r = F.bf16_bits_to_f64(ref_bits)
     assert g.shape == r.shape, (what, g.shape, r.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU values"
     err = np.abs(g - r)
     bound = rtol * (1.0 + np.abs(r))
+    if extra is not None:
+        bound = bound + extra
     bad = err > bound
     if np.any(bad):
         idx = np.argwhere(bad)[:5]
@@ -108,3 +112,31 @@ def packed_layout(w_nk: np.ndarray) -> np.ndarray:
         out[:, :, :, r, c ^ key, :] = blocks[:, :, :, r, c, :]
     return out.reshape(-1)
 
+
+
+def dev_bytes(a: np.ndarray):
+    """uint8 numpy -> uint8 cuda tensor."""
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def packed_mx_layout(q_nk: np.ndarray, s_nk: np.ndarray):
+    """The MXFP8 weight format documented in include/moe_glu.h, written out in
+    numpy from its definition: codes [E][N][K] -> blocks of 256 rows x 128
+    bytes, block (nb, kb) at (nb * K/128 + kb) * 32768, chunk c of row r at
+    16 * (c ^ s(r)); scales [E][N][K/32] -> one dword per (nb, kb, r) holding
+    the row's four block scales of that K-tile.  Rows past N are zero."""
+    E, N, K = q_nk.shape
+    NB, KB = (N + 255) // 256, K // 128
+    qp = np.zeros((E, NB * 256, K), dtype=np.uint8)
+    qp[:, :N] = q_nk
+    sp = np.zeros((E, NB * 256, K // 32), dtype=np.uint8)
+    sp[:, :N] = s_nk
+    blocks = qp.reshape(E, NB, 256, KB, 8, 16).transpose(0, 1, 3, 2, 4, 5)   # e nb kb r c b
+    out = np.zeros((E, NB, KB, 256, 8, 16), dtype=np.uint8)
+    r = np.arange(256)
+    key = (r % 8) ^ ((r // 8) % 4)
+    for c in range(8):
+        out[:, :, :, r, c ^ key, :] = blocks[:, :, :, r, c, :]
+    sc = sp.reshape(E, NB, 256, KB, 4).transpose(0, 1, 3, 2, 4)                # e nb kb r b
+    return out.reshape(-1), np.ascontiguousarray(sc).reshape(-1)

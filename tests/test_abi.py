@@ -97,6 +97,23 @@ def test_host_argument_errors_return_before_launch():
     assert G.raw_call("moe_pack_weight", fake, 2, 100, 128, G.B_NK, fake, NULL) == 2
     assert G.raw_call("moe_pack_weight", fake, 2, 256, 128, G.B_PACKED, fake, NULL) == 4
     assert G.raw_call("moe_pack_weight", fake + 2, 2, 256, 128, G.B_KN, fake, NULL) == 3
+    # MXFP8 weight pack: K a multiple of 128
+    assert G.raw_call("moe_pack_weight_mx", fake, 2, 256, 192, G.B_KN, fake, fake, NULL) == 2
+    assert G.raw_call("moe_pack_weight_mx", fake, 2, 256, 256, G.B_KN, fake, NULL, NULL) == 1
+    assert G.moe_packed_mx_weight_bytes(2, 300, 256) == 2 * 512 * 256
+    assert G.moe_packed_mx_scale_bytes(2, 300, 256) == 2 * 512 * 8
+    # MXFP8 GroupGemm: both operands MXFP8, B packed, scales present, K % 128 == 0
+    amx = G.operand(fake, dtype=G.DT_MXFP8, scales=fake)
+    bmx = G.operand(fake, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=fake)
+    bbf = G.operand(fake, layout=G.B_PACKED)
+    bmx_kn = G.operand(fake, dtype=G.DT_MXFP8, layout=G.B_KN, scales=fake)
+    bmx_ns = G.operand(fake, dtype=G.DT_MXFP8, layout=G.B_PACKED)
+    args = (256, 256, ctypes.byref(grp), fake, NULL, 0, NULL)
+    assert G.raw_call("moe_group_gemm_quant", ctypes.byref(amx), ctypes.byref(bbf), *args) == 4
+    assert G.raw_call("moe_group_gemm_quant", ctypes.byref(amx), ctypes.byref(bmx_kn), *args) == 4
+    assert G.raw_call("moe_group_gemm_quant", ctypes.byref(amx), ctypes.byref(bmx_ns), *args) == 1
+    assert G.raw_call("moe_group_gemm_quant", ctypes.byref(amx), ctypes.byref(bmx), 256, 192,
+                      ctypes.byref(grp), fake, NULL, 0, NULL) == 2
     # packed sizes: experts padded to 256 rows
     assert G.moe_packed_weight_bytes(3, 300, 128) == 3 * 512 * 128 * 2
     assert G.moe_packed_w1_bytes(2, 192, 64) == 2 * 256 * 192 * 2

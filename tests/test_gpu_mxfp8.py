@@ -1,0 +1,168 @@
+"""GPU parity of the MXFP8 x MXFP8 GroupGemm (block-scaled MFMA) and of the
+offline MXFP8 weight pack, through the C ABI, against the CPU oracle.
+
+MXFP8 here follows "Boosting MoE Training Throughput with Advanced Fusion
+Kernels", section "Fusionando cuantización MXFP8…": blocks of 32 values along
+the reduction dimension, one E8M0 scale each, e4m3 elements.  Quantised codes
+and scales are compared bit-exactly; the GEMM's bf16 output within
+    |gpu - ref| <= 2e-2 (1 + |ref|) + 2^-14 sum_k |a_k b_k|
+of the exact dequantise-then-multiply result.  The second term covers the
+block-scaled MFMA's internal accumulation, which is not strict fp32: under
+heavy cancellation (student-t rows, sum |a b| / |result| ~ 10^4) it deviates
+by up to about 2^-17 sum |a b|.  A wrong scale or a misplaced K block gives
+errors of the order of sum |a b| itself.
+Every expected value comes from the oracle on oracle-side inputs.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import moe as O
+from tests.gpu_util import (BF16_NAN_SENTINEL, assert_bf16_close, dev_bits, dev_bytes, dev_i32,
+                            empty_bits, empty_bytes, host_bits, packed_mx_layout)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_gemm_glu_amd as G
+    G.moe_init(0)
+    return G
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _weight_nk(seed, E, N, K, std=0.05):
+    """bf16 [E][N][K] with per-row magnitudes spread over 2^-20 .. 2^20 and an
+    all-zero 32-block, so scales cover a wide exponent range."""
+    g = np.random.default_rng(seed)
+    w = g.standard_normal((E, N, K)).astype(np.float32) * np.float32(std)
+    w *= (2.0 ** g.integers(-20, 21, size=(E, N, 1))).astype(np.float32)
+    w[0, 0, :32] = 0.0
+    return W.to_bf16_bits(w)
+
+
+def _oracle_weight_mx(w_nk):
+    E, N, K = w_nk.shape
+    bq = np.zeros((E, N, K), np.uint8)
+    bs = np.zeros((E, N, K // 32), np.uint8)
+    for e in range(E):
+        bq[e], bs[e] = O.mx_quantize_rows(w_nk[e])
+    return bq, bs
+
+
+def _abs_bound(aq, as_, counts, bq, bs):
+    """2^-14 sum_k |a_k b_k| per output element, from the oracle's dequantised operands."""
+    counts = np.asarray(counts)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    out = np.zeros((int(off[-1]), bq.shape[1]))
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            A = np.abs(O.mx_dequantize_rows(aq[a:b], as_[a:b]))
+            B = np.abs(O.mx_dequantize_rows(bq[e], bs[e]))
+            out[a:b] = A @ B.T
+    return out * 2.0 ** -14
+
+
+def _pack_mx_gpu(G, w_nk, layout):
+    E, N, K = w_nk.shape
+    src = w_nk if layout == "NK" else np.ascontiguousarray(np.transpose(w_nk, (0, 2, 1)))
+    d_q = empty_bytes((G.moe_packed_mx_weight_bytes(E, N, K),))
+    d_s = empty_bytes((G.moe_packed_mx_scale_bytes(E, N, K),))
+    G.moe_pack_weight_mx(dev_bits(src), E, N, K, G.B_NK if layout == "NK" else G.B_KN, d_q, d_s)
+    return d_q, d_s
+
+
+@pytest.mark.parametrize("layout,E,N,K", [("KN", 2, 192, 256), ("NK", 1, 256, 128),
+                                          ("KN", 3, 320, 384)])
+def test_pack_weight_mx_bit_exact(G, layout, E, N, K):
+    w_nk = _weight_nk(N + K + E, E, N, K)
+    d_q, d_s = _pack_mx_gpu(G, w_nk, layout)
+    _sync()
+    q_ref, s_ref = packed_mx_layout(*_oracle_weight_mx(w_nk))
+    assert np.array_equal(d_q.cpu().numpy(), q_ref)
+    assert np.array_equal(d_s.cpu().numpy(), s_ref)
+
+
+def _group_gemm_mx_gpu(G, aq, as_, counts, d_q, d_s, N, K, m_cap):
+    c = empty_bits((m_cap, N))
+    a_op = G.operand(dev_bytes(aq), dtype=G.DT_MXFP8, scales=dev_bytes(as_))
+    b_op = G.operand(d_q, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=d_s)
+    G.moe_group_gemm_quant(a_op, b_op, N, K, G.groups(dev_i32(counts), m_cap), c)
+    _sync()
+    return host_bits(c)
+
+
+@pytest.mark.parametrize("counts,K,N", [([300, 0, 213], 384, 320),   # odd K-tile count
+                                        ([700, 129], 256, 256),      # several m-tiles
+                                        ([5], 128, 64),              # one partial tile
+                                        ([0, 0, 40, 0], 512, 192)])  # mostly empty experts
+def test_group_gemm_mx(G, counts, K, N):
+    counts = np.array(counts)
+    E, M = len(counts), int(counts.sum())
+    m_cap = M + 7
+    g = np.random.default_rng(K + N + M)
+    a = W.to_bf16_bits(g.standard_normal((m_cap, K)).astype(np.float32))
+    aq, as_ = O.mx_quantize_rows(a)
+    w_nk = W.to_bf16_bits((g.standard_normal((E, N, K)) * 0.05).astype(np.float32))
+    d_q, d_s = _pack_mx_gpu(G, w_nk, "KN")
+    out = _group_gemm_mx_gpu(G, aq, as_, counts, d_q, d_s, N, K, m_cap)
+    bq, bs = _oracle_weight_mx(w_nk)
+    ref = O.group_gemm_mx(aq[:M], as_[:M], counts, bq, bs)
+    assert_bf16_close(out[:M], ref, what="group_gemm_mx", normwise=1e-2,
+                      extra=_abs_bound(aq[:M], as_[:M], counts, bq, bs))
+    assert np.all(out[M:] == BF16_NAN_SENTINEL)
+
+
+def test_group_gemm_mx_heavy_tails(G):
+    """Student-t activations (config-5 style) with per-row magnitude spread."""
+    counts = np.array([260, 77])
+    E, M, K, N = 2, 337, 256, 128
+    a = W.student_t_rows_bf16(5, M, K)
+    aq, as_ = O.mx_quantize_rows(a)
+    w_nk = _weight_nk(9, E, N, K, std=0.02)
+    d_q, d_s = _pack_mx_gpu(G, w_nk, "NK")
+    out = _group_gemm_mx_gpu(G, aq, as_, counts, d_q, d_s, N, K, M)
+    bq, bs = _oracle_weight_mx(w_nk)
+    ref = O.group_gemm_mx(aq, as_, counts, bq, bs)
+    assert_bf16_close(out, ref, what="group_gemm_mx student-t", normwise=1e-2,
+                      extra=_abs_bound(aq, as_, counts, bq, bs))
+
+
+def test_fc1_mx_rows_feed_fc2_mx(G):
+    """FC1 + SwiGLU with the fused row-wise MXFP8 output, consumed directly by
+    the block-scaled FC2; the expected value is the oracle's own chain (FC1,
+    SwiGLU, MXFP8 rows, dequantise-then-multiply FC2)."""
+    import torch
+    counts = [200, 0, 57, 300]
+    E, H, I = 4, 128, 256
+    d = W.small_grouped(31, counts, H, I, m_cap=600)
+    m_cap, M = d["M_cap"], d["M"]
+    w1p = empty_bits((G.moe_packed_w1_bytes(E, H, I) // 2,))
+    G.moe_repack_gate_up(dev_bits(d["w1"]), E, H, I, w1p)
+    y = empty_bits((m_cap, I))
+    row_q, row_s = empty_bytes((m_cap, I)), empty_bytes((m_cap, I // 32))
+    grp = G.groups(dev_i32(d["counts"]), m_cap)
+    G.moe_group_gemm_glu_fwd(dev_bits(d["x"]), grp, w1p, H, I, G.epilogue("swiglu"), y, None,
+                             G.mx_out(row_q=row_q, row_s=row_s))
+    w2_nk = np.ascontiguousarray(np.transpose(d["w2"], (0, 2, 1)))      # [E][H][I]
+    d_q, d_s = _pack_mx_gpu(G, w2_nk, "NK")
+    out2 = empty_bits((m_cap, H))
+    G.moe_group_gemm_quant(G.operand(row_q, dtype=G.DT_MXFP8, scales=row_s),
+                           G.operand(d_q, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=d_s),
+                           H, I, grp, out2)
+    _sync()
+    _, ry = O.fc1_glu(d["x"][:M], d["counts"], d["w1"], O.Epilogue())
+    yq, ys = O.mx_quantize_rows(ry)
+    bq, bs = _oracle_weight_mx(w2_nk)
+    ref = O.group_gemm_mx(yq, ys, d["counts"], bq, bs)
+    assert_bf16_close(host_bits(out2)[:M], ref, what="fc1 mx -> fc2 mx", normwise=2e-2,
+                      extra=_abs_bound(yq, ys, d["counts"], bq, bs))

@@ -12,7 +12,8 @@ import pytest
 import workloads as W
 from oracle import formats as F
 from oracle import moe as O
-from tests.gpu_util import (BF16_NAN_SENTINEL, BYTE_SENTINEL, assert_bf16_close, dev_bits, dev_i32,
+from tests.gpu_util import (BF16_NAN_SENTINEL, BYTE_SENTINEL, assert_bf16_close, dev_bits, dev_bytes,
+                            dev_i32, packed_mx_layout,
                             empty_bits, empty_bytes, host_bits, packed_layout)
 
 pytestmark = pytest.mark.gpu
