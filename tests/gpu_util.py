@@ -140,3 +140,65 @@ def packed_mx_layout(q_nk: np.ndarray, s_nk: np.ndarray):
         out[:, :, :, r, c ^ key, :] = blocks[:, :, :, r, c, :]
     sc = sp.reshape(E, NB, 256, KB, 4).transpose(0, 1, 3, 2, 4)                # e nb kb r b
     return out.reshape(-1), np.ascontiguousarray(sc).reshape(-1)
+
+
+def _mx_block_check(gq, gs, gv, rq, rs, rv, what, max_flip=0.02):
+    """Blocks laid out as [..., nblk, 32] (codes, values) and [..., nblk] (scales).
+    Blocks whose 32 source values are bit-identical on both sides must give
+    identical bytes; the others (a bf16 rounding flip upstream) must still
+    dequantise to within one e4m3 step of the oracle value plus the flip."""
+    same = np.all(gv == rv, axis=-1)
+    assert np.array_equal(gq[same], rq[same]), f"{what}: codes differ on identical blocks"
+    assert np.array_equal(gs[same], rs[same]), f"{what}: scales differ on identical blocks"
+    frac = 1.0 - same.mean() if same.size else 0.0
+    assert frac <= max_flip, f"{what}: {frac:.3%} of blocks have different source values"
+    if np.any(~same):
+        scale = F.e8m0_value(gs[~same])[..., None]
+        deq = F.e4m3_decode(gq[~same]) * scale
+        ref = F.bf16_bits_to_f64(rv[~same])
+        gval = F.bf16_bits_to_f64(gv[~same])
+        bound = F.e4m3_ulp(np.abs(ref) / scale) * scale + np.abs(gval - ref)
+        assert np.all(np.abs(deq - ref) <= bound), f"{what}: flipped blocks out of bound"
+
+
+def assert_mx_rows(gpu_q, gpu_s, gpu_vals, ref_vals, what="mx rows", max_flip=0.02):
+    """Row-wise MXFP8 copy of a GPU bf16 tensor against the oracle's
+    quantisation of the ORACLE's values (ref_vals); the GPU values only pick
+    which blocks must match byte for byte.  max_flip bounds the fraction of
+    blocks whose source values differ (a GEMM output whose bf16 rounding flips
+    often, like dGLU's products, needs a large one)."""
+    from oracle import moe as O
+    rq, rs = O.mx_quantize_rows(ref_vals)
+    R, C = ref_vals.shape
+    nb = C // 32
+    _mx_block_check(gpu_q.reshape(R, nb, 32), gpu_s.reshape(R, nb), gpu_vals.reshape(R, nb, 32),
+                    rq.reshape(R, nb, 32), rs.reshape(R, nb), ref_vals.reshape(R, nb, 32), what,
+                    max_flip)
+
+
+def assert_mx_cols(gpu_q, gpu_s, gpu_vals, ref_vals, counts, m_cap, what="mx cols",
+                   max_flip=0.02):
+    """Transposed MXFP8 copy (32-row blocks restarting at each group) against
+    the oracle's quantisation of the oracle's values, as in assert_mx_rows."""
+    from oracle import moe as O
+    rq, rs = O.mx_quantize_cols(ref_vals, counts, m_cap=m_cap)
+    so = O.mx_scale_col_offsets(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    C = ref_vals.shape[1]
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        m = b - a
+        if m == 0:
+            continue
+        nb = (m + 31) // 32
+        pad = nb * 32 - m
+
+        def blocks(v):   # [m][C] -> [C][nb][32], the tail padded with equal zeros
+            t = np.concatenate([v, np.zeros((pad, C), v.dtype)]) if pad else v
+            return t.T.reshape(C, nb, 32)
+
+        gq = np.concatenate([gpu_q[:, a:b], np.zeros((C, pad), np.uint8)], axis=1).reshape(C, nb, 32)
+        rqe = np.concatenate([rq[:, a:b], np.zeros((C, pad), np.uint8)], axis=1).reshape(C, nb, 32)
+        _mx_block_check(gq, gpu_s[:, so[e]:so[e] + nb], blocks(gpu_vals[a:b]),
+                        rqe, rs[:, so[e]:so[e] + nb], blocks(ref_vals[a:b]), f"{what} group {e}",
+                        max_flip)

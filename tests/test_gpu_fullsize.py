@@ -91,8 +91,8 @@ def test_dsv3_fc2_sampled_rows(dsv3_run):
     experts = expert_of_rows(counts, rows)
     for e in np.unique(experts):
         rr = rows[experts == e]
-        # FC2 consumes the GPU's own y (isolates this GEMM from FC1's rounding)
-        ref = O.group_gemm(dsv3_run["y"][rr], [len(rr)], d["w2"][e:e + 1])
+        _, y_r = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
+        ref = O.group_gemm(y_r, [len(rr)], d["w2"][e:e + 1])
         assert_bf16_close(dsv3_run["out2"][rr], ref, what=f"dsv3 fc2 expert {e}")
 
 
@@ -103,8 +103,8 @@ def test_dsv3_dgrad_dglu_sampled_rows(dsv3_run):
     experts = expert_of_rows(counts, rows)
     for e in np.unique(experts):
         rr = rows[experts == e]
-        ref = O.dgrad_dglu(dsv3_run["dy2"][rr], [len(rr)], d["w2"][e:e + 1],
-                           dsv3_run["pre"][rr], O.Epilogue())
+        pre_r, _ = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
+        ref = O.dgrad_dglu(dsv3_run["dy2"][rr], [len(rr)], d["w2"][e:e + 1], pre_r, O.Epilogue())
         assert_bf16_close(dsv3_run["dgu"][rr], ref, what=f"dsv3 dgu expert {e}", normwise=2e-2)
 
 
@@ -115,7 +115,9 @@ def test_dsv3_dx_sampled_rows(dsv3_run):
     experts = expert_of_rows(counts, rows)
     for e in np.unique(experts):
         rr = rows[experts == e]
-        ref = O.dx(dsv3_run["dgu"][rr], [len(rr)], d["w1"][e:e + 1])
+        pre_r, _ = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
+        dgu_r = O.dgrad_dglu(dsv3_run["dy2"][rr], [len(rr)], d["w2"][e:e + 1], pre_r, O.Epilogue())
+        ref = O.dx(dgu_r, [len(rr)], d["w1"][e:e + 1])
         assert_bf16_close(dsv3_run["dx"][rr], ref, what=f"dsv3 dx expert {e}", normwise=2e-2)
 
 

@@ -12,9 +12,9 @@ import pytest
 import workloads as W
 from oracle import formats as F
 from oracle import moe as O
-from tests.gpu_util import (BF16_NAN_SENTINEL, BYTE_SENTINEL, assert_bf16_close, dev_bits, dev_bytes,
-                            dev_i32, packed_mx_layout,
-                            empty_bits, empty_bytes, host_bits, packed_layout)
+from tests.gpu_util import (BF16_NAN_SENTINEL, BYTE_SENTINEL, assert_bf16_close, assert_mx_cols,
+                            assert_mx_rows, dev_bits, dev_i32, empty_bits, empty_bytes, host_bits,
+                            packed_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -209,8 +209,9 @@ def test_fc1_row_permutation_within_group_bit_exact(G):
 
 def test_fc1_mx_epilogue_matches_oracle_quantisation(G):
     """The fused MXFP8 row-wise and transposed copies equal the oracle's
-    quantisation of the GPU's own bf16 y byte for byte, and y itself is within
-    tolerance of the oracle."""
+    quantisation of the oracle's y byte for byte wherever the 32 source values
+    agree bit for bit (all but rare bf16 rounding flips), and y itself is
+    within tolerance of the oracle."""
     counts = np.array([70, 0, 33, 256, 1, 300])
     E, H, I = len(counts), 192, 256          # K = 192: an odd number of 64-deep K-tiles
     m_cap = int(counts.sum()) + 5
@@ -219,13 +220,11 @@ def test_fc1_mx_epilogue_matches_oracle_quantisation(G):
     out = _fc1_gpu(G, x, counts, d["w1"], I, {}, m_cap=m_cap, mx=True)
     M = int(counts.sum())
     _check_fc1(out, x, counts, d["w1"], O.Epilogue(), m_cap, "mx")
-    q, s = O.mx_quantize_rows(out["y"][:M])
-    assert np.array_equal(out["row_q"][:M], q) and np.array_equal(out["row_s"][:M], s)
+    _, ry = O.fc1_glu(x[:M], counts, d["w1"], O.Epilogue())
+    assert_mx_rows(out["row_q"][:M], out["row_s"][:M], out["y"][:M], ry, "fc1 mx rows")
     assert np.all(out["row_q"][M:] == BYTE_SENTINEL)
-    cq, cs = O.mx_quantize_cols(out["y"][:M], counts, m_cap=m_cap)
-    assert np.array_equal(out["col_q"][:, :M], cq[:, :M])
+    assert_mx_cols(out["col_q"], out["col_s"], out["y"][:M], ry, counts, m_cap, "fc1 mx cols")
     used = O.mx_scale_col_offsets(counts)[-1]
-    assert np.array_equal(out["col_s"][:, :used], cs[:, :used])
     assert np.all(out["col_s"][:, used:] == BYTE_SENTINEL)
     assert np.all(out["col_q"][:, M:] == BYTE_SENTINEL)
 
@@ -289,12 +288,8 @@ def test_group_gemm_quant_bf16(G, layout):
     ref = O.group_gemm(a[:M], counts, b)
     assert_bf16_close(out["c"][:M], ref, what="group_gemm " + layout)
     assert np.all(out["c"][M:] == BF16_NAN_SENTINEL)
-    q, s = O.mx_quantize_rows(out["c"][:M])
-    assert np.array_equal(out["row_q"][:M], q) and np.array_equal(out["row_s"][:M], s)
-    cq, cs = O.mx_quantize_cols(out["c"][:M], counts, m_cap=m_cap)
-    used = O.mx_scale_col_offsets(counts)[-1]
-    assert np.array_equal(out["col_q"][:, :M], cq[:, :M])
-    assert np.array_equal(out["col_s"][:, :used], cs[:, :used])
+    assert_mx_rows(out["row_q"][:M], out["row_s"][:M], out["c"][:M], ref, "quant mx rows")
+    assert_mx_cols(out["col_q"], out["col_s"], out["c"][:M], ref, counts, m_cap, "quant mx cols")
 
 
 def test_group_gemm_quant_integer_exact(G):
@@ -366,13 +361,13 @@ def test_dglu_bwd(G, act, clamp, w2_layout):
     ref = O.dgrad_dglu(dy2[:M], counts, w2, pre[:M], O.Epilogue(row_scale=rs, **kw))
     assert_bf16_close(got[:M], ref, what=f"dgu {act}", normwise=2e-2)
     assert np.all(got[M:] == BF16_NAN_SENTINEL)
-    q, s = O.mx_quantize_rows(got[:M])
-    assert np.array_equal(bufs["row_q"].cpu().numpy()[:M], q)
-    assert np.array_equal(bufs["row_s"].cpu().numpy()[:M], s)
-    cq, cs = O.mx_quantize_cols(got[:M], counts, m_cap=m_cap)
-    used = O.mx_scale_col_offsets(counts)[-1]
-    assert np.array_equal(bufs["col_q"].cpu().numpy()[:, :M], cq[:, :M])
-    assert np.array_equal(bufs["col_s"].cpu().numpy()[:, :used], cs[:, :used])
+    # dgu's bf16 rounding flips in most 32-blocks (products of an fp32 GEMM
+    # output with the dGLU factors), so here the check is mostly the
+    # dequantised bound; the byte-exact path is covered by the FC1 tests
+    assert_mx_rows(bufs["row_q"].cpu().numpy()[:M], bufs["row_s"].cpu().numpy()[:M], got[:M], ref,
+                   f"dgu {act} mx rows", max_flip=1.0)
+    assert_mx_cols(bufs["col_q"].cpu().numpy(), bufs["col_s"].cpu().numpy(), got[:M], ref, counts,
+                   m_cap, f"dgu {act} mx cols", max_flip=1.0)
 
 
 # ---------------------------------------------------------------- unfused baseline kernels
