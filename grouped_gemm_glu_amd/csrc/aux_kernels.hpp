@@ -243,12 +243,9 @@ __device__ __forceinline__ uint8_t mx_block_quant(const float* v, int nvalid, ui
     return 0xFF;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t q = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) q |= f32_to_e4m3(ldexpf(v[4 * i + j], -E)) << (8 * j);
-    w[i] = q;
-  }
+  for (int i = 0; i < 8; ++i)
+    w[i] = e4m3x4(ldexpf(v[4 * i], -E), ldexpf(v[4 * i + 1], -E), ldexpf(v[4 * i + 2], -E),
+                  ldexpf(v[4 * i + 3], -E));
   return e8m0_byte(E);
 }
 

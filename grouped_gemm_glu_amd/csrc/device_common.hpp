@@ -76,6 +76,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
+// Four fp32 values -> four e4m3fn codes (byte k = value k) with the hardware
+// conversion v_cvt_pk_fp8_f32 (round to nearest even; identical to
+// f32_to_e4m3 for |x| <= 448, checked exhaustively over the bf16 values).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
 // ---------------------------------------------------------------- activations
 enum { ACT_SWIGLU = 0, ACT_GEGLU = 1, ACT_GEGLU_TANH = 2, ACT_SRELU = 3 };
 
@@ -83,6 +91,23 @@ enum { ACT_SWIGLU = 0, ACT_GEGLU = 1, ACT_GEGLU_TANH = 2, ACT_SRELU = 3 };
 // the results are rounded to bf16).
 __device__ __forceinline__ float sigmoidf_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// a(g) for a compile-time activation (epilogues dispatch once per launch,
+// not per element).
+template <int ACT>
+__device__ __forceinline__ float act_fwd_t(float g, float alpha) {
+  if constexpr (ACT == ACT_SWIGLU) {
+    return g * sigmoidf_fast(alpha * g);
+  } else if constexpr (ACT == ACT_GEGLU) {
+    return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+  } else if constexpr (ACT == ACT_GEGLU_TANH) {
+    const float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
+    return 0.5f * g * (1.0f + tanhf(u));
+  } else {
+    const float r = fmaxf(g, 0.0f);
+    return r * r;
+  }
 }
 
 __device__ __forceinline__ float act_fwd(int act, float g, float alpha) {

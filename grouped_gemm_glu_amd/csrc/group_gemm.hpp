@@ -165,12 +165,9 @@ __device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32
     return 0xFF;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t q = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) q |= f32_to_e4m3(ldexpf(v[4 * i + j], -E)) << (8 * j);
-    w[i] = q;
-  }
+  for (int i = 0; i < 8; ++i)
+    w[i] = e4m3x4(ldexpf(v[4 * i], -E), ldexpf(v[4 * i + 1], -E), ldexpf(v[4 * i + 2], -E),
+                  ldexpf(v[4 * i + 3], -E));
   return e8m0_byte(E);
 }
 
@@ -180,7 +177,7 @@ __device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32
 // col-wise: blocks of 32 rows starting at the tile's first row (a tile always
 // starts a block because tiles start at group row multiples of 256), scale
 // column scol0 + r / 32.
-__device__ void mx_from_stage(const Stg& stg, int rows_valid, int ncols, int grow0,
+__device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, int ncols, int grow0,
                               int col0, const GemmArgs& p, int scol0) {
   const int t = threadIdx.x + opaque_zero();
   if (p.row_q) {
@@ -596,142 +593,160 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       rsc[i] = (p.ep.row_scale && m < rows_valid) ? p.ep.row_scale[row0 + m] : 1.0f;
     }
 
-    if (EPI == EPI_GLU) {
-      // Straight from registers to HBM, no LDS and no barrier.  Pair wn of
-      // this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3.  For two
-      // column groups q = 2p, 2p + 1 a lane holds columns 8q + 4 (lane / 32)
-      // .. + 3 of its row; one v_permlane32_swap per dword gives lane l < 32
-      // columns 16p .. 16p + 7 and lane l + 32 columns 16p + 8 .. 16p + 15, so
-      // every lane stores 16 bytes and each row gets 32 contiguous bytes per
-      // store.  Descriptors cover the tile's valid rows only: stores of the
-      // rows past the group are dropped by the buffer range check.
+    if (EPI == EPI_GLU || EPI == EPI_GLU_MX) {
+      // y goes straight from registers to HBM, no LDS and no barrier.  Pair
+      // wn of this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3.  For
+      // two column groups q = 2p, 2p + 1 a lane holds columns 8q + 4 (lane /
+      // 32) .. + 3 of its row; one v_permlane32_swap per dword gives lane
+      // l < 32 columns 16p .. 16p + 7 and lane l + 32 columns 16p + 8 .. 16p +
+      // 15, so every lane stores 16 bytes and each row gets 32 contiguous
+      // bytes per store.  Descriptors cover the tile's valid rows only: stores
+      // of the rows past the group are dropped by the buffer range check.
+      // The pre-activation (twice y's bytes) leaves through one staged round
+      // of full-row stores instead.  With MXFP8 outputs, y is also staged (a
+      // round before the pre-activation's) for the row-wise and transposed
+      // quantisation.
+      constexpr bool MXO = EPI == EPI_GLU_MX;
       const int cvalid_n = min(128, p.I - nt * 128);
-      if (wn * 64 < cvalid_n) {
-        const long long ld2 = 2LL * p.I;
-        const uint16_t* bias_e = p.ep.bias ? p.ep.bias + (long long)e * ld2 : nullptr;
-        const int lh = (lane >> 5) + z0;
-        const rsrc_t rsY = make_rsrc(p.C ? p.C + (long long)row0 * p.I : p.A,
-                                     p.C ? (long long)rows_valid * p.I * 2 : 0);
-        const rsrc_t rsP = make_rsrc(p.preact ? p.preact + (long long)row0 * ld2 : p.A,
-                                     p.preact ? (long long)rows_valid * ld2 * 2 : 0);
+      const bool wave_on = wn * 64 < cvalid_n;
+      const long long ld2 = 2LL * p.I;
+      const int lh = (lane >> 5) + z0;
+      // bias of this lane's 16 gate and 16 up columns, loaded once per tile
+      // (all loads in flight together)
+      uint2 bgw[2][2][2], buw[2][2][2];
+      const bool has_bias = p.ep.bias != nullptr;
+      if (has_bias && wave_on) {
+        const uint16_t* bias_e = p.ep.bias + (long long)e * ld2;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = nt * 128 + wn * 64 + 32 * jj + 8 * q + 4 * lh;
+            bgw[jj][q >> 1][q & 1] = *reinterpret_cast<const uint2*>(bias_e + c);
+            buw[jj][q >> 1][q & 1] = *reinterpret_cast<const uint2*>(bias_e + p.I + c);
+          }
+      }
+      auto lo16 = [](uint32_t w) { return __uint_as_float(w << 16); };
+      auto hi16 = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+      // z = acc + bias for the 4 columns of column group q = 2 pp + h
+      auto zcols = [&](int i, int jj, int pp, int h, float (&g)[4], float (&u)[4]) {
+        const int q = 2 * pp + h;
+        const uint2 vg = bgw[jj][pp][h], vu = buw[jj][pp][h];
+        const float bg[4] = {lo16(vg.x), hi16(vg.x), lo16(vg.y), hi16(vg.y)};
+        const float bu[4] = {lo16(vu.x), hi16(vu.x), lo16(vu.y), hi16(vu.y)};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          g[s2] = acc[i][jj][4 * q + s2] + (has_bias ? bg[s2] : 0.0f);
+          u[s2] = acc[i][jj + 2][4 * q + s2] + (has_bias ? bu[s2] : 0.0f);
+        }
+      };
+      // stage the pre-activation: gate at columns 0..127, up at 128..255
+      auto stage_preact = [&](int i, int jj, int pp, int h, const float (&g)[4], const float (&u)[4]) {
+        const int c = wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
+        uint16_t* srow = wstg + ((wm * 128 + 32 * i + lm) & 127) * GM_STG_LD_256;
+        *reinterpret_cast<uint2*>(srow + c) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+        *reinterpret_cast<uint2*>(srow + 128 + c) =
+            make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
+      };
+      const rsrc_t rsY = make_rsrc(p.C ? p.C + (long long)row0 * p.I : p.A,
+                                   p.C ? (long long)rows_valid * p.I * 2 : 0);
+      auto body = [&](auto actc) {
+        constexpr int ACT = decltype(actc)::value;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
             __builtin_amdgcn_sched_barrier(0);
-            float bg[2][4], bu[2][4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int c = nt * 128 + wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
-#pragma unroll
-              for (int s2 = 0; s2 < 4; ++s2) bg[h][s2] = bu[h][s2] = 0.0f;
-              if (bias_e) {
-                const uint2 vg = *reinterpret_cast<const uint2*>(bias_e + c);
-                const uint2 vu = *reinterpret_cast<const uint2*>(bias_e + p.I + c);
-                bg[h][0] = __uint_as_float(vg.x << 16); bg[h][1] = __uint_as_float(vg.x & 0xFFFF0000u);
-                bg[h][2] = __uint_as_float(vg.y << 16); bg[h][3] = __uint_as_float(vg.y & 0xFFFF0000u);
-                bu[h][0] = __uint_as_float(vu.x << 16); bu[h][1] = __uint_as_float(vu.x & 0xFFFF0000u);
-                bu[h][2] = __uint_as_float(vu.y << 16); bu[h][3] = __uint_as_float(vu.y & 0xFFFF0000u);
-              }
-            }
             // byte offset of this lane's 16 bytes in row 0 of the tile
             const uint32_t ycol = (uint32_t)(wn * 64 + 32 * jj + 16 * pp + 8 * lh);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const uint32_t m = (uint32_t)(wm * 128 + 32 * i + lm);
-              uint32_t yw[2][2], gw[2][2], uw[2][2];
+              const int m = wm * 128 + 32 * i + lm;
+              uint32_t yw[2][2];
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
-                const int q = 2 * pp + h;
                 float o[4], g[4], u[4];
+                zcols(i, jj, pp, h, g, u);
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
-                  g[s2] = acc[i][jj][4 * q + s2] + bg[h][s2];
-                  u[s2] = acc[i][jj + 2][4 * q + s2] + bu[h][s2];
                   const float gc = fminf(fmaxf(g[s2], p.ep.gate_lo), p.ep.gate_hi);
                   const float uc = fminf(fmaxf(u[s2], p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
-                  o[s2] = act_fwd(p.ep.act, gc, p.ep.alpha) * uc * rsc[i];
+                  o[s2] = act_fwd_t<ACT>(gc, p.ep.alpha) * uc * rsc[i];
                 }
-                yw[h][0] = pack_bf16x2(o[0], o[1]); yw[h][1] = pack_bf16x2(o[2], o[3]);
-                gw[h][0] = pack_bf16x2(g[0], g[1]); gw[h][1] = pack_bf16x2(g[2], g[3]);
-                uw[h][0] = pack_bf16x2(u[0], u[1]); uw[h][1] = pack_bf16x2(u[2], u[3]);
+                yw[h][0] = pack_bf16x2(o[0], o[1]);
+                yw[h][1] = pack_bf16x2(o[2], o[3]);
+                if (MXO) {   // y staged for the MXFP8 round (128 columns)
+                  const int c = wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
+                  *reinterpret_cast<uint2*>(wstg + (m & 127) * GM_STG_LD_128 + c) =
+                      make_uint2(yw[h][0], yw[h][1]);
+                } else if (p.preact) {
+                  stage_preact(i, jj, pp, h, g, u);
+                }
               }
-              auto put = [&](uint32_t (&w)[2][2], const rsrc_t& rs, uint32_t off) {
-                const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
-                const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+              if (p.C) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(yw[0][0], yw[1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(yw[0][1], yw[1][1], false, false);
                 const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
-              };
-              put(yw, rsY, (m * (uint32_t)p.I + (uint32_t)nt * 128 + ycol) * 2u);
-              if (p.preact) {
-                const uint32_t prow = m * (uint32_t)ld2 + (uint32_t)nt * 128 + ycol;
-                put(gw, rsP, prow * 2u);
-                put(uw, rsP, (prow + (uint32_t)p.I) * 2u);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, rsY, ((uint32_t)m * (uint32_t)p.I + (uint32_t)nt * 128 + ycol) * 2u, 0, 0);
               }
             }
           }
+        }
+      };
+      // per row: gate columns nt*128 .. + 127 and up columns I + nt*128 ..
+      // + 127, 256 contiguous bytes each, 16 bytes per lane
+      auto store_preact = [&]() {
+        __syncthreads();
+        const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0,
+                      GM_STG_LD_256};
+        uint16_t* prow0 = p.preact + (long long)row0 * ld2 + nt * 128;
+        const int t = tid + z0;
+#pragma unroll 4
+        for (int it = t; it < GM_BM * 32; it += GM_NT) {
+          const int r = it >> 5, ch = it & 31, cc = (ch & 15) * 8;
+          if (r < rows_valid && cc < cvalid_n) {
+            const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
+            *reinterpret_cast<uint4*>(prow0 + r * ld2 + (ch < 16 ? 0 : p.I) + cc) = v;
+          }
+        }
+        __syncthreads();
+      };
+      // MXFP8 outputs: the pre-activation round first, so the accumulators
+      // are dead by the time the quantisation runs
+      if (MXO && p.preact) {
+        if (wave_on) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  float g[4], u[4];
+                  zcols(i, jj, pp, h, g, u);
+                  stage_preact(i, jj, pp, h, g, u);
+                }
+        }
+        store_preact();
+      }
+      if (wave_on) {
+        switch (p.ep.act) {
+          case ACT_SWIGLU: body(std::integral_constant<int, ACT_SWIGLU>{}); break;
+          case ACT_GEGLU: body(std::integral_constant<int, ACT_GEGLU>{}); break;
+          case ACT_GEGLU_TANH: body(std::integral_constant<int, ACT_GEGLU_TANH>{}); break;
+          default: body(std::integral_constant<int, ACT_SRELU>{}); break;
         }
       }
-    } else if (EPI == EPI_GLU_MX) {
-      // pair wn of this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3
-      const int ld = GM_STG_LD_128;
-      const int cvalid_n = min(128, p.I - nt * 128);
-      const long long ld2 = 2LL * p.I;
-      const uint16_t* bias_e = p.ep.bias ? p.ep.bias + (long long)e * ld2 : nullptr;
-      // round 0: y; round 1: gate pre-activation; round 2: up pre-activation
-#pragma unroll
-      for (int round = 0; round < 3; ++round) {
-        if (round > 0 && !p.preact) break;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int ycol = wn * 64 + 32 * jj + 8 * q + ln;   // 4 consecutive y columns
-            const int c = nt * 128 + ycol;                    // global gate column
-            float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias_e && c < p.I) {
-              const uint2 vg = *reinterpret_cast<const uint2*>(bias_e + c);
-              const uint2 vu = *reinterpret_cast<const uint2*>(bias_e + p.I + c);
-              bg[0] = __uint_as_float(vg.x << 16); bg[1] = __uint_as_float(vg.x & 0xFFFF0000u);
-              bg[2] = __uint_as_float(vg.y << 16); bg[3] = __uint_as_float(vg.y & 0xFFFF0000u);
-              bu[0] = __uint_as_float(vu.x << 16); bu[1] = __uint_as_float(vu.x & 0xFFFF0000u);
-              bu[2] = __uint_as_float(vu.y << 16); bu[3] = __uint_as_float(vu.y & 0xFFFF0000u);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int m = wm * 128 + 32 * i + lm;
-              float o[4];
-#pragma unroll
-              for (int s2 = 0; s2 < 4; ++s2) {
-                const float g = acc[i][jj][4 * q + s2] + bg[s2];
-                const float u = acc[i][jj + 2][4 * q + s2] + bu[s2];
-                if (round == 0) {
-                  const float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
-                  const float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
-                  o[s2] = act_fwd(p.ep.act, gc, p.ep.alpha) * uc * rsc[i];
-                } else {
-                  o[s2] = round == 1 ? g : u;
-                }
-              }
-              *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + ycol) =
-                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-            }
-          }
-        }
+      if (MXO) {
         __syncthreads();
-        if (round == 0) {
-          if (p.C)
-            store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, 128, p.C + (long long)row0 * p.I + nt * 128,
-                        p.I);
-          if (p.row_q || p.col_q)
-            mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, row0, nt * 128, p, gs.mxs_off[e] + mt * 8);
-        } else {
-          const int col0 = (round == 1 ? 0 : p.I) + nt * 128;
-          store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, 128, p.preact + (long long)row0 * ld2 + col0,
-                      ld2);
-        }
+        mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0,
+                          GM_STG_LD_128},
+                      rows_valid, cvalid_n, row0, nt * 128, p, gs.mxs_off[e] + mt * 8);
         __syncthreads();
+      } else if (p.preact) {
+        store_preact();
       }
     } else if (EPI == EPI_STORE) {
       const int ld = GM_STG_LD_256;
