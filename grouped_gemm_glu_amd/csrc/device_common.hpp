@@ -122,6 +122,31 @@ __device__ __forceinline__ float act_fwd(int act, float g, float alpha) {
   }
 }
 
+// a(g) and a'(g) for a compile-time activation.
+template <int ACT>
+__device__ __forceinline__ void act_fwd_bwd_t(float g, float alpha, float& a, float& da) {
+  if constexpr (ACT == ACT_SWIGLU) {
+    const float s = sigmoidf_fast(alpha * g);
+    a = g * s;
+    da = s * (1.0f + alpha * g * (1.0f - s));
+  } else if constexpr (ACT == ACT_GEGLU) {
+    const float cdf = 0.5f * (1.0f + erff(g * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * __expf(-0.5f * g * g);
+    a = g * cdf;
+    da = cdf + g * pdf;
+  } else if constexpr (ACT == ACT_GEGLU_TANH) {
+    const float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
+    const float t = tanhf(u);
+    const float du = 0.79788456080286536f * (1.0f + 3.0f * 0.044715f * g * g);
+    a = 0.5f * g * (1.0f + t);
+    da = 0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * du;
+  } else {
+    const float r = fmaxf(g, 0.0f);
+    a = r * r;
+    da = 2.0f * r;
+  }
+}
+
 // a(g) and a'(g) together (the backward epilogue needs both).
 __device__ __forceinline__ void act_fwd_bwd(int act, float g, float alpha, float& a, float& da) {
   switch (act) {

@@ -774,28 +774,57 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     } else {  // EPI_DGLU: acc = G = dL/dy for columns n0 .. n0+255 of I
       const int ld = GM_STG_LD_256;
       const long long ld2 = 2LL * p.I;
-      const int cvalid_n = min(GM_BN, p.I - n0);
-      // round 0: dg staged, du kept as packed bf16 in registers; round 1: du staged
-      uint32_t dupk[4][4][4][2];
+      const int lh = (lane >> 5) + z0;
+      // The saved pre-activation of this tile's rows comes in through a
+      // descriptor over rows row0 .. row0 + rows_valid - 1 (rows past it read
+      // zero; columns past I give values that are never stored).  Per column
+      // block j all 16 loads of 16 bytes are in flight together; lane half h
+      // loads columns 16p + 8h .. + 7 of the pair p, and one v_permlane32_swap
+      // per dword turns that into the MFMA layout (columns 8q + 4h .. + 3).
+      // Two rounds, each finishing half of every wave's columns (blocks j =
+      // 2r, 2r + 1): the staged row holds [dg wn0 | dg wn1 | du wn0 | du wn1],
+      // 64 columns each, and goes out as four 128-byte row segments.
+      const rsrc_t rsPre = make_rsrc(p.preact + (long long)row0 * ld2,
+                                     (long long)rows_valid * ld2 * 2);
+      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld};
+      auto do_block = [&](auto actc, auto jc) {
+        constexpr int ACT = decltype(actc)::value;
+        constexpr int j = decltype(jc)::value;
+        u32x4 lg[4][2], lu[4][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t rowb = (uint32_t)(wm * 128 + 32 * i + lm) * (uint32_t)ld2 * 2u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          __builtin_amdgcn_sched_barrier(0);
-          const int n = wn * 128 + 32 * j + 8 * q + ln;
-          const int c = n0 + n;                        // column of I (4 consecutive)
+          for (int pp = 0; pp < 2; ++pp) {
+            const uint32_t col = (uint32_t)(n0 + wn * 128 + 32 * j + 16 * pp + 8 * lh);
+            lg[i][pp] = __builtin_amdgcn_raw_buffer_load_b128(rsPre, rowb + col * 2u, 0, 0);
+            lu[i][pp] = __builtin_amdgcn_raw_buffer_load_b128(
+                rsPre, rowb + (col + (uint32_t)p.I) * 2u, 0, 0);
+          }
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = wm * 128 + 32 * i + lm;
-            float dg[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
-            if (m < rows_valid && c < p.I) {
-              const uint16_t* pr = p.preact + (long long)(row0 + m) * ld2 + c;
-              const uint2 vg = *reinterpret_cast<const uint2*>(pr);
-              const uint2 vu = *reinterpret_cast<const uint2*>(pr + p.I);
-              const float gv[4] = {__uint_as_float(vg.x << 16), __uint_as_float(vg.x & 0xFFFF0000u),
-                                   __uint_as_float(vg.y << 16), __uint_as_float(vg.y & 0xFFFF0000u)};
-              const float uv[4] = {__uint_as_float(vu.x << 16), __uint_as_float(vu.x & 0xFFFF0000u),
-                                   __uint_as_float(vu.y << 16), __uint_as_float(vu.y & 0xFFFF0000u)};
+        for (int i = 0; i < 4; ++i) {
+          const int m = wm * 128 + 32 * i + lm;
+          uint16_t* srow = wstg + (m & 127) * ld;
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            // w[h2][d]: dword d (columns 2d, 2d+1) of column group q = 2pp + h2
+            uint32_t gw[2][2], uw[2][2];
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const auto sg = __builtin_amdgcn_permlane32_swap(lg[i][pp][d], lg[i][pp][d + 2], false, false);
+              const auto su = __builtin_amdgcn_permlane32_swap(lu[i][pp][d], lu[i][pp][d + 2], false, false);
+              gw[0][d] = sg[0]; gw[1][d] = sg[1];
+              uw[0][d] = su[0]; uw[1][d] = su[1];
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const int q = 2 * pp + h2;
+              const float gv[4] = {__uint_as_float(gw[h2][0] << 16), __uint_as_float(gw[h2][0] & 0xFFFF0000u),
+                                   __uint_as_float(gw[h2][1] << 16), __uint_as_float(gw[h2][1] & 0xFFFF0000u)};
+              const float uv[4] = {__uint_as_float(uw[h2][0] << 16), __uint_as_float(uw[h2][0] & 0xFFFF0000u),
+                                   __uint_as_float(uw[h2][1] << 16), __uint_as_float(uw[h2][1] & 0xFFFF0000u)};
+              float dg[4], du[4];
 #pragma unroll
               for (int s2 = 0; s2 < 4; ++s2) {
                 const float G = acc[i][j][4 * q + s2] * rsc[i];
@@ -803,41 +832,70 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
                 const float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
                 const float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
                 float a, da;
-                act_fwd_bwd(p.ep.act, gc, p.ep.alpha, a, da);
+                act_fwd_bwd_t<ACT>(gc, p.ep.alpha, a, da);
                 const bool gin = (g >= p.ep.gate_lo) && (g <= p.ep.gate_hi);
                 const bool uin = (u >= p.ep.up_lo) && (u <= p.ep.up_hi);
                 dg[s2] = gin ? G * uc * da : 0.0f;
                 du[s2] = uin ? G * a : 0.0f;
               }
+              // staged column: wave's 64-column half (j & 1) at chunk wn (dg) / 2 + wn (du)
+              const int sc = wn * 64 + 32 * (j & 1) + 8 * q + ln;
+              *reinterpret_cast<uint2*>(srow + sc) =
+                  make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+              *reinterpret_cast<uint2*>(srow + 128 + sc) =
+                  make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
             }
-            *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + n) =
-                make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-            dupk[i][j][q][0] = pack_bf16x2(du[0], du[1]);
-            dupk[i][j][q][1] = pack_bf16x2(du[2], du[3]);
           }
         }
+      };
+      // (accumulator indices must stay compile-time constants, or the
+      // accumulators move to scratch memory: every block index is a template
+      // constant and both rounds are written out)
+      auto blocks = [&](auto actc, auto rc) {
+        constexpr int R = decltype(rc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        do_block(actc, std::integral_constant<int, 2 * R>{});
+        __builtin_amdgcn_sched_barrier(0);
+        do_block(actc, std::integral_constant<int, 2 * R + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto stage_round = [&](auto rc) {
+        switch (p.ep.act) {
+          case ACT_SWIGLU: blocks(std::integral_constant<int, ACT_SWIGLU>{}, rc); break;
+          case ACT_GEGLU: blocks(std::integral_constant<int, ACT_GEGLU>{}, rc); break;
+          case ACT_GEGLU_TANH: blocks(std::integral_constant<int, ACT_GEGLU_TANH>{}, rc); break;
+          default: blocks(std::integral_constant<int, ACT_SRELU>{}, rc); break;
+        }
+      };
 #pragma unroll
       for (int round = 0; round < 2; ++round) {
-        if (round == 1) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = wm * 128 + 32 * i + lm;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int n = wn * 128 + 32 * j + 8 * q + ln;
-                *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + n) =
-                    make_uint2(dupk[i][j][q][0], dupk[i][j][q][1]);
-              }
+        if (round == 0) stage_round(std::integral_constant<int, 0>{});
+        else stage_round(std::integral_constant<int, 1>{});
+        __syncthreads();
+        // staged chunk k (64 columns): dg (k < 2) or du, of wave half wn = k & 1;
+        // its first global column of I is n0 + 128 (k & 1) + 64 round
+        auto chunk_col = [&](int k) { return n0 + 128 * (k & 1) + 64 * round; };
+        if (p.C) {
+          const int t = tid + z0;
+#pragma unroll 4
+          for (int it = t; it < GM_BM * 32; it += GM_NT) {
+            const int r = it >> 5, k = (it >> 3) & 3, pc = it & 7;
+            const int c = chunk_col(k) + pc * 8;
+            if (r < rows_valid && c < p.I) {
+              const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + k * 64 + pc * 8);
+              *reinterpret_cast<uint4*>(p.C + (long long)(row0 + r) * ld2 + (k < 2 ? 0 : p.I) + c) = v;
+            }
           }
         }
-        __syncthreads();
-        const int ccol0 = (round == 0 ? 0 : p.I) + n0;
-        if (p.C)
-          store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * ld2 + ccol0, ld2);
-        if (p.row_q || p.col_q)
-          mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, row0, ccol0, p, gs.mxs_off[e] + mt * 8);
+        if (p.row_q || p.col_q) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int nv = min(64, p.I - chunk_col(k));
+            if (nv > 0)
+              mx_from_stage(Stg{stg.h0 + k * 64, stg.h1 + k * 64, ld}, rows_valid, nv, row0,
+                            (k < 2 ? 0 : p.I) + chunk_col(k), p, gs.mxs_off[e] + mt * 8);
+          }
+        }
         __syncthreads();
       }
     }
