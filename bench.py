@@ -15,7 +15,7 @@ when the timed region starts.  `value` is the step's algorithmic TFLOP/s
 (sum over experts of 2 m_e K N for the four GEMMs) divided by the measured
 step time.  The dominant kernel (FC1) is also timed on its own with HIP events
 on the launch stream, for the roofline entry.  The CPU oracle is timed on a
-bounded sample of the same step for `cpu_baseline`.
+the whole step (every routed row, float64) for `cpu_baseline`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -536,11 +536,11 @@ def read_traffic(path):
     return rec.get("fc1_hbm_bytes_per_launch")
 
 
-def cpu_baseline(d, dy2_h, rows_per_expert=768):
-    """The oracle, as it stands, on a bounded sample of the same step: the
-    first min(m_e, 768) rows of every expert through FC1+SwiGLU, FC2,
+def cpu_baseline(d, dy2_h, rows_per_expert=None):
+    """The oracle, as it stands, on the same step: by default every routed row
+    of every expert (the whole workload) through FC1+SwiGLU, FC2,
     dgrad+dSwiGLU and dX in float64 (numpy/BLAS), timed on this host's cores
-    (about 10-20 s of CPU work)."""
+    (about 10-20 s of CPU work); rows_per_expert caps each expert's rows."""
     from oracle import moe as O
     try:
         cores = len(os.sched_getaffinity(0))
@@ -552,7 +552,8 @@ def cpu_baseline(d, dy2_h, rows_per_expert=768):
     counts = d["counts"]
     off = np.concatenate([[0], np.cumsum(counts)])
     H, I = d["H"], d["I"]
-    c = np.minimum(counts, rows_per_expert).astype(np.int64)
+    cap = int(counts.max()) if rows_per_expert is None else rows_per_expert
+    c = np.minimum(counts, cap).astype(np.int64)
     sel = np.concatenate([np.arange(off[e], off[e] + c[e]) for e in range(len(counts))])
     xs, dys = d["x"][sel], dy2_h[sel]
     ep = O.Epilogue()
@@ -565,9 +566,10 @@ def cpu_baseline(d, dy2_h, rows_per_expert=768):
     flops = float(c.sum()) * (2 * H * 2 * I + 2 * I * H + 2 * H * I + 2 * 2 * I * H)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first min(m_e, {rows_per_expert}) rows of each of the 32 experts "
-                      f"({int(c.sum())} of {int(counts.sum())} rows) through the full step "
-                      "(FC1+SwiGLU, FC2, dgrad+dSwiGLU, dX), float64"}
+            "sample": (f"all {int(c.sum())} routed rows of the 32 experts" if rows_per_expert is None
+                       else f"first min(m_e, {cap}) rows of each of the 32 experts "
+                            f"({int(c.sum())} of {int(counts.sum())} rows)")
+                      + " through the full step (FC1+SwiGLU, FC2, dgrad+dSwiGLU, dX), float64"}
 
 
 if __name__ == "__main__":
