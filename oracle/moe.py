@@ -345,6 +345,41 @@ def dx(dgu_bits, counts, w1_bits, dtype=np.float64):
     return out
 
 
+def wgrad(a_bits, counts, b_bits, dtype=np.float64):
+    """Weight gradient as a K-grouped GroupGemm: for each expert e with rows
+    [o_e, o_e + m_e), C_e = A_e^T @ B_e, the reduction running over the
+    group's rows ("Boosting MoE Training Throughput with Advanced Fusion
+    Kernels": the column-wise copies exist "for back prop", i.e. for these
+    products).  dW1 = wgrad(Xg, dgu) [E][H][2I] (plain W1 order) and
+    dW2 = wgrad(y, dY2) [E][I][H].  An empty group gives zeros.  Returns
+    float64 [E][P][Q]; the GPU keeps fp32.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    P, Q = a_bits.shape[1], b_bits.shape[1]
+    out = np.zeros((len(counts), P, Q), dtype=np.float64)
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        out[e] = (_as_f(a_bits[a:b], dtype).T @ _as_f(b_bits[a:b], dtype)).astype(np.float64)
+    return out
+
+
+def wgrad_abs(a_bits, counts, b_bits):
+    """sum_k |a_k| |b_k| for every element of ``wgrad`` (the scale of its
+    rounding error under fp32 accumulation)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    P, Q = a_bits.shape[1], b_bits.shape[1]
+    out = np.zeros((len(counts), P, Q), dtype=np.float64)
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            out[e] = np.abs(bf16_bits_to_f64(a_bits[a:b])).T @ np.abs(bf16_bits_to_f64(b_bits[a:b]))
+    return out
+
+
 # ============================================================================ MXFP8
 MX_BLOCK = 32
 

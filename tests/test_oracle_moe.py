@@ -419,3 +419,76 @@ def test_group_gemm_mx_against_loops():
                     xb = F.e4m3_decode(bq[e, n, k]) * 2.0 ** (int(bs[e, n, k // 32]) - 127)
                     s += xa * xb
                 assert out[r, n] == F.f64_to_bf16_bits(np.array([s]))[0]
+
+
+# ------------------------------------------------------------------ weight gradients
+def test_wgrad_against_loops_and_empty_groups():
+    rng = np.random.default_rng(51)
+    counts = np.array([3, 0, 2])
+    M, P, Q = 5, 4, 6
+    a = W.to_bf16_bits(rng.standard_normal((M + 2, P)).astype(np.float32))
+    b = W.to_bf16_bits(rng.standard_normal((M + 2, Q)).astype(np.float32))
+    out = O.wgrad(a, counts, b)
+    assert out.shape == (3, P, Q)
+    assert np.all(out[1] == 0.0)
+    off = [0, 3, 3, 5]
+    A, B = F.bf16_bits_to_f64(a), F.bf16_bits_to_f64(b)
+    for e in range(3):
+        for i in range(P):
+            for j in range(Q):
+                s = 0.0
+                for r in range(off[e], off[e + 1]):
+                    s += A[r, i] * B[r, j]
+                assert out[e, i, j] == pytest.approx(s, rel=1e-15, abs=1e-300)
+    # rows past the routed ones never enter
+    b2 = b.copy()
+    b2[M:] = 0x7FC0
+    assert np.array_equal(O.wgrad(a, counts, b2), out)
+
+
+@pytest.mark.parametrize("act,ep_kw", [("swiglu", {}),
+                                       ("swiglu", dict(alpha=1.702, gate_lo=-0.7, gate_hi=0.7,
+                                                       up_lo=-0.7, up_hi=0.7)),
+                                       ("geglu", {})])
+def test_wgrads_against_finite_differences(act, ep_kw):
+    """dW1 = wgrad(X, dgu) and dW2 = wgrad(y, dY2) are the gradients of
+    L = <dY2, FC2(GLU(FC1(X)))> with respect to W1 and W2."""
+    counts, x, w1, b1, w2, dy2, ep = _tiny_chain(23, act, ep_kw)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    dz_all, y_all = [], []
+    for e in range(2):
+        a, b = off[e], off[e + 1]
+        z = x[a:b] @ w1[e] + b1[e]
+        dz_all.append(O.dglu(dy2[a:b] @ w2[e].T, z, ep))
+        y_all.append(O.glu_from_preact(z, ep))
+    dz, y = np.concatenate(dz_all), np.concatenate(y_all)
+    # the oracle takes bf16 bit patterns: dz and y are rounded to bf16 first,
+    # so compare within that rounding (2^-8 of sum |a||b|); a transposed or
+    # swapped operand, or rows of the wrong group, would miss by O(1)
+    dzb, yb = F.f64_to_bf16_bits(dz), F.f64_to_bf16_bits(y)
+    xb, dyb = F.f64_to_bf16_bits(x), F.f64_to_bf16_bits(dy2)
+    dW1, dW2 = O.wgrad(xb, counts, dzb), O.wgrad(yb, counts, dyb)
+    tol1 = 2.0 ** -8 * O.wgrad_abs(xb, counts, dzb) + 1e-9
+    tol2 = 2.0 ** -8 * O.wgrad_abs(yb, counts, dyb) + 1e-9
+    checked = 0
+    for e in range(2):
+        for (wname, wt, grad, tol) in (("w1", w1, dW1, tol1), ("w2", w2, dW2, tol2)):
+            for idx in [(0, 0), (1, 3), (wt.shape[1] - 1, wt.shape[2] - 1), (2, 5)]:
+                h = 1e-6 * max(1.0, abs(wt[e][idx]))
+                wp, wm = wt.copy(), wt.copy()
+                wp[e][idx] += h
+                wm[e][idx] -= h
+                args_p = (x, counts, wp, b1, w2, dy2, ep) if wname == "w1" else (x, counts, w1, b1, wp, dy2, ep)
+                args_m = (x, counts, wm, b1, w2, dy2, ep) if wname == "w1" else (x, counts, w1, b1, wm, dy2, ep)
+                fd = (_loss(*args_p) - _loss(*args_m)) / (2 * h)
+                if wname == "w1" and ep_kw:
+                    # skip perturbations that move a pre-activation across a clamp bound
+                    a, b = off[e], off[e + 1]
+                    z = x[a:b] @ w1[e] + b1[e]
+                    dzmax = 2 * h * np.max(np.abs(x[a:b, idx[0]]))
+                    bounds = [ep.gate_lo, ep.gate_hi, ep.up_lo, ep.up_hi]
+                    if np.any([np.any(np.abs(z - bd) <= 2 * dzmax) for bd in bounds]):
+                        continue
+                assert abs(fd - grad[e][idx]) <= tol[e][idx] + 1e-6 * abs(fd), (wname, e, idx, fd, grad[e][idx])
+                checked += 1
+    assert checked >= 12
