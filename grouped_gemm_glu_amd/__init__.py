@@ -72,6 +72,7 @@ _SIGS = {
                                  ctypes.POINTER(EpilogueT), _P, ctypes.POINTER(MxOutT), _I, _P], _I),
     "moe_group_gemm_quant": ([ctypes.POINTER(OperandT), ctypes.POINTER(OperandT), _I, _I,
                               ctypes.POINTER(GroupsT), _P, ctypes.POINTER(MxOutT), _I, _P], _I),
+    "moe_group_gemm_wgrad": ([_P, _P, _I, _I, ctypes.POINTER(GroupsT), _P, _I, _I, _P], _I),
     "moe_glu_unfused": ([_P, ctypes.POINTER(GroupsT), _I, ctypes.POINTER(EpilogueT), _P, _P], _I),
     "moe_mxfp8_quantize": ([_P, _I, _I, ctypes.POINTER(GroupsT), ctypes.POINTER(MxOutT), _P], _I),
 }
@@ -218,6 +219,13 @@ def moe_group_gemm_quant(a: OperandT, b: OperandT, N, K, grp: GroupsT, c_bf16=No
     _check("moe_group_gemm_quant",
            _lib.moe_group_gemm_quant(ctypes.byref(a), ctypes.byref(b), N, K, ctypes.byref(grp),
                                      _ptr(c_bf16), _ref(mx), cu_margin, _stream(stream)))
+
+
+def moe_group_gemm_wgrad(a, b, P, Q, grp: GroupsT, c, accumulate: bool = False,
+                         cu_margin: int = 0, stream=None):
+    _check("moe_group_gemm_wgrad",
+           _lib.moe_group_gemm_wgrad(_ptr(a), _ptr(b), P, Q, ctypes.byref(grp), _ptr(c),
+                                     1 if accumulate else 0, cu_margin, _stream(stream)))
 
 
 def moe_glu_unfused(z, grp: GroupsT, I, ep: EpilogueT, y, stream=None):

@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libmoeglu.so")
-SOURCES = ["api.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_mx.hip"]
+SOURCES = ["api.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_mx.hip", "gemm_wgrad.hip"]
 ARCH = "gfx950"
 
 

@@ -354,6 +354,36 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t
   return launch_group_gemm_fwd(EPI_STORE, blay, a, grid, (hipStream_t)stream);
 }
 
+moe_status_t moe_group_gemm_wgrad(const void* a, const void* b, int P, int Q,
+                                  const moe_groups_t* groups, float* c, int accumulate,
+                                  int cu_margin, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!a || !b || !c) return MOE_ERR_NULL;
+  if (P < 64 || P % 64 != 0 || Q < 64 || Q % 64 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MOE_ERR_ALIGN;
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  fill_groups(&g, groups);
+  g.A = static_cast<const uint16_t*>(a);
+  g.B = static_cast<const uint16_t*>(b);
+  g.ldb = Q;
+  g.N = Q;
+  g.K = 64;                       // unused: each tile reduces over its group's rows
+  g.wg_P = P;
+  g.ntiles_m = (P + GM_BM - 1) / GM_BM;
+  g.ntiles_n = (Q + GM_BN - 1) / GM_BN;
+  g.Cf = c;
+  g.accumulate = accumulate ? 1 : 0;
+  int usable = cus - (cu_margin > 0 ? cu_margin : 0);
+  if (usable < 1) usable = 1;
+  const long long tiles = (long long)groups->E * g.ntiles_m * g.ntiles_n;
+  const int grid = (int)(tiles < usable ? tiles : usable);
+  return launch_group_gemm_wgrad(g, grid, (hipStream_t)stream);
+}
+
 moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
                              const moe_epilogue_t* ep, void* y, void* stream) {
   moe_status_t st = check_groups(groups);

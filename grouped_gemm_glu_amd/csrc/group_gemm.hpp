@@ -57,7 +57,7 @@ struct Stg {
   }
 };
 
-enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3 };
+enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4 };
 enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 // operand element type: bf16, or MXFP8 (OCP e4m3 codes with one E8M0 scale
 // per 32 consecutive K values, consumed by the block-scaled MFMA)
@@ -88,6 +88,12 @@ struct GemmArgs {
   // order [E][ceil(N/256)][K/128][256][4] (4 consecutive K blocks per row)
   const uint8_t* a_scales;
   const uint8_t* b_scales;
+  // weight gradient (K-grouped): C_e [wg_P][N] fp32 = A_e^T B_e over the
+  // group's rows; A [M_cap][wg_P], B [M_cap][N] bf16
+  int wg_P;
+  int ntiles_m;             // ceil(wg_P / 256)
+  float* Cf;                // [E][wg_P][N]
+  int accumulate;           // 1: C += result
 };
 
 // Physical 16-byte chunk of logical chunk c in operand-tile row r.  The XOR
@@ -251,6 +257,11 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   constexpr int KSTEPS = MXT ? 2 : 4;         // k-steps per K-tile
   static_assert(!MXT || (BLAY == BL_PACKED && EPI == EPI_STORE), "MXFP8: packed B, plain store");
   static_assert(2 * GM_TILE_BYTES + 2048 <= GM_STAGE_ALLOC, "scale slots");
+  // Weight gradients reduce over a group's rows: both operands are stored
+  // [rows][columns] with the reduction dimension as the row index, so both
+  // go through the register transpose (the N-contiguous path).
+  constexpr bool WG = EPI == EPI_WGRAD;
+  static_assert(!WG || (BLAY == BL_KN && !MXT), "weight gradient: N-contiguous bf16 operands");
   // Two distinct stage arrays: the compiler can then see that the LDS-DMA
   // writes of the next stage never alias the fragment reads of the current
   // one, and does not wait for the prefetch before computing.
@@ -265,7 +276,22 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 
   build_group_scan<GM_NT>(gs, p.counts, p.E, p.M_cap, GM_BM, p.offsets_out, p.status_out,
                           blockIdx.x == 0);
-  const int total_tiles = gs.tile_off[p.E] * p.ntiles_n;
+  if (WG) {
+    // Every expert owns the same number of output tiles but its tiles cost
+    // m_e: hand them out largest group first (ties: lower id), the order kept
+    // in mxs_off (the MX scale prefix is not needed here).
+    for (int ee = tid; ee < p.E; ee += GM_NT) {
+      const int ce = gs.row_off[ee + 1] - gs.row_off[ee];
+      int rank = 0;
+      for (int j = 0; j < p.E; ++j) {
+        const int cj = gs.row_off[j + 1] - gs.row_off[j];
+        rank += (cj > ce) || (cj == ce && j < ee);
+      }
+      gs.mxs_off[rank] = ee;
+    }
+    __syncthreads();
+  }
+  const int total_tiles = WG ? p.E * p.ntiles_m * p.ntiles_n : gs.tile_off[p.E] * p.ntiles_n;
 
   // XCD-aware slot: consecutive workgroups land on different XCDs (round
   // robin over 8), so give each XCD a contiguous run of tile ids per round.
@@ -283,14 +309,23 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // ids an XCD takes per round shares few A panels and few B panels.
     int e, mt, nt;
     {
-      int lo = 0, hi = p.E;  // invariant: tile_off[lo]*NT <= tile < tile_off[hi]*NT
-      while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (gs.tile_off[mid] * NT <= tile) lo = mid; else hi = mid;
+      int local, MT;
+      if (WG) {   // weight gradient: p.ntiles_m x NT output tiles per expert
+        const int per = p.ntiles_m * NT;
+        const int rank = tile / per;
+        e = gs.mxs_off[rank];
+        local = tile - rank * per;
+        MT = p.ntiles_m;
+      } else {
+        int lo = 0, hi = p.E;  // invariant: tile_off[lo]*NT <= tile < tile_off[hi]*NT
+        while (hi - lo > 1) {
+          int mid = (lo + hi) >> 1;
+          if (gs.tile_off[mid] * NT <= tile) lo = mid; else hi = mid;
+        }
+        e = lo;
+        local = tile - gs.tile_off[e] * NT;
+        MT = gs.tile_off[e + 1] - gs.tile_off[e];
       }
-      e = lo;
-      const int local = tile - gs.tile_off[e] * NT;
-      const int MT = gs.tile_off[e + 1] - gs.tile_off[e];
       constexpr int BHT = 4, BWT = 8;
       const int band = local / (BHT * NT);
       const int bh = min(BHT, MT - band * BHT);
@@ -302,9 +337,12 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     }
     const int g_row0 = gs.row_off[e];
     const int m_e = gs.row_off[e + 1] - g_row0;
-    const int row0 = g_row0 + mt * GM_BM;            // first grouped row of the tile
-    const int rows_valid = min(GM_BM, m_e - mt * GM_BM);
+    // grouped GEMM: the tile's first grouped row; weight gradient: the
+    // group's first row (the reduction runs over all m_e rows)
+    const int row0 = WG ? g_row0 : g_row0 + mt * GM_BM;
+    const int rows_valid = WG ? min(GM_BM, p.wg_P - mt * GM_BM) : min(GM_BM, m_e - mt * GM_BM);
     const int n0 = nt * GM_BN;
+    const int nk_t = WG ? (m_e + 63) / 64 : nk;      // K-tiles of this tile
 
     // Per-tile opaque zero: main-loop addressing is recomputed for each tile,
     // so it is not live across the epilogue.
@@ -313,14 +351,18 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 
     // ---- buffer descriptors: loads past the record count return zero, so
     // rows past M_cap (A) or past N (K-contiguous B) need no clamping.
-    const uint32_t a_stride = (uint32_t)p.K * ESZ;
-    const long long a_bytes = (long long)(p.M_cap - row0) * a_stride;
+    const uint32_t a_stride = WG ? (uint32_t)p.wg_P * 2u : (uint32_t)p.K * ESZ;
+    // weight gradient: only the group's rows (the next group's rows read zero)
+    const long long a_bytes = (long long)(WG ? m_e : p.M_cap - row0) * a_stride;
     const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A);
     const rsrc_t rsA = make_rsrc(Ab + (long long)row0 * a_stride, a_bytes);
-    const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (long long)e * p.b_estride * ESZ;
+    const uint8_t* Bb = WG ? reinterpret_cast<const uint8_t*>(p.B) + (long long)row0 * p.ldb * 2
+                           : reinterpret_cast<const uint8_t*>(p.B) + (long long)e * p.b_estride * ESZ;
     const uint32_t b_stride = (uint32_t)p.ldb * ESZ;
     rsrc_t rsB;
-    if (BLAY == BL_NK)
+    if (WG)
+      rsB = make_rsrc(Bb, (long long)m_e * b_stride);
+    else if (BLAY == BL_NK)
       rsB = make_rsrc(Bb + (long long)n0 * b_stride, (long long)(p.N - n0) * b_stride);
     else if (BLAY == BL_PACKED)   // the n-tile's K/64 contiguous 32 KB blocks
       rsB = make_rsrc(Bb + (long long)nt * nk * GM_TILE_BYTES, (long long)nk * GM_TILE_BYTES);
@@ -342,6 +384,9 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     const int kn_c = (tid + zt) & 31, kn_g = (tid + zt) >> 5;
     const uint32_t kn_voff =
         (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
+    const uint32_t kn_voff_a =
+        WG ? (uint32_t)(kn_g * 8) * a_stride + (uint32_t)min(mt * GM_BM + kn_c * 8, p.wg_P - 8) * 2u
+           : 0u;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -378,8 +423,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       }
     };
     auto issue_direct = [&](int kt, uint8_t* sa) {
-      const bool in = kt < nk;
-      issue_tile(in ? rsA : rsZ, sa, a_stride, (uint32_t)kt * 128u);
+      const bool in = kt < nk_t;
+      if (!WG) issue_tile(in ? rsA : rsZ, sa, a_stride, (uint32_t)kt * 128u);
       if (BLAY == BL_NK)
         issue_tile(in ? rsB : rsZ, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * 128u);
       if (BLAY == BL_PACKED)
@@ -395,30 +440,39 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
             r * 4u, (uint32_t)kt * 1024u, 0, 0);
       }
     };
-    u32x4 rb[8];
+    u32x4 rb[8], ra[8];
     auto kn_load = [&](int kt) {
-      const bool in = kt < nk;
+      const bool in = kt < nk_t;
       const int ktc = in ? kt : 0;
       const long long krow = (long long)ktc * 64;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         rb[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsB : rsZ, kn_voff,
                                                       (uint32_t)((krow + i) * b_stride), 0);
+      if (WG) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          ra[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsA : rsZ, kn_voff_a,
+                                                        (uint32_t)((krow + i) * a_stride), 0);
+      }
     };
-    auto kn_store = [&](uint8_t* stage) {
-      uint8_t* sb = stage + GM_TILE_BYTES;
-      // rb[i] holds 8 columns at k = 8*kn_g + i; transpose to 8 k-values per column
+    // r[i] holds 8 columns at k = 8*kn_g + i; transposed to 8 k-values per column
+    auto kn_put = [&](const u32x4 (&r)[8], uint8_t* t) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint32_t o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = rb[2 * q][j >> 1], hi = rb[2 * q + 1][j >> 1];
+          const uint32_t lo = r[2 * q][j >> 1], hi = r[2 * q + 1][j >> 1];
           o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
         }
-        *reinterpret_cast<uint4*>(sb + swz_off(kn_c * 8 + j, kn_g)) =
+        *reinterpret_cast<uint4*>(t + swz_off(kn_c * 8 + j, kn_g)) =
             make_uint4(o[0], o[1], o[2], o[3]);
       }
+    };
+    auto kn_store = [&](uint8_t* stage) {
+      kn_put(rb, stage + GM_TILE_BYTES);
+      if (WG) kn_put(ra, stage);
     };
 
     // Fragments are double-buffered one k-step ahead.  A K-tile is 4 k-steps
@@ -555,7 +609,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     if (BLAY == BL_KN) kn_load(1);
     __builtin_amdgcn_sched_barrier(0);
     frag_load(lds0, 0, 0, 0);
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = 0; kt < nk_t; kt += 2) {
       first_steps(lds0, 0);
       if (BLAY == BL_KN) kn_store(lds1);
       stage_barrier();
@@ -593,7 +647,36 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       rsc[i] = (p.ep.row_scale && m < rows_valid) ? p.ep.row_scale[row0 + m] : 1.0f;
     }
 
-    if (EPI == EPI_GLU || EPI == EPI_GLU_MX) {
+    if constexpr (WG) {
+      // fp32 C_e rows mt*256 + m (rows past wg_P are outside the descriptor
+      // and dropped), 4 consecutive columns per lane and 16-byte stores;
+      // accumulate adds the current contents first.
+      const long long PQ = (long long)p.wg_P * p.N;
+      const rsrc_t rsC = make_rsrc(p.Cf + (long long)e * PQ, PQ * 4);
+      const int lh = (lane >> 5) + z0;
+      if (!(p.accumulate && m_e == 0)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t rowb = (uint32_t)(mt * GM_BM + wm * 128 + 32 * i + lm) * (uint32_t)p.N * 4u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int q0 = n0 + wn * 128 + 32 * j + 8 * rq + 4 * lh;
+              if (q0 < p.N) {
+                const uint32_t off = rowb + (uint32_t)q0 * 4u;
+                float4 v = make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                                       acc[i][j][4 * rq + 3]);
+                if (p.accumulate) {
+                  const float4 o = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsC, off, 0, 0));
+                  v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsC, off, 0, 0);
+              }
+            }
+        }
+      }
+    } else if (EPI == EPI_GLU || EPI == EPI_GLU_MX) {
       // y goes straight from registers to HBM, no LDS and no barrier.  Pair
       // wn of this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3.  For
       // two column groups q = 2p, 2p + 1 a lane holds columns 8q + 4 (lane /

@@ -16,5 +16,7 @@ moe_status_t launch_group_gemm_bwd(int epi, int blay, const GemmArgs& args, int 
                                    hipStream_t stream);
 // MXFP8 x MXFP8 GroupGemm (packed MXFP8 weight, bf16 output)
 moe_status_t launch_group_gemm_mx(const GemmArgs& args, int grid, hipStream_t stream);
+// K-grouped weight gradient (fp32 output)
+moe_status_t launch_group_gemm_wgrad(const GemmArgs& args, int grid, hipStream_t stream);
 
 }  // namespace moe

@@ -264,6 +264,20 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a, const moe_operand_t* b
                                   const moe_groups_t* groups, void* c_bf16,
                                   const moe_mx_out_t* mx, int cu_margin, void* stream);
 
+/* Weight gradients as K-grouped GroupGemms ([BLOG] "Fusionando cuantización
+ * MXFP8…": the transposed copies exist for back prop, i.e. for these
+ * products).  For each expert e with rows [o_e, o_e + m_e):
+ *     c_e = a_e^T . b_e          fp32 accumulate, fp32 output [E][P][Q]
+ * a: bf16 [M_cap][P] grouped rows, b: bf16 [M_cap][Q] grouped rows; the
+ * reduction runs over the group's rows (counts in device memory only).
+ * dW1 = wgrad(xg [M_cap][H], dgu [M_cap][2I]) -> [E][H][2I] (plain W1 order);
+ * dW2 = wgrad(y [M_cap][I], dy2 [M_cap][H]) -> [E][I][H].
+ * accumulate = 0 overwrites c (an empty group writes zeros); 1 adds to it.
+ * Requires P % 64 == 0, Q % 64 == 0; a, b, c 16-byte aligned. */
+moe_status_t moe_group_gemm_wgrad(const void* a, const void* b, int P, int Q,
+                                  const moe_groups_t* groups, float* c, int accumulate,
+                                  int cu_margin, void* stream);
+
 /* Unfused GLU pass (baseline and fallback): y = GLU epilogue of z, where z is
  * the plain-order bf16 [M_cap][2I] FC1 output WITHOUT bias (bias, if any, is
  * added here).  Same arithmetic as the fused epilogue, as its own kernel. */
