@@ -172,6 +172,30 @@ def main():
 
     kern_ms = {"fc1_glu": time_kernel(fc1), "fc2": time_kernel(fc2),
                "dgrad_dglu": time_kernel(dglu), "dx": time_kernel(dxk)}
+    # weight gradients (K-grouped, fp32 out)
+    dW1 = torch.empty((E, H, 2 * I), dtype=torch.float32, device=dev)
+    dW2 = torch.empty((E, I, H), dtype=torch.float32, device=dev)
+
+    def dw1():
+        G.moe_group_gemm_wgrad(x, dgu, H, 2 * I, grp, dW1)
+
+    def dw2():
+        G.moe_group_gemm_wgrad(y, dy2, I, H, grp, dW2)
+
+    kern_ms["dw1"] = time_kernel(dw1)
+    kern_ms["dw2"] = time_kernel(dw2)
+
+    def train_step():
+        step()
+        dw1()
+        dw2()
+
+    ts_ms = _ev_ms(torch, train_step, args.steps)
+    train = {"ms": round(ts_ms, 4),
+             "tflops": round((step_flops + 2.0 * M * H * 2 * I + 2.0 * M * I * H) / ts_ms / 1e9, 1),
+             "what": "the step plus the weight gradients dW1 = Xg^T dgu [E][H][2I] and "
+                     "dW2 = y^T dY2 [E][I][H] (K-grouped, fp32 out)"}
+    del dW1, dW2
 
     # ---- the same step as one hipGraph replay (no host sync inside)
     graph_ms = None
@@ -223,7 +247,7 @@ def main():
 
     extra = None
     if not args.no_extra:
-        extra = {}
+        extra = {"training_step_with_wgrads": train}
         log("secondary: B2 traditional path")
         extra["b2_traditional_fc1"] = bench_b2(G, torch, time_kernel, x, counts, counts_h, w1, E,
                                                M, H, I, ep, y, kern_ms["fc1_glu"])
