@@ -251,6 +251,8 @@ def main():
         log("secondary: B2 traditional path")
         extra["b2_traditional_fc1"] = bench_b2(G, torch, time_kernel, x, counts, counts_h, w1, E,
                                                M, H, I, ep, y, kern_ms["fc1_glu"])
+        log("secondary: CU margin with a concurrent copy")
+        extra["cu_margin_overlap"] = bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre)
         log("secondary: MXFP8 forward")
         extra["mxfp8_dsv3_share"] = bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts,
                                                 counts_h, E, M, H, I, kern_ms)
@@ -374,6 +376,51 @@ def bench_b2(G, torch, time_kernel, x, counts, counts_h, w1, E, M, H, I, ep, y, 
     del w1t, z
     return {"ms": round(ms, 4), "fused_speedup": round(ms / fused_ms, 3),
             "what": "host readback of counts + 32 per-expert GEMM launches on 4 streams + GLU pass"}
+
+
+def bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre, margin=32, copy_mib=2048):
+    """FC1 leaving `margin` CUs free while a bandwidth-bound copy runs on a
+    second stream (both at default priority), against each alone and against
+    the same pair with no margin: the knob the pages use to let communication
+    kernels run beside the GEMMs."""
+    dev = x.device
+    n = copy_mib * (1 << 20) // 2
+    src = torch.empty(n, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def fc1(m):
+        G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, y, pre, cu_margin=m)
+
+    def copy():
+        dst.copy_(src)
+
+    def both(m):
+        side.wait_stream(main)
+        fc1(m)
+        with torch.cuda.stream(side):
+            copy()
+        main.wait_stream(side)
+
+    def wall(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / reps
+
+    res = {"fc1_ms": round(wall(lambda: fc1(0)), 4),
+           f"fc1_margin{margin}_ms": round(wall(lambda: fc1(margin)), 4),
+           "copy_ms": round(wall(copy), 4),
+           "fc1_and_copy_ms": round(wall(lambda: both(0)), 4),
+           f"fc1_margin{margin}_and_copy_ms": round(wall(lambda: both(margin)), 4),
+           "copy_gib": copy_mib / 1024}
+    res["copy_gbs_alone"] = round(2 * copy_mib * (1 << 20) / res["copy_ms"] / 1e6, 1)
+    del src, dst
+    return res
 
 
 def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I, kern_ms):

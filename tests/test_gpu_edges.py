@@ -106,3 +106,15 @@ def test_quant_minimum_and_half_tile(G):
         G.moe_pack_weight(dev_bits(b), 3, N, K, G.B_KN, bp)
         q = _quant_gpu(G, a, counts, bp, G.B_PACKED, N, K, M)
         assert_bf16_close(q["c"], O.group_gemm(a, counts, b), what=f"quant N{N}")
+
+
+@pytest.mark.parametrize("margin", [100, 250])
+def test_cu_margin_leaves_results_unchanged(G, margin):
+    """Fewer persistent workgroups (CUs left to concurrent kernels; with 100
+    the grid is no longer a multiple of the 8 XCDs) compute the same bits."""
+    counts = np.array([300, 0, 77, 512])
+    H, I = 64, 2560        # 20 n-tiles: enough tiles for a grid of 156 (margin 100) or 6
+    d = W.small_grouped(46, counts, H, I)
+    ref = _fc1_gpu(G, d["x"], counts, d["w1"], I, {}, preact=True)
+    got = _fc1_gpu(G, d["x"], counts, d["w1"], I, {}, preact=True, cu_margin=margin)
+    assert np.array_equal(got["y"], ref["y"]) and np.array_equal(got["preact"], ref["preact"])
