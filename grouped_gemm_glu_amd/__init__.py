@@ -63,6 +63,10 @@ _SIGS = {
     "moe_packed_mx_weight_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "moe_packed_mx_scale_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "moe_pack_weight_mx": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
+    "moe_repack_gate_up_mx": ([_P, _I, _I, _I, _P, _P, _P], _I),
+    "moe_group_gemm_glu_fwd_mx": ([ctypes.POINTER(OperandT), ctypes.POINTER(GroupsT),
+                                   ctypes.POINTER(OperandT), _I, _I, ctypes.POINTER(EpilogueT), _P,
+                                   _P, ctypes.POINTER(MxOutT), _I, _P], _I),
     "moe_repack_gate_up": ([_P, _I, _I, _I, _P, _P], _I),
     "moe_unpack_gate_up": ([_P, _I, _I, _I, _P, _P], _I),
     "moe_route_group": ([_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P], _I),
@@ -178,6 +182,20 @@ def moe_pack_weight_mx(src, E, N, K, src_layout, dst_q, dst_s, stream=None):
     _check("moe_pack_weight_mx",
            _lib.moe_pack_weight_mx(_ptr(src), E, N, K, src_layout, _ptr(dst_q), _ptr(dst_s),
                                    _stream(stream)))
+
+
+def moe_repack_gate_up_mx(w1, E, H, I, dst_q, dst_s, stream=None):
+    _check("moe_repack_gate_up_mx",
+           _lib.moe_repack_gate_up_mx(_ptr(w1), E, H, I, _ptr(dst_q), _ptr(dst_s), _stream(stream)))
+
+
+def moe_group_gemm_glu_fwd_mx(xg: OperandT, grp: GroupsT, w1: OperandT, H, I, ep: EpilogueT, y=None,
+                              preact=None, mx: Optional[MxOutT] = None, cu_margin: int = 0,
+                              stream=None):
+    _check("moe_group_gemm_glu_fwd_mx",
+           _lib.moe_group_gemm_glu_fwd_mx(ctypes.byref(xg), ctypes.byref(grp), ctypes.byref(w1), H, I,
+                                          ctypes.byref(ep), _ptr(y), _ptr(preact), _ref(mx),
+                                          cu_margin, _stream(stream)))
 
 
 def moe_repack_gate_up(w1, E, H, I, w1_packed, stream=None):

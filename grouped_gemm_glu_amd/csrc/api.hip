@@ -170,7 +170,22 @@ moe_status_t moe_pack_weight_mx(const void* src, int E, int N, int K, int src_la
   dim3 grid(K / 128, (N + 255) / 256, E);
   hipLaunchKernelGGL(pack_mx_kernel, grid, dim3(256), 0, (hipStream_t)stream,
                      static_cast<const uint16_t*>(src), static_cast<uint8_t*>(dst_q),
-                     static_cast<uint8_t*>(dst_s), N, K, src_layout == MOE_B_KN ? 1 : 0);
+                     static_cast<uint8_t*>(dst_s), N, K, src_layout == MOE_B_KN ? 1 : 0, 0);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status_t moe_repack_gate_up_mx(const void* w1, int E, int H, int I, void* dst_q, void* dst_s,
+                                   void* stream) {
+  if (!w1 || !dst_q || !dst_s) return MOE_ERR_NULL;
+  if (E < 1 || H < 128 || H % 128 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(w1) || !aligned16(dst_q) || !aligned16(dst_s)) return MOE_ERR_ALIGN;
+  int cus;
+  moe_status_t st = ensure_init(&cus);
+  if (st != MOE_OK) return st;
+  dim3 grid(H / 128, (2 * I + 255) / 256, E);
+  hipLaunchKernelGGL(pack_mx_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(w1), static_cast<uint8_t*>(dst_q),
+                     static_cast<uint8_t*>(dst_s), 2 * I, H, 1, I);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
@@ -260,6 +275,45 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
   const int epi = (a.row_q || a.col_q) ? EPI_GLU_MX : EPI_GLU;
   return launch_group_gemm_fwd(epi, BL_PACKED, a, grid, (hipStream_t)stream);
+}
+
+moe_status_t moe_group_gemm_glu_fwd_mx(const moe_operand_t* xg, const moe_groups_t* groups,
+                                       const moe_operand_t* w1, int H, int I,
+                                       const moe_epilogue_t* ep, void* y, void* preact,
+                                       const moe_mx_out_t* mx, int cu_margin, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!xg || !w1 || !ep || !xg->data || !xg->scales || !w1->data || !w1->scales) return MOE_ERR_NULL;
+  if ((st = check_mx(mx)) != MOE_OK) return st;
+  if (H < 128 || H % 128 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (ep->gated != 1 || xg->dtype != MOE_DT_MXFP8 || w1->dtype != MOE_DT_MXFP8 ||
+      w1->layout != MOE_B_PACKED)
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(xg->data) || !aligned16(xg->scales) || !aligned16(w1->data) ||
+      !aligned16(w1->scales) || (y && !aligned16(y)) || (preact && !aligned16(preact)))
+    return MOE_ERR_ALIGN;
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = fill_epilogue(ep, &a.ep)) != MOE_OK) return st;
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  fill_groups(&a, groups);
+  a.A = static_cast<const uint16_t*>(xg->data);
+  a.a_scales = xg->scales;
+  a.B = static_cast<const uint16_t*>(w1->data);
+  a.b_scales = w1->scales;
+  a.b_estride = (long long)moe_packed_mx_weight_bytes(1, 2 * I, H);   // bytes = elements
+  a.ldb = H;
+  a.N = 2 * I;
+  a.K = H;
+  a.I = I;
+  a.C = static_cast<uint16_t*>(y);
+  a.preact = static_cast<uint16_t*>(preact);
+  fill_mx(&a, mx, I, groups);
+  a.ntiles_n = (2 * I + GM_BN - 1) / GM_BN;
+  int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
+  return launch_group_gemm_mx_glu(a, (a.row_q || a.col_q) ? EPI_GLU_MX : EPI_GLU, grid,
+                                  (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, int H, int I,

@@ -346,13 +346,17 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict
 // dword at ((nb * K/128 + kb) * 256 + r) * 4 of the scale array (byte b: K
 // values kb * 128 + 32 b .. + 31).  Rows past N are zero with scale byte 0.
 // Grid (K/128, ceil(N/256), E), one thread per row.
+// gate_up_I > 0: the packed rows are W1's gate/up-interleaved columns (row n
+// of the packed order holds plain column plain_col_of_packed(n, I); src is
+// [E][K = H][N = 2I]).
 __global__ __launch_bounds__(256) void pack_mx_kernel(const uint16_t* __restrict__ src,
                                                       uint8_t* __restrict__ q,
                                                       uint8_t* __restrict__ sc, int N, int K,
-                                                      int src_kn) {
+                                                      int src_kn, int gate_up_I) {
   const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
   const int nk = gridDim.x, NB = gridDim.y;
-  const int r = threadIdx.x, n = nb * 256 + r;
+  const int r = threadIdx.x, n_pk = nb * 256 + r;
+  const int n = (gate_up_I > 0 && n_pk < N) ? plain_col_of_packed(n_pk, gate_up_I) : n_pk;
   const uint16_t* W = src + (long long)e * N * K;
   const long long blk = ((long long)e * NB + nb) * nk + kb;
   uint8_t* row = q + blk * 32768 + r * 128;
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
       const long long k = (long long)kb * 128 + b * 32 + t;
-      v[t] = n < N ? bf16_to_f32(src_kn ? W[k * N + n] : W[(long long)n * K + k]) : 0.0f;
+      v[t] = n_pk < N ? bf16_to_f32(src_kn ? W[k * N + n] : W[(long long)n * K + k]) : 0.0f;
     }
     uint32_t w[8];
     sword |= (uint32_t)mx_block_quant(v, 32, w) << (8 * b);

@@ -255,7 +255,9 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   constexpr bool MXT = AT == AT_MX;
   constexpr int ESZ = MXT ? 1 : 2;            // operand element bytes
   constexpr int KSTEPS = MXT ? 2 : 4;         // k-steps per K-tile
-  static_assert(!MXT || (BLAY == BL_PACKED && EPI == EPI_STORE), "MXFP8: packed B, plain store");
+  static_assert(!MXT || (BLAY == BL_PACKED && (EPI == EPI_STORE || EPI == EPI_GLU ||
+                                                EPI == EPI_GLU_MX)),
+                "MXFP8 inputs: packed B; plain store or GLU epilogue");
   static_assert(2 * GM_TILE_BYTES + 2048 <= GM_STAGE_ALLOC, "scale slots");
   // Weight gradients reduce over a group's rows: both operands are stored
   // [rows][columns] with the reduction dimension as the row index, so both

@@ -178,6 +178,15 @@ size_t moe_packed_mx_scale_bytes(int E, int N, int K);
 moe_status_t moe_pack_weight_mx(const void* src, int E, int N, int K, int src_layout,
                                 void* dst_q, void* dst_s, void* stream);
 
+/* The gate/up-repacked W1 as MXFP8 (the FC1 weight of the MXFP8 recipe):
+ * W1 [E][H][2I] bf16 (plain: gate | up) quantised along H (the reduction
+ * dimension) and stored in the MXFP8 layout above with N = 2I in the packed
+ * gate/up order of moe_repack_gate_up and K = H.  Sizes:
+ * moe_packed_mx_weight_bytes(E, 2I, H), moe_packed_mx_scale_bytes(E, 2I, H).
+ * Requires H % 128 == 0, I % 64 == 0. */
+moe_status_t moe_repack_gate_up_mx(const void* w1, int E, int H, int I, void* dst_q, void* dst_s,
+                                   void* stream);
+
 /* Bytes of the packed W1 for E experts, hidden H, intermediate I:
  * moe_packed_weight_bytes(E, 2I, H). */
 size_t moe_packed_w1_bytes(int E, int H, int I);
@@ -227,6 +236,18 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
                                     const void* w1_packed, int H, int I,
                                     const moe_epilogue_t* ep, void* y, void* preact,
                                     const moe_mx_out_t* mx, int cu_margin, void* stream);
+
+/* moe_group_gemm_glu_fwd with MXFP8 inputs ([BLOG] "Fusionando cuantización
+ * MXFP8…": the MXFP8 training recipe's FC1): xg = e4m3 [M_cap][H] with E8M0
+ * row-block scales [M_cap][H/32] (e.g. moe_mxfp8_quantize of the bf16 rows),
+ * w1 = MOE_B_PACKED from moe_repack_gate_up_mx.  z is accumulated in fp32 by
+ * the block-scaled MFMA from the dequantised operands; the epilogue and the
+ * outputs are those of moe_group_gemm_glu_fwd.  Requires H % 128 == 0,
+ * I % 64 == 0. */
+moe_status_t moe_group_gemm_glu_fwd_mx(const moe_operand_t* xg, const moe_groups_t* groups,
+                                       const moe_operand_t* w1, int H, int I,
+                                       const moe_epilogue_t* ep, void* y, void* preact,
+                                       const moe_mx_out_t* mx, int cu_margin, void* stream);
 
 /* GroupGemm + dActivation (+ Quantize/Transpose), the fused backward of FC1's
  * activation ([BLOG] "Optimizando GLU…": in back prop the epilogue reads the

@@ -345,6 +345,34 @@ def dx(dgu_bits, counts, w1_bits, dtype=np.float64):
     return out
 
 
+def fc1_glu_mx(aq, as_, counts, w1q_t, w1s_t, ep: "Epilogue"):
+    """FC1 + GLU with MXFP8 inputs ([BLOG] "Fusionando cuantización MXFP8…"):
+    the exact dequantise-then-multiply pre-activation z_e = deq(A_e) deq(W_e)
+    (+ bias), then the same epilogue as ``fc1_glu``.  aq [M][H] e4m3 codes
+    with as_ [M][H/32] row scales; w1q_t [E][2I][H] the codes of W1_e^T in
+    PLAIN (gate | up) order with w1s_t [E][2I][H/32].  Returns (preact, y)
+    bf16 bits, as ``fc1_glu``."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    M = int(off[-1])
+    E, N2, H = w1q_t.shape
+    I = N2 // 2
+    preact = np.zeros((M, 2 * I), dtype=np.uint16)
+    y = np.zeros((M, I), dtype=np.uint16)
+    rs_all = None if ep.row_scale is None else np.asarray(ep.row_scale, dtype=np.float64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        z = mx_dequantize_rows(aq[a:b], as_[a:b]) @ mx_dequantize_rows(w1q_t[e], w1s_t[e]).T
+        if ep.bias is not None:
+            z = z + bf16_bits_to_f64(np.asarray(ep.bias)[e])[None, :]
+        preact[a:b] = f64_to_bf16_bits(z)
+        rs = None if rs_all is None else rs_all[a:b]
+        y[a:b] = f64_to_bf16_bits(glu_from_preact(z, ep, rs))
+    return preact, y
+
+
 def wgrad(a_bits, counts, b_bits, dtype=np.float64):
     """Weight gradient as a K-grouped GroupGemm: for each expert e with rows
     [o_e, o_e + m_e), C_e = A_e^T @ B_e, the reduction running over the

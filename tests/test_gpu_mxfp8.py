@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import formats as F
 from oracle import moe as O
 from tests.gpu_util import (BF16_NAN_SENTINEL, assert_bf16_close, dev_bits, dev_bytes, dev_i32,
                             empty_bits, empty_bytes, host_bits, packed_mx_layout)
@@ -166,3 +167,107 @@ def test_fc1_mx_rows_feed_fc2_mx(G):
     ref = O.group_gemm_mx(yq, ys, d["counts"], bq, bs)
     assert_bf16_close(host_bits(out2)[:M], ref, what="fc1 mx -> fc2 mx", normwise=2e-2,
                       extra=_abs_bound(yq, ys, d["counts"], bq, bs))
+
+
+# ---------------------------------------------------------------- MXFP8 FC1 (inputs)
+def _oracle_w1_mx(w1):
+    """MXFP8 codes/scales of W1_e^T [2I][H] in plain order, and in the packed
+    gate/up row order (the layout moe_repack_gate_up_mx writes)."""
+    E, H, N2 = w1.shape
+    w1t = np.ascontiguousarray(np.transpose(w1, (0, 2, 1)))
+    q, s = _oracle_weight_mx(w1t)
+    perm = O.packed_column_of(np.arange(N2), N2 // 2)      # plain column -> packed row
+    qp, sp = np.zeros_like(q), np.zeros_like(s)
+    qp[:, perm], sp[:, perm] = q, s
+    return q, s, qp, sp
+
+
+@pytest.mark.parametrize("E,H,I", [(2, 128, 64), (3, 256, 192), (1, 384, 320)])
+def test_repack_gate_up_mx_bit_exact(G, E, H, I):
+    w1 = W.to_bf16_bits((np.random.default_rng(H + I).standard_normal((E, H, 2 * I)) * 0.05)
+                        .astype(np.float32))
+    d_q = empty_bytes((G.moe_packed_mx_weight_bytes(E, 2 * I, H),))
+    d_s = empty_bytes((G.moe_packed_mx_scale_bytes(E, 2 * I, H),))
+    G.moe_repack_gate_up_mx(dev_bits(w1), E, H, I, d_q, d_s)
+    _sync()
+    _, _, qp, sp = _oracle_w1_mx(w1)
+    q_ref, s_ref = packed_mx_layout(qp, sp)
+    assert np.array_equal(d_q.cpu().numpy(), q_ref)
+    assert np.array_equal(d_s.cpu().numpy(), s_ref)
+
+
+def _fc1_mx_gpu(G, aq, as_, counts, w1, H, I, m_cap, ep, mx=False):
+    E = w1.shape[0]
+    d_q = empty_bytes((G.moe_packed_mx_weight_bytes(E, 2 * I, H),))
+    d_s = empty_bytes((G.moe_packed_mx_scale_bytes(E, 2 * I, H),))
+    G.moe_repack_gate_up_mx(dev_bits(w1), E, H, I, d_q, d_s)
+    y, pre = empty_bits((m_cap, I)), empty_bits((m_cap, 2 * I))
+    bufs = None
+    if mx:
+        bufs = dict(row_q=empty_bytes((m_cap, I)), row_s=empty_bytes((m_cap, I // 32)))
+    G.moe_group_gemm_glu_fwd_mx(G.operand(dev_bytes(aq), dtype=G.DT_MXFP8, scales=dev_bytes(as_)),
+                                G.groups(dev_i32(counts), m_cap),
+                                G.operand(d_q, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=d_s),
+                                H, I, ep, y, pre, None if bufs is None else G.mx_out(**bufs))
+    _sync()
+    out = dict(y=host_bits(y), pre=host_bits(pre))
+    if bufs:
+        out.update({k: v.cpu().numpy() for k, v in bufs.items()})
+    return out
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_fc1_glu_fwd_mx(G, bias):
+    counts = np.array([300, 0, 57, 260])
+    E, H, I = 4, 256, 320                 # I = 320: a half n-tile
+    M = int(counts.sum())
+    m_cap = M + 9
+    d = W.small_grouped(34, counts, H, I, bias=bias, m_cap=m_cap)
+    x = W.student_t_rows_bf16(34, m_cap, H)
+    aq, as_ = O.mx_quantize_rows(x)
+    kw = dict(alpha=1.702, gate_lo=-7.0, gate_hi=7.0, up_lo=-7.0, up_hi=7.0) if bias else {}
+    ep = G.epilogue(bias=dev_bits(d["b1"]) if bias else None, **kw)
+    out = _fc1_mx_gpu(G, aq, as_, counts, d["w1"], H, I, m_cap, ep)
+    q, s, _, _ = _oracle_w1_mx(d["w1"])
+    ep_o = O.Epilogue(bias=d["b1"] if bias else None, **kw)
+    rp, ry = O.fc1_glu_mx(aq[:M], as_[:M], counts, q, s, ep_o)
+    zb = _abs_bound(aq[:M], as_[:M], counts, q, s)          # accumulation bound on z
+    assert_bf16_close(out["pre"][:M], rp, what="fc1 mx preact", extra=zb)
+    # y = a(g) u: an error dz of z moves y by at most |a'(g)| |u| dz_g + |a(g)| dz_u,
+    # with |a'| <= 1.1 and |a(g)| <= |g| for SwiGLU (alpha >= 1)
+    zr = np.abs(F.bf16_bits_to_f64(rp))
+    ey = 1.2 * zr[:, I:] * zb[:, :I] + (zr[:, :I] + 1.0) * zb[:, I:]
+    assert_bf16_close(out["y"][:M], ry, what="fc1 mx y", normwise=2e-2, extra=ey)
+    assert np.all(out["y"][M:] == BF16_NAN_SENTINEL) and np.all(out["pre"][M:] == BF16_NAN_SENTINEL)
+
+
+def test_mxfp8_forward_chain(G):
+    """The MXFP8 forward: rows quantised on the GPU, FC1 + SwiGLU on the
+    block-scaled MFMA writing the MXFP8 rows of y, FC2 on the block-scaled
+    MFMA; the oracle runs the same chain from the same bf16 inputs."""
+    counts = np.array([200, 0, 57, 300])
+    E, H, I = 4, 256, 256
+    M = int(counts.sum())
+    d = W.small_grouped(35, counts, H, I, m_cap=M)
+    x = W.student_t_rows_bf16(35, M, H)
+    xq, xs = empty_bytes((M, H)), empty_bytes((M, H // 32))
+    G.moe_mxfp8_quantize(dev_bits(x), M, H, None, G.mx_out(row_q=xq, row_s=xs))
+    _sync()
+    aq, as_ = O.mx_quantize_rows(x)
+    assert np.array_equal(xq.cpu().numpy(), aq) and np.array_equal(xs.cpu().numpy(), as_)
+    out = _fc1_mx_gpu(G, aq, as_, counts, d["w1"], H, I, M, G.epilogue(), mx=True)
+    w2_nk = np.ascontiguousarray(np.transpose(d["w2"], (0, 2, 1)))
+    d_q, d_s = _pack_mx_gpu(G, w2_nk, "NK")
+    out2 = empty_bits((M, H))
+    G.moe_group_gemm_quant(G.operand(dev_bytes(out["row_q"]), dtype=G.DT_MXFP8,
+                                     scales=dev_bytes(out["row_s"])),
+                           G.operand(d_q, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=d_s),
+                           H, I, G.groups(dev_i32(counts), M), out2)
+    _sync()
+    q1, s1, _, _ = _oracle_w1_mx(d["w1"])
+    _, ry = O.fc1_glu_mx(aq, as_, counts, q1, s1, O.Epilogue())
+    yq, ys = O.mx_quantize_rows(ry)
+    bq, bs = _oracle_weight_mx(w2_nk)
+    ref = O.group_gemm_mx(yq, ys, counts, bq, bs)
+    assert_bf16_close(host_bits(out2), ref, what="mx forward chain", normwise=3e-2,
+                      extra=_abs_bound(yq, ys, counts, bq, bs))

@@ -492,3 +492,37 @@ def test_wgrads_against_finite_differences(act, ep_kw):
                 assert abs(fd - grad[e][idx]) <= tol[e][idx] + 1e-6 * abs(fd), (wname, e, idx, fd, grad[e][idx])
                 checked += 1
     assert checked >= 12
+
+
+def _mx_exact_values(rng, shape):
+    """bf16 bits of values that MXFP8 quantisation reproduces exactly: each
+    32-block is e4m3 values times 2^E with its first value at 448 * 2^E (so
+    the block's scale rule gives E back)."""
+    R, C = shape
+    codes = rng.integers(0, 0x7F, size=(R, C)).astype(np.uint8)      # finite e4m3 codes
+    codes[:, ::32] = 0x7E                                            # 448
+    sign = rng.integers(0, 2, size=(R, C)).astype(np.uint8) << 7
+    E = rng.integers(-12, 3, size=(R, C // 32))
+    v = F.e4m3_decode(codes | sign) * np.repeat(2.0 ** E, 32, axis=1)
+    return F.f64_to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_fc1_glu_mx_equals_fc1_glu_on_exactly_quantised_inputs(bias):
+    rng = np.random.default_rng(61)
+    counts = np.array([5, 0, 3])
+    E, H, I = 3, 64, 32
+    x = _mx_exact_values(rng, (8, H))
+    w1t = np.stack([_mx_exact_values(rng, (2 * I, H)) for _ in range(E)])   # W1_e^T [2I][H]
+    w1 = np.ascontiguousarray(np.transpose(w1t, (0, 2, 1)))
+    b1 = W.to_bf16_bits((rng.standard_normal((E, 2 * I)) * 0.1).astype(np.float32)) if bias else None
+    ep = O.Epilogue(alpha=1.702, gate_lo=-7, gate_hi=7, up_lo=-7, up_hi=7, bias=b1)
+    aq, as_ = O.mx_quantize_rows(x)
+    assert np.array_equal(F.f64_to_bf16_bits(O.mx_dequantize_rows(aq, as_)), x)   # exact round trip
+    wq = np.zeros((E, 2 * I, H), np.uint8)
+    ws = np.zeros((E, 2 * I, H // 32), np.uint8)
+    for e in range(E):
+        wq[e], ws[e] = O.mx_quantize_rows(w1t[e])
+    pre_mx, y_mx = O.fc1_glu_mx(aq, as_, counts, wq, ws, ep)
+    pre, y = O.fc1_glu(x, counts, w1, ep)
+    assert np.array_equal(pre_mx, pre) and np.array_equal(y_mx, y)
