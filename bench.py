@@ -468,6 +468,22 @@ def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I
 
     pm = paired_ms(torch, {"fused": fc1_mx, "b1": b1})
     fc1_ms, b1_ms = pm["fused"], pm["b1"]
+    # the MXFP8 recipe's FC1 itself on the block-scaled MFMA: rows of x
+    # quantised on the GPU, gate/up-repacked MXFP8 W1
+    xq = torch.empty((M, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
+    G.moe_mxfp8_quantize(x, M, H, None, G.mx_out(row_q=xq, row_s=xs))
+    w1q = torch.empty(G.moe_packed_mx_weight_bytes(E, 2 * I, H), dtype=torch.uint8, device=dev)
+    w1s = torch.empty(G.moe_packed_mx_scale_bytes(E, 2 * I, H), dtype=torch.uint8, device=dev)
+    G.moe_repack_gate_up_mx(w1, E, H, I, w1q, w1s)
+    op_xq = G.operand(xq, dtype=G.DT_MXFP8, scales=xs)
+    op_w1q = G.operand(w1q, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=w1s)
+
+    def fc1_mxin():
+        G.moe_group_gemm_glu_fwd_mx(op_xq, grp, op_w1q, H, I, ep, None, pre, mx)
+
+    fc1_mxin_ms = time_kernel(fc1_mxin)
+    del xq, xs, w1q, w1s
     fc2_flops = 2.0 * M * I * H
     fc1_flops = 2.0 * M * H * 2 * I
     del x, w1t, z, w2q, w2s
@@ -477,6 +493,9 @@ def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I
             "fc2_mxfp8_ms": round(fc2_ms, 4), "fc2_tflops": round(fc2_flops / fc2_ms / 1e9, 1),
             "fc2_frac_fp8_peak": round(fc2_flops / fc2_ms / 1e9 / 5000.0, 4),
             "fc2_bf16_ms": round(kern_ms["fc2"], 4),
+            "fc1_mxfp8_inputs_ms": round(fc1_mxin_ms, 4),
+            "fc1_mxfp8_inputs_tflops": round(fc1_flops / fc1_mxin_ms / 1e9, 1),
+            "fc1_mxfp8_inputs_frac_fp8_peak": round(fc1_flops / fc1_mxin_ms / 1e9 / 5000.0, 4),
             "activations": "student-t(3) x 0.5, bf16"}
 
 
