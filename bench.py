@@ -253,6 +253,8 @@ def main():
                                                M, H, I, ep, y, kern_ms["fc1_glu"])
         log("secondary: CU margin with a concurrent copy")
         extra["cu_margin_overlap"] = bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre)
+        log("secondary: NVFP4-style amax outputs")
+        extra["amax_outputs"] = bench_amax(G, torch, x, grp, w1p, H, I, y, pre, dy2, op_w2d, dgu)
         log("secondary: MXFP8 forward")
         extra["mxfp8_dsv3_share"] = bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts,
                                                 counts_h, E, M, H, I, kern_ms)
@@ -421,6 +423,28 @@ def bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre, margin=32, copy_mib=2
     res["copy_gbs_alone"] = round(2 * copy_mib * (1 << 20) / res["copy_ms"] / 1e6, 1)
     del src, dst
     return res
+
+
+def bench_amax(G, torch, x, grp, w1p, H, I, y, pre, dy2, op_w2d, dgu):
+    """FC1 with the per-tensor amax of y, and dgrad + dSwiGLU with the amax of
+    the 16-row Hadamard rotation of dgu^T, each beside the same kernel without
+    it (interleaved timing)."""
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ep0 = G.epilogue("swiglu")
+    ep1 = G.epilogue("swiglu", amax_out=amax, rht_signs=0x5A3C)
+
+    def fc1(ep):
+        return lambda: G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, y, pre)
+
+    def dglu(ep):
+        return lambda: G.moe_group_gemm_dglu_bwd(dy2, op_w2d, H, I, grp, pre, ep, dgu)
+
+    pm = paired_ms(torch, {"fc1": fc1(ep0), "fc1_amax": fc1(ep1),
+                           "dglu": dglu(ep0), "dglu_rht_amax": dglu(ep1)})
+    return {k: round(v, 4) for k, v in pm.items()} | {
+        "what": "FC1 + SwiGLU with max|y| and dgrad + dSwiGLU with the amax of H16 S / 4 "
+                "over 16-row runs of dgu^T, against the same kernels without them",
+        "timing": "interleaved, best of 3 rounds of 10"}
 
 
 def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I, kern_ms):

@@ -62,6 +62,9 @@ moe_status_t fill_epilogue(const moe_epilogue_t* ep, EpiParams* out) {
   out->up_offset = ep->up_offset;
   out->bias = static_cast<const uint16_t*>(ep->bias);
   out->row_scale = ep->row_scale;
+  if (ep->amax_out && !aligned4(ep->amax_out)) return MOE_ERR_ALIGN;
+  out->amax_out = ep->amax_out;
+  out->rht_signs = ep->rht_signs & 0xFFFFu;
   return MOE_OK;
 }
 

@@ -186,6 +186,8 @@ struct EpiParams {
   float gate_lo, gate_hi, up_lo, up_hi, up_offset;
   const uint16_t* bias;      // plain [E][2I] or null
   const float* row_scale;    // [M_cap] or null
+  float* amax_out;           // raised atomically to an amax, or null
+  uint32_t rht_signs;        // row signs of the 16-point rotation (bit i: row i)
 };
 
 // ---------------------------------------------------------------- group scan

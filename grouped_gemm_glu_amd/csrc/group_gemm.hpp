@@ -230,6 +230,76 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
   }
 }
 
+// Wave maximum of a non-negative float (no NaN), raised into *dst with one
+// atomic per wave: for such values the float order is the order of their
+// bits as unsigned integers.  Swizzle in bitmask mode pairs lane ^ xm within
+// each half of the wave.
+__device__ __forceinline__ void wave_amax_atomic(float v, float* dst, int lane) {
+  uint32_t b = __float_as_uint(v);
+  b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (1 << 10) | 0x1F));
+  b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (2 << 10) | 0x1F));
+  b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (4 << 10) | 0x1F));
+  b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (8 << 10) | 0x1F));
+  b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (16 << 10) | 0x1F));
+  b = max((uint32_t)__builtin_amdgcn_readlane((int)b, 0), (uint32_t)__builtin_amdgcn_readlane((int)b, 32));
+  if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(dst), b);
+}
+
+// In-place Walsh-Hadamard butterflies of 16 values (Sylvester order, not
+// normalised).
+__device__ __forceinline__ void fwht16(float (&v)[16]) {
+#pragma unroll
+  for (int len = 1; len < 16; len <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & len) == 0) {
+        const float a = v[i], b = v[i + len];
+        v[i] = a + b;
+        v[i + len] = a - b;
+      }
+}
+
+// Largest |.| of the orthonormal 16-point Hadamard rotation of the transposed
+// staged tile: every column (of the 64-column chunks whose bit is set in
+// chunk_ok) is cut into runs of 16 consecutive rows starting at the tile's
+// first row (tiles start at group row multiples of 256, so the runs restart
+// at each group's first row); rows from rows_valid on count as zero, and row
+// i of every run is negated first when bit i of signs is set.  One item is
+// 4 columns x 16 rows, read as 16 conflict-free 8-byte rows.
+__device__ __forceinline__ float rht16_amax_stage(const Stg& stg, int rows_valid, uint32_t chunk_ok,
+                                                  uint32_t signs) {
+  const int t = threadIdx.x + opaque_zero();
+  float amax = 0.0f;
+  for (int it = t; it < (GM_BM / 16) * 64; it += GM_NT) {
+    const int ch = it & 63, r0 = (it >> 6) * 16;
+    if (r0 >= rows_valid || !((chunk_ok >> (ch >> 4)) & 1u)) continue;
+    uint2 w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      w[i] = r0 + i < rows_valid ? *reinterpret_cast<const uint2*>(stg.row(r0 + i) + ch * 4)
+                                 : make_uint2(0u, 0u);
+      const uint32_t neg = ((signs >> i) & 1u) * 0x80008000u;
+      w[i].x ^= neg;
+      w[i].y ^= neg;
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      float lo[16], hi[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t x = d ? w[i].y : w[i].x;
+        lo[i] = __uint_as_float(x << 16);
+        hi[i] = __uint_as_float(x & 0xFFFF0000u);
+      }
+      fwht16(lo);
+      fwht16(hi);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(lo[i]), fabsf(hi[i])));
+    }
+  }
+  return 0.25f * amax;   // the 1/4 of the orthonormal H16 (exact)
+}
+
 // Coalesced store of a staged bf16 tile (ncols % 8 == 0 assumed per 8-chunk validity).
 __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
                                             int ncols_valid, int ncols_tile, uint16_t* dst,
@@ -735,6 +805,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       };
       const rsrc_t rsY = make_rsrc(p.C ? p.C + (long long)row0 * p.I : p.A,
                                    p.C ? (long long)rows_valid * p.I * 2 : 0);
+      float ymax = 0.0f;                   // max |y| of this lane's valid rows
       auto body = [&](auto actc) {
         constexpr int ACT = decltype(actc)::value;
 #pragma unroll
@@ -760,6 +831,12 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
                 }
                 yw[h][0] = pack_bf16x2(o[0], o[1]);
                 yw[h][1] = pack_bf16x2(o[2], o[3]);
+                if (p.ep.amax_out && m < rows_valid) {
+#pragma unroll
+                  for (int w2 = 0; w2 < 2; ++w2)
+                    ymax = fmaxf(ymax, fmaxf(fabsf(__uint_as_float(yw[h][w2] << 16)),
+                                             fabsf(__uint_as_float(yw[h][w2] & 0xFFFF0000u))));
+                }
                 if (MXO) {   // y staged for the MXFP8 round (128 columns)
                   const int c = wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
                   *reinterpret_cast<uint2*>(wstg + (m & 127) * GM_STG_LD_128 + c) =
@@ -823,6 +900,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           case ACT_GEGLU_TANH: body(std::integral_constant<int, ACT_GEGLU_TANH>{}); break;
           default: body(std::integral_constant<int, ACT_SRELU>{}); break;
         }
+        if (p.ep.amax_out) wave_amax_atomic(ymax, p.ep.amax_out, lane);   // NaN dropped by fmaxf
       }
       if (MXO) {
         __syncthreads();
@@ -952,6 +1030,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           default: blocks(std::integral_constant<int, ACT_SRELU>{}, rc); break;
         }
       };
+      float hmax = 0.0f;   // rotated amax of this thread's share of the tile
 #pragma unroll
       for (int round = 0; round < 2; ++round) {
         if (round == 0) stage_round(std::integral_constant<int, 0>{});
@@ -960,6 +1039,10 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         // staged chunk k (64 columns): dg (k < 2) or du, of wave half wn = k & 1;
         // its first global column of I is n0 + 128 (k & 1) + 64 round
         auto chunk_col = [&](int k) { return n0 + 128 * (k & 1) + 64 * round; };
+        if (p.ep.amax_out) {
+          const uint32_t ok = (chunk_col(0) < p.I ? 5u : 0u) | (chunk_col(1) < p.I ? 10u : 0u);
+          hmax = fmaxf(hmax, rht16_amax_stage(stg, rows_valid, ok, p.ep.rht_signs));
+        }
         if (p.C) {
           const int t = tid + z0;
 #pragma unroll 4
@@ -983,6 +1066,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         }
         __syncthreads();
       }
+      if (p.ep.amax_out) wave_amax_atomic(hmax, p.ep.amax_out, lane);
     }
   }
 }

@@ -75,6 +75,19 @@ typedef struct {
   float up_offset;          /* added to the clamped up value; 0 = off */
   const void* bias;         /* nullable: bf16 [E][2I] in PLAIN order (gate | up) */
   const float* row_scale;   /* nullable: fp32 [M_cap], multiplies y per row */
+  /* Per-tensor amax for an NVFP4-style recipe ([BLOG] "Fusionando cuantización MXFP8 y
+     NVFP4": the forward emits its output's amax, the backward the amax of the Hadamard
+     rotation of its transposed output).  Nullable device float, 4-byte aligned, raised
+     (atomic max) by the call, so the caller sets it to 0 (or a running max) first:
+       moe_group_gemm_glu_fwd(_mx): max |y| over the routed rows, bf16 values as written;
+       moe_group_gemm_dglu_bwd:     max |R d| over every column d of dgu = [dg | du] (bf16
+         values as written) cut into runs of 16 consecutive rows that restart at each group's
+         first row, the last run of a group padded with zero rows, and R = H16 S / 4: H16 the
+         Sylvester Hadamard matrix of order 16 and S = diag(s_i), s_i = -1 where bit i of
+         rht_signs is set (row i of the run), else +1.
+     NaN values are skipped.  Other entry points ignore both fields. */
+  float* amax_out;
+  uint32_t rht_signs;       /* low 16 bits: the row signs of the backward rotation */
 } moe_epilogue_t;
 
 /* MXFP8 outputs ([BLOG] "Fusionando cuantización MXFP8 y NVFP4": the

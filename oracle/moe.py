@@ -373,6 +373,55 @@ def fc1_glu_mx(aq, as_, counts, w1q_t, w1s_t, ep: "Epilogue"):
     return preact, y
 
 
+def tensor_amax(y_bits, counts) -> float:
+    """Per-tensor amax of the FC1 output ([BLOG] "Fusionando cuantización
+    MXFP8 y NVFP4": for NVFP4 the forward kernel emits the bf16 output and
+    its per-tensor amax): max |y| over the routed rows [0, sum m_e) of the
+    bf16 values as stored.  NaN entries are skipped (reading: an amax feeds a
+    scale, and the GPU's maximum ignores NaN); no routed rows gives 0."""
+    M = int(np.sum(np.asarray(counts, dtype=np.int64)))
+    v = np.abs(bf16_bits_to_f64(np.asarray(y_bits)[:M]))
+    v = v[~np.isnan(v)]
+    return float(v.max()) if v.size else 0.0
+
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """The Sylvester Hadamard matrix of order n (a power of two): H_1 = [1],
+    H_2k = [[H_k, H_k], [H_k, -H_k]]."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def rht16_amax(dgu_bits, counts, signs: int = 0) -> float:
+    """Amax of the Hadamard rotation of the transposed backward output ([BLOG]
+    "Fusionando cuantización MXFP8 y NVFP4": in back prop the kernel computes
+    the amax of the Hadamard-rotated transpose of its output).  Readings: the
+    rotation acts along the token dimension (the one the weight-gradient GEMM
+    reduces over), in runs of 16 rows that restart at each group's first row
+    (a run never mixes experts), a group's last run padded with zero rows; it
+    is the orthonormal R = H16 S / 4 with S = diag(s_i), s_i = -1 where bit i
+    of ``signs`` is set.  Returns max |R X| over all runs X (16 x 2I) of the
+    bf16 values; NaN skipped; 0 without routed rows."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    s = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
+    R = sylvester_hadamard(16) * s[None, :] / 4.0
+    v = bf16_bits_to_f64(np.asarray(dgu_bits))
+    amax = 0.0
+    for e in range(len(counts)):
+        for r0 in range(int(off[e]), int(off[e + 1]), 16):
+            r1 = min(r0 + 16, int(off[e + 1]))
+            X = np.zeros((16, v.shape[1]))
+            X[: r1 - r0] = v[r0:r1]
+            rot = np.abs(R @ X)
+            rot = rot[~np.isnan(rot)]
+            if rot.size:
+                amax = max(amax, float(rot.max()))
+    return amax
+
+
 def wgrad(a_bits, counts, b_bits, dtype=np.float64):
     """Weight gradient as a K-grouped GroupGemm: for each expert e with rows
     [o_e, o_e + m_e), C_e = A_e^T @ B_e, the reduction running over the

@@ -112,7 +112,7 @@ def test_route_group_bit_exact(G, case):
 
 # ---------------------------------------------------------------- FC1 + GLU
 def _fc1_gpu(G, x, counts, w1, I, ep_kw, m_cap=None, preact=True, mx=False, bias=None,
-             row_scale=None, cu_margin=0):
+             row_scale=None, cu_margin=0, amax_init=None):
     import torch
     E, H, _ = w1.shape
     M = int(np.sum(counts))
@@ -128,7 +128,10 @@ def _fc1_gpu(G, x, counts, w1, I, ep_kw, m_cap=None, preact=True, mx=False, bias
     pre = empty_bits((m_cap, 2 * I)) if preact else None
     d_bias = dev_bits(bias) if bias is not None else None
     d_rs = torch.from_numpy(row_scale).cuda() if row_scale is not None else None
-    ep = G.epilogue(bias=d_bias, row_scale=d_rs, **ep_kw)
+    d_amax = None
+    if amax_init is not None:
+        d_amax = torch.full((1,), float(amax_init), dtype=torch.float32, device="cuda")
+    ep = G.epilogue(bias=d_bias, row_scale=d_rs, amax_out=d_amax, **ep_kw)
     grp = G.groups(d_counts, m_cap, d_off, d_status)
     mxo, bufs = None, None
     if mx:
@@ -142,6 +145,8 @@ def _fc1_gpu(G, x, counts, w1, I, ep_kw, m_cap=None, preact=True, mx=False, bias
         out["preact"] = host_bits(pre)
     if mx:
         out.update({k: v.cpu().numpy() for k, v in bufs.items()})
+    if d_amax is not None:
+        out["amax"] = float(d_amax.item())
     return out
 
 

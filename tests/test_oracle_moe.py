@@ -526,3 +526,96 @@ def test_fc1_glu_mx_equals_fc1_glu_on_exactly_quantised_inputs(bias):
     pre_mx, y_mx = O.fc1_glu_mx(aq, as_, counts, wq, ws, ep)
     pre, y = O.fc1_glu(x, counts, w1, ep)
     assert np.array_equal(pre_mx, pre) and np.array_equal(y_mx, y)
+
+
+def test_tensor_amax_planted_values():
+    """Planted extremes: the largest magnitude is negative, a larger one sits in
+    a row past the routed ones, NaN is skipped, and no routed rows gives 0."""
+    y = np.zeros((6, 4), dtype=np.uint16)
+    y[0, 1] = 0x4040                     # 3.0
+    y[3, 2] = 0xC060                     # -3.5
+    y[4, 0] = 0x7FC0                     # NaN (routed)
+    y[5, 3] = 0x4300                     # 128.0 in an unrouted row
+    counts = np.array([2, 0, 3])         # M = 5
+    assert O.tensor_amax(y, counts) == 3.5
+    assert O.tensor_amax(y, np.array([6])) == 128.0
+    assert O.tensor_amax(y, np.array([0, 0])) == 0.0
+    y[1, 0] = 0xFF80                     # -inf
+    assert O.tensor_amax(y, counts) == math.inf
+
+
+def test_tensor_amax_of_fc1_bounds_the_glu_closed_form():
+    """amax of y from fc1_glu against the closed form of one routed row:
+    with W1 one-hot, z = x's entries, so y_j = silu(x_g) x_u in bf16 and the
+    amax is the largest of those products."""
+    H, I = 8, 4
+    x = W.to_bf16_bits(np.array([[1.0, -2.0, 0.5, 3.0, 2.0, -1.0, 0.25, 4.0]], dtype=np.float32))
+    w1 = np.zeros((1, H, 2 * I), dtype=np.float32)
+    for j in range(2 * I):
+        w1[0, j, j] = 1.0                # z_j = x_j
+    _, y = O.fc1_glu(x, np.array([1]), W.to_bf16_bits(w1), O.Epilogue())
+    g, u = np.array([1.0, -2.0, 0.5, 3.0]), np.array([2.0, -1.0, 0.25, 4.0])
+    silu = g / (1.0 + np.exp(-g))
+    want = np.max(np.abs(F.bf16_bits_to_f64(F.f64_to_bf16_bits(silu * u))))
+    assert O.tensor_amax(y, np.array([1])) == want
+    assert abs(want - 3.0 / (1.0 + math.exp(-3.0)) * 4.0) < 0.05
+
+
+def test_sylvester_hadamard_against_library_and_orthogonality():
+    import scipy.linalg
+    for n in (1, 2, 4, 16):
+        assert np.array_equal(O.sylvester_hadamard(n), scipy.linalg.hadamard(n))
+    h = O.sylvester_hadamard(16)
+    assert np.array_equal(h @ h.T, 16 * np.eye(16))
+
+
+def _bf(vals):
+    return W.to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def test_rht16_amax_closed_forms():
+    """Closed forms of the 16-row rotation R = H16 S / 4 on one column."""
+    c = 3.0
+    # a lone entry x: every output is +-x/4
+    col = np.zeros((16, 1)); col[5, 0] = -6.0
+    assert O.rht16_amax(_bf(col), [16]) == 1.5
+    # a constant run: all of it lands in output 0 (4c), whatever the uniform sign
+    col = np.full((16, 1), c)
+    assert O.rht16_amax(_bf(col), [16]) == 4 * c
+    assert O.rht16_amax(_bf(col), [16], signs=0xFFFF) == 4 * c
+    # one flipped row: output 0 is 14c/4, every other output +-2c/4
+    assert O.rht16_amax(_bf(col), [16], signs=0x0001) == 3.5 * c
+    # a partial run of 4 rows is padded with zeros: outputs 0, 4, 8, 12 are c
+    assert O.rht16_amax(_bf(np.full((4, 1), c)), [4]) == c
+    # runs restart at each group's first row: rows 5..20 form one run of
+    # group 1 (not 11 + 5 rows of two runs aligned at row 0)
+    col = np.zeros((21, 1)); col[5:] = c
+    assert O.rht16_amax(_bf(col), [5, 16]) == 4 * c
+    assert O.rht16_amax(_bf(col), [21]) == 11 * c / 4
+    # rows past the routed ones do not count; no routed rows gives 0
+    assert O.rht16_amax(_bf(col), [5, 0]) == 0.0
+
+
+def test_rht16_amax_against_library_hadamard():
+    """Random ragged groups with random signs against an explicit product
+    with scipy's Hadamard matrix, run by run."""
+    import scipy.linalg
+    rng = np.random.default_rng(11)
+    counts = np.array([37, 0, 16, 1, 50])
+    x = _bf(rng.standard_normal((int(counts.sum()) + 3, 24)))
+    signs = int(rng.integers(0, 1 << 16))
+    v = F.bf16_bits_to_f64(x)
+    S = np.diag([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
+    best, r = 0.0, 0
+    for m in counts:
+        for k in range(0, int(m), 16):
+            blk = np.zeros((16, 24))
+            n = min(16, int(m) - k)
+            blk[:n] = v[r + k: r + k + n]
+            best = max(best, float(np.abs(scipy.linalg.hadamard(16) @ S @ blk).max()) / 4)
+        r += int(m)
+    assert O.rht16_amax(x, counts, signs) == best
+    # Parseval on the full runs: the rotation keeps every run's norm
+    blk = v[:16]
+    R = O.sylvester_hadamard(16) @ S / 4
+    assert np.isclose(np.linalg.norm(R @ blk), np.linalg.norm(blk))
