@@ -23,7 +23,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libmoeglu.so")
-SOURCES = ["api.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_mx.hip", "gemm_wgrad.hip"]
+# (source, object name, extra flags): the activation kernels are compiled once
+# per activation (MOE_ACT = the moe_act_t value), which also spreads the
+# largest translation units over more parallel jobs.
+SOURCES = ([("api.hip", "api", []), ("gemm_fwd.hip", "gemm_fwd", []), ("gemm_bwd.hip", "gemm_bwd", []),
+            ("gemm_mx.hip", "gemm_mx", []), ("gemm_wgrad.hip", "gemm_wgrad", [])]
+           + [(f"gemm_act_{d}.hip", f"gemm_act_{d}_{a}", [f"-DMOE_ACT={a}"])
+              for d in ("bwd", "fwd") for a in range(4)])
 ARCH = "gfx950"
 
 
@@ -40,9 +46,10 @@ def common_flags():
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 
-def compile_one(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + common_flags()
+def compile_one(unit, verbose: bool) -> str:
+    src, name, extra = unit
+    obj = os.path.join(OBJDIR, name + ".o")
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + common_flags() + extra
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

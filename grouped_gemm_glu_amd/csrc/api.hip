@@ -98,6 +98,22 @@ int persistent_grid(int cus, int cu_margin, int M_cap, int E, int ntiles_n) {
 
 }  // namespace
 
+namespace moe {
+
+moe_status_t launch_activation_kernel(int kind, const GemmArgs& a, int grid, hipStream_t s) {
+  const bool bwd = kind == KIND_DGLU_PACKED || kind == KIND_DGLU_NK;
+  switch (a.ep.act) {
+    case ACT_SWIGLU: return bwd ? launch_act_bwd_0(kind, a, grid, s) : launch_act_fwd_0(kind, a, grid, s);
+    case ACT_GEGLU: return bwd ? launch_act_bwd_1(kind, a, grid, s) : launch_act_fwd_1(kind, a, grid, s);
+    case ACT_GEGLU_TANH:
+      return bwd ? launch_act_bwd_2(kind, a, grid, s) : launch_act_fwd_2(kind, a, grid, s);
+    case ACT_SRELU: return bwd ? launch_act_bwd_3(kind, a, grid, s) : launch_act_fwd_3(kind, a, grid, s);
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace moe
+
 extern "C" {
 
 moe_status_t moe_init(int device) {
@@ -276,8 +292,8 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
   fill_mx(&a, mx, I, groups);
   a.ntiles_n = (2 * I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  const int epi = (a.row_q || a.col_q) ? EPI_GLU_MX : EPI_GLU;
-  return launch_group_gemm_fwd(epi, BL_PACKED, a, grid, (hipStream_t)stream);
+  return launch_activation_kernel((a.row_q || a.col_q) ? KIND_GLU_MXO : KIND_GLU, a, grid,
+                                  (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_glu_fwd_mx(const moe_operand_t* xg, const moe_groups_t* groups,
@@ -315,8 +331,8 @@ moe_status_t moe_group_gemm_glu_fwd_mx(const moe_operand_t* xg, const moe_groups
   fill_mx(&a, mx, I, groups);
   a.ntiles_n = (2 * I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  return launch_group_gemm_mx_glu(a, (a.row_q || a.col_q) ? EPI_GLU_MX : EPI_GLU, grid,
-                                  (hipStream_t)stream);
+  return launch_activation_kernel((a.row_q || a.col_q) ? KIND_MXIN_GLU_MXO : KIND_MXIN_GLU, a,
+                                  grid, (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, int H, int I,
@@ -352,8 +368,8 @@ moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, i
   fill_mx(&a, mx, 2 * I, groups);
   a.ntiles_n = (I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  return launch_group_gemm_bwd(EPI_DGLU, w2_packed ? BL_PACKED : BL_NK, a, grid,
-                               (hipStream_t)stream);
+  return launch_activation_kernel(w2_packed ? KIND_DGLU_PACKED : KIND_DGLU_NK, a, grid,
+                                  (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t* b_op, int N,

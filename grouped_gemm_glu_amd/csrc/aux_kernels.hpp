@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void glu_unfused_kernel(const uint16_t* __rest
                                                           int M_cap, int I, EpiParams ep,
                                                           uint16_t* __restrict__ y) {
   __shared__ GroupScan gs;
-  build_group_scan<256>(gs, counts, E, M_cap, 1, nullptr, nullptr, false);
+  build_group_scan<256>(gs, counts, E, M_cap, 1, 0, nullptr, nullptr, false);
   const int M = gs.row_off[E];
   const int cpr = I >> 3;
   long long total = (long long)M * cpr;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
   __shared__ GroupScan gs;
   int Ruse = R;
   if (counts) {
-    build_group_scan<256>(gs, counts, E, R, 1, nullptr, nullptr, false);
+    build_group_scan<256>(gs, counts, E, R, 1, 0, nullptr, nullptr, false);
     Ruse = gs.row_off[E];
   }
   const int nb = C >> 5;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict
   __shared__ GroupScan gs;
   int nblocks;
   if (counts) {
-    build_group_scan<256>(gs, counts, E, R, 1, nullptr, nullptr, false);
+    build_group_scan<256>(gs, counts, E, R, 1, 0, nullptr, nullptr, false);
     nblocks = gs.mxs_off[E];
   } else {
     nblocks = (R + 31) >> 5;

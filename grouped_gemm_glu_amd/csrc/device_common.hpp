@@ -197,7 +197,8 @@ struct EpiParams {
 // counts become 0 (status bit 0) and rows past M_cap are dropped (bit 1).
 struct GroupScan {
   int row_off[kMaxExperts + 1];   // o_e of the clamped counts
-  int tile_off[kMaxExperts + 1];  // prefix of m-tiles per expert
+  int tile_off[kMaxExperts + 1];  // prefix of full-height m-tiles per expert
+  int half_off[kMaxExperts + 1];  // prefix of half-height m-tiles (0 or 1 per expert)
   int mxs_off[kMaxExperts + 1];   // prefix of ceil(m_e/32): MX column-scale offsets
   long long wave_tmp[16];
   long long total_raw;
@@ -220,12 +221,16 @@ __device__ __forceinline__ T block_incl_scan(T v, long long* wave_tmp) {
   return v + add;
 }
 
-// Fills gs from counts[0..E) for m-tiles of BM rows.  NT threads, each owning
-// up to kMaxExperts/NT consecutive experts.  The writer workgroup also stores
-// the clamped offsets and the status bits.  gs is valid after the final barrier.
+// Fills gs from counts[0..E) for m-tiles of BM rows.  With half_rows > 0 an
+// expert's last m-tile counts as a half-height tile (half_off) when it holds
+// 1 .. half_rows rows, else as a full one (tile_off); half_rows = 0 makes every
+// m-tile full.  NT threads, each owning up to kMaxExperts/NT consecutive
+// experts.  The writer workgroup also stores the clamped offsets and the
+// status bits.  gs is valid after the final barrier.
 template <int NT>
 __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, int E, int M_cap,
-                                 int BM, int* offsets_out, int* status_out, bool writer) {
+                                 int BM, int half_rows, int* offsets_out, int* status_out,
+                                 bool writer) {
   const int t = threadIdx.x;
   constexpr int PER = (kMaxExperts + NT - 1) / NT;
   int c[PER];
@@ -241,8 +246,10 @@ __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, 
   }
   long long incl = block_incl_scan<NT, long long>(raw_sum, gs.wave_tmp);
   long long run = incl - raw_sum;  // exclusive prefix of the non-negative counts
-  int mt_sum = 0, mx_sum = 0;
+  int mt_sum = 0, hf_sum = 0, mx_sum = 0;
   int mloc[PER];
+  auto n_half = [&](int m) { const int r = m % BM; return (half_rows > 0 && r > 0 && r <= half_rows) ? 1 : 0; };
+  auto n_full = [&](int m) { return (m + BM - 1) / BM - n_half(m); };
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     int e = t * PER + i;
@@ -252,25 +259,30 @@ __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, 
     mloc[i] = m;
     if (e < E) gs.row_off[e] = run < M_cap ? (int)run : M_cap;
     run += c[i];
-    mt_sum += (m + BM - 1) / BM;
+    mt_sum += n_full(m);
+    hf_sum += n_half(m);
     mx_sum += (m + kMxBlock - 1) / kMxBlock;
   }
   if (t == NT - 1) gs.total_raw = run;
   int mt_incl = block_incl_scan<NT, int>(mt_sum, gs.wave_tmp);
+  int hf_incl = block_incl_scan<NT, int>(hf_sum, gs.wave_tmp);
   int mx_incl = block_incl_scan<NT, int>(mx_sum, gs.wave_tmp);
-  int mt_run = mt_incl - mt_sum, mx_run = mx_incl - mx_sum;
+  int mt_run = mt_incl - mt_sum, hf_run = hf_incl - hf_sum, mx_run = mx_incl - mx_sum;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     int e = t * PER + i;
     if (e < E) {
       gs.tile_off[e] = mt_run;
+      gs.half_off[e] = hf_run;
       gs.mxs_off[e] = mx_run;
     }
-    mt_run += (mloc[i] + BM - 1) / BM;
+    mt_run += n_full(mloc[i]);
+    hf_run += n_half(mloc[i]);
     mx_run += (mloc[i] + kMxBlock - 1) / kMxBlock;
   }
   if (t == NT - 1) {
     gs.tile_off[E] = mt_run;
+    gs.half_off[E] = hf_run;
     gs.mxs_off[E] = mx_run;
   }
   int neg_any = __syncthreads_or(bad_neg);
@@ -284,17 +296,6 @@ __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, 
       if (st) atomicOr(status_out, st);
     }
   }
-}
-
-// Index of the expert owning global tile t: the last e with tile_off[e] <= t
-// (experts with zero tiles are skipped because their range is empty).
-__device__ __forceinline__ int find_expert(const int* tile_off, int E, int t) {
-  int lo = 0, hi = E;  // invariant: tile_off[lo] <= t < tile_off[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (tile_off[mid] <= t) lo = mid; else hi = mid;
-  }
-  return lo;
 }
 
 }  // namespace moe

@@ -1,0 +1,31 @@
+// dgrad + dGLU kernels for one activation (MOE_ACT, a moe_act_t value given
+// on the compile line; the build compiles this file once per activation):
+// W2 read as W2^T from the packed copy or from the K-contiguous [I][H].
+#include "internal.hpp"
+
+#ifndef MOE_ACT
+#error "compile once per activation with -DMOE_ACT=<0..3>"
+#endif
+
+#define MOE_CAT_(a, b) a##b
+#define MOE_CAT(a, b) MOE_CAT_(a, b)
+
+namespace moe {
+
+template <int BLAY>
+static void launch_dglu(const GemmArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((group_gemm_kernel<EPI_DGLU, BLAY, AT_BF16, MOE_ACT>), dim3(grid), dim3(GM_NT), 0,
+                     s, a);
+}
+
+moe_status_t MOE_CAT(launch_act_bwd_, MOE_ACT)(int kind, const GemmArgs& a, int grid,
+                                               hipStream_t s) {
+  switch (kind) {
+    case KIND_DGLU_PACKED: launch_dglu<BL_PACKED>(a, grid, s); break;
+    case KIND_DGLU_NK: launch_dglu<BL_NK>(a, grid, s); break;
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+}  // namespace moe

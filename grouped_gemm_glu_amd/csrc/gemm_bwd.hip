@@ -1,7 +1,5 @@
-// Instantiations of the persistent grouped GEMM used by the backward pass and
-// by every packed-weight GEMM: dgrad + dGLU (W2 read as W2^T, packed or as the
-// K-contiguous [I][H]) and the plain GroupGemm on a tile-blocked packed weight
-// (FC2, dX).
+// Instantiation of the persistent grouped GEMM for the plain GroupGemm on a
+// tile-blocked packed weight (FC2, dX).
 #include "internal.hpp"
 
 namespace moe {
@@ -13,8 +11,6 @@ static moe_status_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
 }
 
 moe_status_t launch_group_gemm_bwd(int epi, int blay, const GemmArgs& a, int grid, hipStream_t s) {
-  if (epi == EPI_DGLU && blay == BL_PACKED) return launch_one<EPI_DGLU, BL_PACKED>(a, grid, s);
-  if (epi == EPI_DGLU && blay == BL_NK) return launch_one<EPI_DGLU, BL_NK>(a, grid, s);
   if (epi == EPI_STORE && blay == BL_PACKED) return launch_one<EPI_STORE, BL_PACKED>(a, grid, s);
   return MOE_ERR_UNSUPPORTED;
 }

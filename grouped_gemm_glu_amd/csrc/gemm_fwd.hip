@@ -1,6 +1,6 @@
-// Instantiations of the persistent grouped GEMM used by the forward pass:
-// FC1 + GLU on the tile-blocked packed W1, and the plain GroupGemm on the two
-// unpacked weight orientations (N-contiguous [K][N] and K-contiguous [N][K]).
+// Instantiations of the persistent grouped GEMM for the plain GroupGemm on the
+// two unpacked weight orientations (N-contiguous [K][N] and K-contiguous
+// [N][K]).
 #include "internal.hpp"
 
 namespace moe {
@@ -12,8 +12,6 @@ static moe_status_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
 }
 
 moe_status_t launch_group_gemm_fwd(int epi, int blay, const GemmArgs& a, int grid, hipStream_t s) {
-  if (epi == EPI_GLU && blay == BL_PACKED) return launch_one<EPI_GLU, BL_PACKED>(a, grid, s);
-  if (epi == EPI_GLU_MX && blay == BL_PACKED) return launch_one<EPI_GLU_MX, BL_PACKED>(a, grid, s);
   if (epi == EPI_STORE && blay == BL_KN) return launch_one<EPI_STORE, BL_KN>(a, grid, s);
   if (epi == EPI_STORE && blay == BL_NK) return launch_one<EPI_STORE, BL_NK>(a, grid, s);
   return MOE_ERR_UNSUPPORTED;

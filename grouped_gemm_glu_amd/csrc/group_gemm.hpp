@@ -28,9 +28,22 @@
 // Output tiles are staged in LDS and written with 16-byte coalesced stores.
 #pragma once
 
+#include <utility>
+
 #include "device_common.hpp"
 
 namespace moe {
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): loop
+// bodies whose indices must be compile-time constants.
+template <typename F, int... G>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, G...>) {
+  (f(std::integral_constant<int, G>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int GM_BM = 256;
 constexpr int GM_BN = 256;
@@ -47,14 +60,17 @@ constexpr int GM_HALF_STG_BYTES = (GM_BM / 2) * GM_STG_LD_256 * 2;   // 66 KB
 constexpr int GM_STAGE_ALLOC =
     GM_HALF_STG_BYTES > GM_STAGE_BYTES ? GM_HALF_STG_BYTES : GM_STAGE_BYTES;
 
-// Staged output tile split over the two stage arrays by row halves.
+// Staged output tile split over the two stage arrays by row halves: hr rows
+// each (128 for a 256-row tile, 64 for a 128-row tile).
 struct Stg {
   uint16_t* h0;
   uint16_t* h1;
   int ld;
+  int hr = 128;
   __device__ __forceinline__ uint16_t* row(int r) const {
-    return (r < 128 ? h0 : h1) + (r & 127) * ld;
+    return (r < hr ? h0 : h1) + (r < hr ? r : r - hr) * ld;
   }
+  __device__ __forceinline__ int rows() const { return 2 * hr; }
 };
 
 enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4 };
@@ -188,7 +204,7 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
   const int t = threadIdx.x + opaque_zero();
   if (p.row_q) {
     const int nb = ncols >> 5;
-    for (int it = t; it < GM_BM * nb; it += GM_NT) {
+    for (int it = t; it < stg.rows() * nb; it += GM_NT) {
       int r = it / nb, cb = it - r * nb;
       if (r >= rows_valid) continue;
       float v[32];
@@ -213,7 +229,7 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
   }
   if (p.col_q) {
     const int nrb = (rows_valid + 31) >> 5;
-    for (int it = t; it < ncols * 8; it += GM_NT) {
+    for (int it = t; it < ncols * (stg.rows() >> 5); it += GM_NT) {
       int c = it % ncols, rb = it / ncols;
       if (rb >= nrb) continue;
       int nvalid = rows_valid - rb * 32;
@@ -270,7 +286,7 @@ __device__ __forceinline__ float rht16_amax_stage(const Stg& stg, int rows_valid
                                                   uint32_t signs) {
   const int t = threadIdx.x + opaque_zero();
   float amax = 0.0f;
-  for (int it = t; it < (GM_BM / 16) * 64; it += GM_NT) {
+  for (int it = t; it < (stg.rows() / 16) * 64; it += GM_NT) {
     const int ch = it & 63, r0 = (it >> 6) * 16;
     if (r0 >= rows_valid || !((chunk_ok >> (ch >> 4)) & 1u)) continue;
     uint2 w[16];
@@ -306,7 +322,7 @@ __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
                                             long long dst_ld) {
   const int t = threadIdx.x + opaque_zero();
   const int cpr = ncols_tile >> 3;  // 16-byte chunks per row
-  for (int it = t; it < GM_BM * cpr; it += GM_NT) {
+  for (int it = t; it < stg.rows() * cpr; it += GM_NT) {
     int r = it / cpr, ch = it - r * cpr;
     if (r < rows_valid && ch * 8 < ncols_valid) {
       uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
@@ -316,7 +332,9 @@ __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
 }
 
 // ---------------------------------------------------------------- the kernel
-template <int EPI, int BLAY, int AT = AT_BF16>
+// ACT: the activation of the GLU and dGLU epilogues (one kernel per
+// activation, so the epilogue holds no dispatch); unused by the others.
+template <int EPI, int BLAY, int AT = AT_BF16, int ACT = ACT_SWIGLU>
 __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   // Operand rows are staged as 128-byte K slices whatever the type: 64 bf16
   // (4 k-steps of v_mfma_f32_32x32x16_bf16) or 128 e4m3 (2 k-steps of
@@ -346,8 +364,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
 
-  build_group_scan<GM_NT>(gs, p.counts, p.E, p.M_cap, GM_BM, p.offsets_out, p.status_out,
-                          blockIdx.x == 0);
+  build_group_scan<GM_NT>(gs, p.counts, p.E, p.M_cap, GM_BM, WG ? 0 : GM_BM / 2, p.offsets_out,
+                          p.status_out, blockIdx.x == 0);
   if (WG) {
     // Every expert owns the same number of output tiles but its tiles cost
     // m_e: hand them out largest group first (ties: lower id), the order kept
@@ -363,7 +381,13 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     }
     __syncthreads();
   }
-  const int total_tiles = WG ? p.E * p.ntiles_m * p.ntiles_n : gs.tile_off[p.E] * p.ntiles_n;
+  // grouped GEMM: the half-height tiles (ids [0, n_half)) come first, then
+  // the full ones, so that every workgroup's share is balanced: with F full
+  // and H half tiles on P workgroups, H <= P gives each workgroup at most
+  // ceil((H + F) / P) tiles of which the first may be a half one.
+  const int n_half = WG ? 0 : gs.half_off[p.E] * p.ntiles_n;
+  const int total_tiles =
+      WG ? p.E * p.ntiles_m * p.ntiles_n : n_half + gs.tile_off[p.E] * p.ntiles_n;
 
   // XCD-aware slot: consecutive workgroups land on different XCDs (round
   // robin over 8), so give each XCD a contiguous run of tile ids per round.
@@ -375,12 +399,23 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   const int rl = lane >> 3, pc = lane & 7;
 
   for (int tile = slot; tile < total_tiles; tile += P) {
-    // ---- decode (expert, m-tile, n-tile).  Expert e owns tiles
-    // [tile_off[e] * NT, tile_off[e+1] * NT).  Within an expert, tiles run in
-    // blocks of 4 m-tiles x 8 n-tiles (m fastest), so the run of consecutive
-    // ids an XCD takes per round shares few A panels and few B panels.
+    // ---- decode (expert, m-tile, n-tile).  Half tiles: expert e owns ids
+    // [half_off[e] * NT, half_off[e+1] * NT), one per n-tile of its last
+    // m-tile.  Full tiles: expert e owns ids n_half + [tile_off[e] * NT,
+    // tile_off[e+1] * NT), in blocks of 4 m-tiles x 8 n-tiles (m fastest), so
+    // the run of consecutive ids an XCD takes per round shares few A panels
+    // and few B panels.
     int e, mt, nt;
-    {
+    if (!WG && tile < n_half) {
+      int lo = 0, hi = p.E;  // invariant: half_off[lo]*NT <= tile < half_off[hi]*NT
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (gs.half_off[mid] * NT <= tile) lo = mid; else hi = mid;
+      }
+      e = lo;
+      nt = tile - gs.half_off[e] * NT;
+      mt = gs.tile_off[e + 1] - gs.tile_off[e];   // after the expert's full m-tiles
+    } else {
       int local, MT;
       if (WG) {   // weight gradient: p.ntiles_m x NT output tiles per expert
         const int per = p.ntiles_m * NT;
@@ -389,13 +424,14 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         local = tile - rank * per;
         MT = p.ntiles_m;
       } else {
-        int lo = 0, hi = p.E;  // invariant: tile_off[lo]*NT <= tile < tile_off[hi]*NT
+        const int ft = tile - n_half;
+        int lo = 0, hi = p.E;  // invariant: tile_off[lo]*NT <= ft < tile_off[hi]*NT
         while (hi - lo > 1) {
           int mid = (lo + hi) >> 1;
-          if (gs.tile_off[mid] * NT <= tile) lo = mid; else hi = mid;
+          if (gs.tile_off[mid] * NT <= ft) lo = mid; else hi = mid;
         }
         e = lo;
-        local = tile - gs.tile_off[e] * NT;
+        local = ft - gs.tile_off[e] * NT;
         MT = gs.tile_off[e + 1] - gs.tile_off[e];
       }
       constexpr int BHT = 4, BWT = 8;
@@ -415,6 +451,15 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     const int rows_valid = WG ? min(GM_BM, p.wg_P - mt * GM_BM) : min(GM_BM, m_e - mt * GM_BM);
     const int n0 = nt * GM_BN;
     const int nk_t = WG ? (m_e + 63) / 64 : nk;      // K-tiles of this tile
+
+    // The tile body for MI 32-row MFMA blocks per wave: MI = 4 is the 256-row
+    // tile (waves 128 x 128); a group's last m-tile with at most 128 valid
+    // rows runs with MI = 2 as a 128-row tile (waves 64 x 128), half the MFMA
+    // work of the padded 256-row tile.  Weight-gradient tiles are always full.
+    auto tile_body = [&](auto mic) {
+    constexpr int MI = decltype(mic)::value;
+    constexpr int HR = 32 * MI;                 // rows per wave row
+    constexpr int TBM = 2 * HR;                 // tile rows
 
     // Per-tile opaque zero: main-loop addressing is recomputed for each tile,
     // so it is not live across the epilogue.
@@ -463,26 +508,29 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         WG ? (uint32_t)(kn_g * 8) * a_stride + (uint32_t)min(mt * GM_BM + kn_c * 8, p.wg_P - 8) * 2u
            : 0u;
 
-    f32x16 acc[4][4];
+    f32x16 acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // direct global -> LDS of one 256 x 64 operand tile (swizzled layout).
-    // Instruction j of wave w fills rows 8 (8w + j) .. + 7; lane (rl, pc)
-    // lands on row 8 (8w + j) + rl, physical chunk pc, so it fetches logical
-    // chunk pc ^ key(row), key = rl ^ (j & 3).
+    // direct global -> LDS of one ROWS x 64 operand tile (swizzled layout).
+    // Instruction j of wave w fills rows 8 (NJ w + j) .. + 7 (NJ = ROWS / 32);
+    // lane (rl, pc) lands on row 8 (NJ w + j) + rl, physical chunk pc, so it
+    // fetches logical chunk pc ^ key(row), key = rl ^ (j & 3) (NJ is a
+    // multiple of 4).
     const int rl_t = lane_t >> 3, pc_t = lane_t & 7;
-    auto issue_tile = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t stride, uint32_t koff) {
-      const uint32_t vrow = (uint32_t)(wave * 64 + rl_t) * stride;
+    auto issue_tile = [&](auto rowsc, const rsrc_t& rs, uint8_t* lds_tile, uint32_t stride,
+                          uint32_t koff) {
+      constexpr int NJ = decltype(rowsc)::value / 32;
+      const uint32_t vrow = (uint32_t)(wave * 8 * NJ + rl_t) * stride;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int c = pc_t ^ (rl_t ^ (j & 3));
         const uint32_t voff = vrow + (uint32_t)(j * 8) * stride + (uint32_t)(c << 4);
-        lds_dma16(rs, lds_tile + (wave * 8 + j) * 1024, voff, koff);
+        lds_dma16(rs, lds_tile + (wave * NJ + j) * 1024, voff, koff);
       }
     };
     // K-tiles past the end are fetched through a descriptor with no records:
@@ -499,9 +547,12 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     };
     auto issue_direct = [&](int kt, uint8_t* sa) {
       const bool in = kt < nk_t;
-      if (!WG) issue_tile(in ? rsA : rsZ, sa, a_stride, (uint32_t)kt * 128u);
+      if (!WG)
+        issue_tile(std::integral_constant<int, TBM>{}, in ? rsA : rsZ, sa, a_stride,
+                   (uint32_t)kt * 128u);
       if (BLAY == BL_NK)
-        issue_tile(in ? rsB : rsZ, sa + GM_TILE_BYTES, b_stride, (uint32_t)kt * 128u);
+        issue_tile(std::integral_constant<int, GM_BN>{}, in ? rsB : rsZ, sa + GM_TILE_BYTES,
+                   b_stride, (uint32_t)kt * 128u);
       if (BLAY == BL_PACKED)
         issue_block(in ? rsB : rsZ, sa + GM_TILE_BYTES, (uint32_t)kt * GM_TILE_BYTES);
       if (MXT) {   // 4 scale bytes per row: one dword per lane, 64 rows per wave
@@ -555,9 +606,9 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // sits before the LAST k-step of each K-tile: that k-step's fragments are
     // already in registers, so its 16 MFMAs keep the pipe busy while the next
     // stage's first fragments are read and the next DMA is issued.
-    bf16x8 af[2][4], bfr[2][4];                 // bf16 fragments
-    i32x8 afx[2][4], bfx[2][4];                 // e4m3 fragments (32 bytes per lane)
-    uint32_t sca[2][4], scb[2][4];              // E8M0 scales per stage set
+    bf16x8 af[2][MI], bfr[2][4];                // bf16 fragments
+    i32x8 afx[2][MI], bfx[2][4];                // e4m3 fragments (32 bytes per lane)
+    uint32_t sca[2][MI], scb[2][4];             // E8M0 scales per stage set
     // reads in order of first use by the MFMA sequence (i outer, j inner).
     // bf16: lane half h = lane / 32 takes 16-byte chunk 2 ks + h of its row
     // (8 k values).  e4m3: the block-scaled MFMA takes, in lane half h, bytes
@@ -570,7 +621,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     auto frag_load = [&](const uint8_t* sa, int ks, int buf, int sset) {
       const uint8_t* sb = sa + GM_TILE_BYTES;
       const int h = lane_t >> 5;
-      const int ra = wm * 128 + (lane_t & 31), rbw = wn * 128 + (lane_t & 31);
+      const int ra = wm * HR + (lane_t & 31), rbw = wn * 128 + (lane_t & 31);
       if constexpr (!MXT) {
         const int ch = ks * 2 + h;
         auto rd_a = [&](int i) {
@@ -581,7 +632,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         };
         rd_a(0);
         rd_b(0); rd_b(1); rd_b(2); rd_b(3);
-        rd_a(1); rd_a(2); rd_a(3);
+#pragma unroll
+        for (int i = 1; i < MI; ++i) rd_a(i);
       } else {
         const int ch = ks * 4 + h;
         auto rd32 = [&](const uint8_t* t, int r) {
@@ -595,7 +647,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           const uint32_t* ssa = reinterpret_cast<const uint32_t*>(sa + 2 * GM_TILE_BYTES);
           const uint32_t* ssb = reinterpret_cast<const uint32_t*>(sa + 2 * GM_TILE_BYTES + 1024);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sca[sset][i] = ssa[ra + i * 32];
+          for (int i = 0; i < MI; ++i) sca[sset][i] = ssa[ra + i * 32];
 #pragma unroll
           for (int j = 0; j < 4; ++j) scb[sset][j] = ssb[rbw + j * 32];
         }
@@ -603,14 +655,14 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) bfx[buf][j] = rd32(sb, rbw + j * 32);
 #pragma unroll
-        for (int i = 1; i < 4; ++i) afx[buf][i] = rd32(sa, ra + i * 32);
+        for (int i = 1; i < MI; ++i) afx[buf][i] = rd32(sa, ra + i * 32);
       }
     };
     // the 16 MFMAs of one k-step on fragment buffer buf (k-step ks of the
     // K-tile, scale set sset)
     auto mfmas = [&](int buf, int sset, int ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (!MXT) {
@@ -629,30 +681,35 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         }
     };
     // LDS reads issued by the frag_load just before a k-step
-    constexpr int DS_STEP = MXT ? 16 : 8;
-    // 16 MFMAs; the LDS reads issued just before are spread over them from
-    // the first MFMA on, so each has many MFMAs of cover before its use
+    constexpr int DS_STEP = MXT ? 2 * (MI + 4) : MI + 4;
+    constexpr int NMF = 4 * MI;                 // MFMAs per k-step
+    // NMF MFMAs; the LDS reads issued just before are spread over them from
+    // the first MFMA on (two per MFMA where there are more reads than
+    // MFMAs), so each has many MFMAs of cover before its use
     auto mfma_step = [&](int buf, int sset, int ks) {
       mfmas(buf, sset, ks);
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        if (g < DS_STEP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
-      }
+      static_for<NMF>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        if constexpr (g < DS_STEP)
+          __builtin_amdgcn_sched_group_barrier(0x100, g < DS_STEP - NMF ? 2 : 1, 0);   // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // 1 MFMA
+      });
       __builtin_amdgcn_sched_barrier(0);
     };
-    // The same with the next stage's DMA (16 VMEM instructions per wave, 18
-    // with MXFP8 scales) spread over the MFMAs, one per MFMA: issued as a
-    // burst right after the barrier, the four waves' DMA instructions queue
-    // at the address unit and hold up the MFMAs issued behind them.
+    // The same with the next stage's DMA (NVM VMEM instructions per wave, 2
+    // more with MXFP8 scales) spread over the MFMAs, one or two per MFMA:
+    // issued as a burst right after the barrier, the four waves' DMA
+    // instructions queue at the address unit and hold up the MFMAs issued
+    // behind them.
+    constexpr int NVM = WG ? 16 : TBM / 32 + 8;
     auto mfma_step_dma = [&](int buf, int sset, int ks) {
       mfmas(buf, sset, ks);
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        if (g < DS_STEP) __builtin_amdgcn_sched_group_barrier(0x100, MXT ? 2 : 1, 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                         // 1 VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // 1 MFMA
-      }
+      static_for<NMF>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        if constexpr (g < DS_STEP) __builtin_amdgcn_sched_group_barrier(0x100, MXT ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, NVM / NMF + (g < NVM % NMF ? 1 : 0), 0);  // DMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // MFMA
+      });
       __builtin_amdgcn_sched_barrier(0);
     };
     // k-steps 0 .. KSTEPS-2 of the K-tile in stage sa (fragments of k-step 0
@@ -715,10 +772,10 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     uint16_t* wstg = reinterpret_cast<uint16_t*>(wm ? lds1 : lds0) + z0;
     const int lm = (lane & 31) + z0;
     const int ln = 4 * (lane >> 5) + z0;
-    float rsc[4];
+    float rsc[MI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wm * 128 + 32 * i + lm;
+    for (int i = 0; i < MI; ++i) {
+      const int m = wm * HR + 32 * i + lm;
       rsc[i] = (p.ep.row_scale && m < rows_valid) ? p.ep.row_scale[row0 + m] : 1.0f;
     }
 
@@ -731,8 +788,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       const int lh = (lane >> 5) + z0;
       if (!(p.accumulate && m_e == 0)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t rowb = (uint32_t)(mt * GM_BM + wm * 128 + 32 * i + lm) * (uint32_t)p.N * 4u;
+        for (int i = 0; i < MI; ++i) {
+          const uint32_t rowb = (uint32_t)(mt * GM_BM + wm * HR + 32 * i + lm) * (uint32_t)p.N * 4u;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -801,7 +858,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       // stage the pre-activation: gate at columns 0..127, up at 128..255
       auto stage_preact = [&](int i, int jj, int pp, int h, const float (&g)[4], const float (&u)[4]) {
         const int c = wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
-        uint16_t* srow = wstg + ((wm * 128 + 32 * i + lm) & 127) * GM_STG_LD_256;
+        uint16_t* srow = wstg + (32 * i + lm) * GM_STG_LD_256;
         *reinterpret_cast<uint2*>(srow + c) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
         *reinterpret_cast<uint2*>(srow + 128 + c) =
             make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
@@ -809,8 +866,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       const rsrc_t rsY = make_rsrc(p.C ? p.C + (long long)row0 * p.I : p.A,
                                    p.C ? (long long)rows_valid * p.I * 2 : 0);
       float ymax = 0.0f;                   // max |y| of this lane's valid rows
-      auto body = [&](auto actc) {
-        constexpr int ACT = decltype(actc)::value;
+      auto body = [&]() {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
@@ -819,8 +875,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
             // byte offset of this lane's 16 bytes in row 0 of the tile
             const uint32_t ycol = (uint32_t)(wn * 64 + 32 * jj + 16 * pp + 8 * lh);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int m = wm * 128 + 32 * i + lm;
+            for (int i = 0; i < MI; ++i) {
+              const int m = wm * HR + 32 * i + lm;
               uint32_t yw[2][2];
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
@@ -842,7 +898,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
                 }
                 if (MXO) {   // y staged for the MXFP8 round (128 columns)
                   const int c = wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
-                  *reinterpret_cast<uint2*>(wstg + (m & 127) * GM_STG_LD_128 + c) =
+                  *reinterpret_cast<uint2*>(wstg + (32 * i + lm) * GM_STG_LD_128 + c) =
                       make_uint2(yw[h][0], yw[h][1]);
                 } else if (p.preact) {
                   stage_preact(i, jj, pp, h, g, u);
@@ -864,11 +920,11 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       auto store_preact = [&]() {
         __syncthreads();
         const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0,
-                      GM_STG_LD_256};
+                      GM_STG_LD_256, HR};
         uint16_t* prow0 = p.preact + (long long)row0 * ld2 + nt * 128;
         const int t = tid + z0;
 #pragma unroll 4
-        for (int it = t; it < GM_BM * 32; it += GM_NT) {
+        for (int it = t; it < TBM * 32; it += GM_NT) {
           const int r = it >> 5, ch = it & 31, cc = (ch & 15) * 8;
           if (r < rows_valid && cc < cvalid_n) {
             const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
@@ -886,7 +942,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
+              for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                   float g[4], u[4];
@@ -897,18 +953,13 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         store_preact();
       }
       if (wave_on) {
-        switch (p.ep.act) {
-          case ACT_SWIGLU: body(std::integral_constant<int, ACT_SWIGLU>{}); break;
-          case ACT_GEGLU: body(std::integral_constant<int, ACT_GEGLU>{}); break;
-          case ACT_GEGLU_TANH: body(std::integral_constant<int, ACT_GEGLU_TANH>{}); break;
-          default: body(std::integral_constant<int, ACT_SRELU>{}); break;
-        }
+        body();
         if (p.ep.amax_out) wave_amax_atomic(ymax, p.ep.amax_out, lane);   // NaN dropped by fmaxf
       }
       if (MXO) {
         __syncthreads();
         mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0,
-                          GM_STG_LD_128},
+                          GM_STG_LD_128, HR},
                       rows_valid, cvalid_n, row0, nt * 128, p, gs.mxs_off[e] + mt * 8);
         __syncthreads();
       } else if (p.preact) {
@@ -917,15 +968,14 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     } else if (EPI == EPI_STORE) {
       const int ld = GM_STG_LD_256;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 128 + 32 * i + lm;
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_sched_barrier(0);
             const int n = wn * 128 + 32 * j + 8 * q + ln;
-            *reinterpret_cast<uint2*>(wstg + (m & 127) * ld + n) =
+            *reinterpret_cast<uint2*>(wstg + (32 * i + lm) * ld + n) =
                 make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                            pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
           }
@@ -933,9 +983,11 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       __syncthreads();
       const int cvalid_n = min(GM_BN, p.N - n0);
       if (p.C)
-        store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
+        store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR},
+                    rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
       if (p.row_q || p.col_q)
-        mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld}, rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
+        mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR},
+                      rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
       __syncthreads();
     } else {  // EPI_DGLU: acc = G = dL/dy for columns n0 .. n0+255 of I
       const int ld = GM_STG_LD_256;
@@ -952,14 +1004,13 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       // 64 columns each, and goes out as four 128-byte row segments.
       const rsrc_t rsPre = make_rsrc(p.preact + (long long)row0 * ld2,
                                      (long long)rows_valid * ld2 * 2);
-      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld};
-      auto do_block = [&](auto actc, auto jc) {
-        constexpr int ACT = decltype(actc)::value;
+      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR};
+      auto do_block = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        u32x4 lg[4][2], lu[4][2];
+        u32x4 lg[MI][2], lu[MI][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t rowb = (uint32_t)(wm * 128 + 32 * i + lm) * (uint32_t)ld2 * 2u;
+        for (int i = 0; i < MI; ++i) {
+          const uint32_t rowb = (uint32_t)(wm * HR + 32 * i + lm) * (uint32_t)ld2 * 2u;
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
             const uint32_t col = (uint32_t)(n0 + wn * 128 + 32 * j + 16 * pp + 8 * lh);
@@ -969,9 +1020,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = wm * 128 + 32 * i + lm;
-          uint16_t* srow = wstg + (m & 127) * ld;
+        for (int i = 0; i < MI; ++i) {
+          uint16_t* srow = wstg + (32 * i + lm) * ld;
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
             // w[h2][d]: dword d (columns 2d, 2d+1) of column group q = 2pp + h2
@@ -1017,21 +1067,13 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       // (accumulator indices must stay compile-time constants, or the
       // accumulators move to scratch memory: every block index is a template
       // constant and both rounds are written out)
-      auto blocks = [&](auto actc, auto rc) {
+      auto stage_round = [&](auto rc) {
         constexpr int R = decltype(rc)::value;
         __builtin_amdgcn_sched_barrier(0);
-        do_block(actc, std::integral_constant<int, 2 * R>{});
+        do_block(std::integral_constant<int, 2 * R>{});
         __builtin_amdgcn_sched_barrier(0);
-        do_block(actc, std::integral_constant<int, 2 * R + 1>{});
+        do_block(std::integral_constant<int, 2 * R + 1>{});
         __builtin_amdgcn_sched_barrier(0);
-      };
-      auto stage_round = [&](auto rc) {
-        switch (p.ep.act) {
-          case ACT_SWIGLU: blocks(std::integral_constant<int, ACT_SWIGLU>{}, rc); break;
-          case ACT_GEGLU: blocks(std::integral_constant<int, ACT_GEGLU>{}, rc); break;
-          case ACT_GEGLU_TANH: blocks(std::integral_constant<int, ACT_GEGLU_TANH>{}, rc); break;
-          default: blocks(std::integral_constant<int, ACT_SRELU>{}, rc); break;
-        }
       };
       float hmax = 0.0f;   // rotated amax of this thread's share of the tile
 #pragma unroll
@@ -1049,7 +1091,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         if (p.C) {
           const int t = tid + z0;
 #pragma unroll 4
-          for (int it = t; it < GM_BM * 32; it += GM_NT) {
+          for (int it = t; it < TBM * 32; it += GM_NT) {
             const int r = it >> 5, k = (it >> 3) & 3, pc = it & 7;
             const int c = chunk_col(k) + pc * 8;
             if (r < rows_valid && c < p.I) {
@@ -1063,13 +1105,20 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           for (int k = 0; k < 4; ++k) {
             const int nv = min(64, p.I - chunk_col(k));
             if (nv > 0)
-              mx_from_stage(Stg{stg.h0 + k * 64, stg.h1 + k * 64, ld}, rows_valid, nv, row0,
+              mx_from_stage(Stg{stg.h0 + k * 64, stg.h1 + k * 64, ld, HR}, rows_valid, nv, row0,
                             (k < 2 ? 0 : p.I) + chunk_col(k), p, gs.mxs_off[e] + mt * 8);
           }
         }
         __syncthreads();
       }
       if (p.ep.amax_out) wave_amax_atomic(hmax, p.ep.amax_out, lane);
+    }
+    };  // tile_body
+    if constexpr (WG) {
+      tile_body(std::integral_constant<int, 4>{});
+    } else {
+      if (rows_valid <= 128) tile_body(std::integral_constant<int, 2>{});
+      else tile_body(std::integral_constant<int, 4>{});
     }
   }
 }

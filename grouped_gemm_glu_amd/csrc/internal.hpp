@@ -16,8 +16,27 @@ moe_status_t launch_group_gemm_bwd(int epi, int blay, const GemmArgs& args, int 
                                    hipStream_t stream);
 // MXFP8 x MXFP8 GroupGemm (packed MXFP8 weight, bf16 output)
 moe_status_t launch_group_gemm_mx(const GemmArgs& args, int grid, hipStream_t stream);
-// FC1 + GLU with MXFP8 inputs (epi: EPI_GLU or EPI_GLU_MX)
-moe_status_t launch_group_gemm_mx_glu(const GemmArgs& args, int epi, int grid, hipStream_t stream);
+
+// Kernels whose epilogue applies the activation exist once per activation
+// (gemm_act_fwd.hip and gemm_act_bwd.hip are compiled once per value of
+// MOE_ACT); launch_activation_kernel picks the one for args.ep.act.
+enum {
+  KIND_GLU = 0,          // FC1 + GLU, bf16 operands, packed W1
+  KIND_GLU_MXO,          // the same with MXFP8 outputs
+  KIND_MXIN_GLU,         // FC1 + GLU, MXFP8 operands
+  KIND_MXIN_GLU_MXO,     // the same with MXFP8 outputs
+  KIND_DGLU_PACKED,      // dgrad + dGLU, packed W2
+  KIND_DGLU_NK           // dgrad + dGLU, W2 as [I][H]
+};
+moe_status_t launch_activation_kernel(int kind, const GemmArgs& args, int grid, hipStream_t stream);
+#define MOE_DECLARE_ACT_LAUNCHERS(n)                                                              \
+  moe_status_t launch_act_fwd_##n(int kind, const GemmArgs& args, int grid, hipStream_t stream); \
+  moe_status_t launch_act_bwd_##n(int kind, const GemmArgs& args, int grid, hipStream_t stream);
+MOE_DECLARE_ACT_LAUNCHERS(0)
+MOE_DECLARE_ACT_LAUNCHERS(1)
+MOE_DECLARE_ACT_LAUNCHERS(2)
+MOE_DECLARE_ACT_LAUNCHERS(3)
+#undef MOE_DECLARE_ACT_LAUNCHERS
 // K-grouped weight gradient (fp32 output)
 moe_status_t launch_group_gemm_wgrad(const GemmArgs& args, int grid, hipStream_t stream);
 
