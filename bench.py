@@ -253,8 +253,9 @@ def main():
                                                M, H, I, ep, y, kern_ms["fc1_glu"])
         log("secondary: CU margin with a concurrent copy")
         extra["cu_margin_overlap"] = bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre)
-        log("secondary: NVFP4-style amax outputs")
-        extra["amax_outputs"] = bench_amax(G, torch, x, grp, w1p, H, I, y, pre, dy2, op_w2d, dgu)
+        log("secondary: amax outputs and parameter gradients")
+        extra["epilogue_extras"] = bench_amax(G, torch, x, grp, w1p, E, H, I, y, pre, dy2, op_w2d,
+                                               dgu)
         log("secondary: MXFP8 forward")
         extra["mxfp8_dsv3_share"] = bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts,
                                                 counts_h, E, M, H, I, kern_ms)
@@ -425,13 +426,18 @@ def bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre, margin=32, copy_mib=2
     return res
 
 
-def bench_amax(G, torch, x, grp, w1p, H, I, y, pre, dy2, op_w2d, dgu):
+def bench_amax(G, torch, x, grp, w1p, E, H, I, y, pre, dy2, op_w2d, dgu):
     """FC1 with the per-tensor amax of y, and dgrad + dSwiGLU with the amax of
     the 16-row Hadamard rotation of dgu^T, each beside the same kernel without
     it (interleaved timing)."""
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    db = torch.zeros((E, 2 * I), dtype=torch.float32, device="cuda")
+    drs = torch.zeros(y.shape[0], dtype=torch.float32, device="cuda")
     ep0 = G.epilogue("swiglu")
     ep1 = G.epilogue("swiglu", amax_out=amax, rht_signs=0x5A3C)
+    ep2 = G.epilogue("swiglu", dbias_out=db, drow_scale_out=drs)
+    ep3 = G.epilogue("swiglu", dbias_out=db)
+    ep4 = G.epilogue("swiglu", drow_scale_out=drs)
 
     def fc1(ep):
         return lambda: G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, y, pre)
@@ -440,10 +446,13 @@ def bench_amax(G, torch, x, grp, w1p, H, I, y, pre, dy2, op_w2d, dgu):
         return lambda: G.moe_group_gemm_dglu_bwd(dy2, op_w2d, H, I, grp, pre, ep, dgu)
 
     pm = paired_ms(torch, {"fc1": fc1(ep0), "fc1_amax": fc1(ep1),
-                           "dglu": dglu(ep0), "dglu_rht_amax": dglu(ep1)})
+                           "dglu": dglu(ep0), "dglu_rht_amax": dglu(ep1),
+                           "dglu_param_grads": dglu(ep2), "dglu_dbias": dglu(ep3),
+                           "dglu_drow_scale": dglu(ep4)})
     return {k: round(v, 4) for k, v in pm.items()} | {
-        "what": "FC1 + SwiGLU with max|y| and dgrad + dSwiGLU with the amax of H16 S / 4 "
-                "over 16-row runs of dgu^T, against the same kernels without them",
+        "what": "FC1 + SwiGLU with max|y|; dgrad + dSwiGLU with the amax of H16 S / 4 over "
+                "16-row runs of dgu^T, and with d(bias) and d(row_scale) added; against the "
+                "same kernels without them",
         "timing": "interleaved, best of 3 rounds of 10"}
 
 

@@ -35,7 +35,8 @@ class EpilogueT(ctypes.Structure):
                 ("up_lo", ctypes.c_float), ("up_hi", ctypes.c_float),
                 ("up_offset", ctypes.c_float), ("bias", ctypes.c_void_p),
                 ("row_scale", ctypes.c_void_p), ("amax_out", ctypes.c_void_p),
-                ("rht_signs", ctypes.c_uint32)]
+                ("rht_signs", ctypes.c_uint32), ("dbias_out", ctypes.c_void_p),
+                ("drow_scale_out", ctypes.c_void_p)]
 
 
 class MxOutT(ctypes.Structure):
@@ -130,14 +131,18 @@ def _keep(struct, *objs):
 def epilogue(act: str = "swiglu", alpha: float = 1.0, gate_lo: float = -math.inf,
              gate_hi: float = math.inf, up_lo: float = -math.inf, up_hi: float = math.inf,
              up_offset: float = 0.0, bias=None, row_scale=None, gated: bool = True,
-             amax_out=None, rht_signs: int = 0) -> EpilogueT:
+             amax_out=None, rht_signs: int = 0, dbias_out=None,
+             drow_scale_out=None) -> EpilogueT:
     """Builds the moe_epilogue_t struct; ``bias`` is plain-order bf16 [E][2I];
     ``amax_out`` a one-element float32 device tensor raised to the output's
     amax (forward) or to the amax of its 16-row Hadamard rotation (dGLU
-    backward, row signs from the low 16 bits of ``rht_signs``)."""
+    backward, row signs from the low 16 bits of ``rht_signs``);
+    ``dbias_out`` float32 [E][2I] and ``drow_scale_out`` float32 [M_cap]
+    (dGLU backward) are added to."""
     return _keep(EpilogueT(ACT[act], 1 if gated else 0, alpha, gate_lo, gate_hi, up_lo, up_hi,
                            up_offset, _ptr(bias), _ptr(row_scale), _ptr(amax_out),
-                           rht_signs & 0xFFFF), bias, row_scale, amax_out)
+                           rht_signs & 0xFFFF, _ptr(dbias_out), _ptr(drow_scale_out)),
+                 bias, row_scale, amax_out, dbias_out, drow_scale_out)
 
 
 def groups(counts, M_cap: int, offsets_out=None, status_out=None) -> GroupsT:

@@ -65,6 +65,10 @@ moe_status_t fill_epilogue(const moe_epilogue_t* ep, EpiParams* out) {
   if (ep->amax_out && !aligned4(ep->amax_out)) return MOE_ERR_ALIGN;
   out->amax_out = ep->amax_out;
   out->rht_signs = ep->rht_signs & 0xFFFFu;
+  if ((ep->dbias_out && !aligned4(ep->dbias_out)) || (ep->drow_scale_out && !aligned4(ep->drow_scale_out)))
+    return MOE_ERR_ALIGN;
+  out->dbias_out = ep->dbias_out;
+  out->drs_out = ep->drow_scale_out;
   return MOE_OK;
 }
 
@@ -101,7 +105,7 @@ int persistent_grid(int cus, int cu_margin, int M_cap, int E, int ntiles_n) {
 namespace moe {
 
 moe_status_t launch_activation_kernel(int kind, const GemmArgs& a, int grid, hipStream_t s) {
-  const bool bwd = kind == KIND_DGLU_PACKED || kind == KIND_DGLU_NK;
+  const bool bwd = kind >= KIND_DGLU_PACKED;
   switch (a.ep.act) {
     case ACT_SWIGLU: return bwd ? launch_act_bwd_0(kind, a, grid, s) : launch_act_fwd_0(kind, a, grid, s);
     case ACT_GEGLU: return bwd ? launch_act_bwd_1(kind, a, grid, s) : launch_act_fwd_1(kind, a, grid, s);
@@ -368,8 +372,10 @@ moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, i
   fill_mx(&a, mx, 2 * I, groups);
   a.ntiles_n = (I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  return launch_activation_kernel(w2_packed ? KIND_DGLU_PACKED : KIND_DGLU_NK, a, grid,
-                                  (hipStream_t)stream);
+  const bool grads = a.ep.dbias_out || a.ep.drs_out;
+  return launch_activation_kernel(grads ? (w2_packed ? KIND_DGLU_G_PACKED : KIND_DGLU_G_NK)
+                                        : (w2_packed ? KIND_DGLU_PACKED : KIND_DGLU_NK),
+                                  a, grid, (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t* b_op, int N,

@@ -188,6 +188,8 @@ struct EpiParams {
   const float* row_scale;    // [M_cap] or null
   float* amax_out;           // raised atomically to an amax, or null
   uint32_t rht_signs;        // row signs of the 16-point rotation (bit i: row i)
+  float* dbias_out;          // backward: [E][2I] += column sums of dgu, or null
+  float* drs_out;            // backward: [M_cap] += d(row_scale), or null
 };
 
 // ---------------------------------------------------------------- group scan

@@ -73,7 +73,10 @@ struct Stg {
   __device__ __forceinline__ int rows() const { return 2 * hr; }
 };
 
-enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4 };
+// EPI_DGLU_G: EPI_DGLU that also adds the gradients of the epilogue's own
+// parameters (bias, row scale); a kernel of its own, so that the plain
+// backward epilogue keeps its register allocation.
+enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4, EPI_DGLU_G = 5 };
 enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 // operand element type: bf16, or MXFP8 (OCP e4m3 codes with one E8M0 scale
 // per 32 consecutive K values, consumed by the block-scaled MFMA)
@@ -358,6 +361,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[GM_STAGE_ALLOC];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[GM_STAGE_ALLOC];
   __shared__ GroupScan gs;
+  __shared__ float drs_lds[GM_BM];   // dGLU: per-row d(row_scale) of the tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1005,8 +1009,19 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       const rsrc_t rsPre = make_rsrc(p.preact + (long long)row0 * ld2,
                                      (long long)rows_valid * ld2 * 2);
       const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR};
+      // d(row_scale): per block j and row block, each lane sums G * a(g_c) *
+      // u_c (dL/dy times the unscaled y) over its 16 columns and adds that
+      // to the row's LDS slot; after the tile one global atomic per row
+      constexpr bool PG = EPI == EPI_DGLU_G;
+      const bool want_drs = PG && p.ep.drs_out != nullptr;
+      if (want_drs) {
+        for (int r = tid; r < TBM; r += GM_NT) drs_lds[r] = 0.0f;
+        __syncthreads();
+      }
       auto do_block = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
+        // (a select, not a branch: the block stays one scheduling region)
+        const bool drs_j = want_drs && n0 + wn * 128 + 32 * j < p.I;   // whole block (I % 64 == 0)
         u32x4 lg[MI][2], lu[MI][2];
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -1022,6 +1037,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           uint16_t* srow = wstg + (32 * i + lm) * ld;
+          float drs_part = 0.0f;
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
             // w[h2][d]: dword d (columns 2d, 2d+1) of column group q = 2pp + h2
@@ -1043,7 +1059,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
               float dg[4], du[4];
 #pragma unroll
               for (int s2 = 0; s2 < 4; ++s2) {
-                const float G = acc[i][j][4 * q + s2] * rsc[i];
+                const float Gu = acc[i][j][4 * q + s2];
+                const float G = Gu * rsc[i];
                 const float g = gv[s2], u = uv[s2];
                 const float gc = fminf(fmaxf(g, p.ep.gate_lo), p.ep.gate_hi);
                 const float uc = fminf(fmaxf(u, p.ep.up_lo), p.ep.up_hi) + p.ep.up_offset;
@@ -1053,6 +1070,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
                 const bool uin = (u >= p.ep.up_lo) && (u <= p.ep.up_hi);
                 dg[s2] = gin ? G * uc * da : 0.0f;
                 du[s2] = uin ? G * a : 0.0f;
+                if constexpr (PG) drs_part += Gu * (a * uc);
               }
               // staged column: wave's 64-column half (j & 1) at chunk wn (dg) / 2 + wn (du)
               const int sc = wn * 64 + 32 * (j & 1) + 8 * q + ln;
@@ -1062,6 +1080,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
                   make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
             }
           }
+          if (PG && drs_j) atomicAdd(&drs_lds[wm * HR + 32 * i + lm], drs_part);   // LDS add
         }
       };
       // (accumulator indices must stay compile-time constants, or the
@@ -1088,6 +1107,28 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           const uint32_t ok = (chunk_col(0) < p.I ? 5u : 0u) | (chunk_col(1) < p.I ? 10u : 0u);
           hmax = fmaxf(hmax, rht16_amax_stage(stg, rows_valid, ok, p.ep.rht_signs));
         }
+        if (PG && p.ep.dbias_out) {
+          // d(bias): thread t sums staged column t (chunk t / 64) over the
+          // tile's valid rows (bf16 values as written), one atomic per column
+          const int t = tid + z0, k = t >> 6, c = chunk_col(k) + (t & 63);
+          if (c < p.I) {
+            // 8 rows per step, 4 partial sums: the loads run ahead of the adds
+            float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const uint16_t* col = (hh ? stg.h1 : stg.h0) + k * 64 + (t & 63);
+              const int nr = min(HR, rows_valid - hh * HR);
+              int r = 0;
+              for (; r + 8 <= nr; r += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) s4[u & 3] += bf16_to_f32(col[(r + u) * ld]);
+              }
+              for (; r < nr; ++r) s4[0] += bf16_to_f32(col[r * ld]);
+            }
+            atomicAdd(p.ep.dbias_out + (long long)e * ld2 + (k < 2 ? 0 : p.I) + c,
+                      (s4[0] + s4[1]) + (s4[2] + s4[3]));
+          }
+        }
         if (p.C) {
           const int t = tid + z0;
 #pragma unroll 4
@@ -1112,6 +1153,10 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         __syncthreads();
       }
       if (p.ep.amax_out) wave_amax_atomic(hmax, p.ep.amax_out, lane);
+      if (want_drs) {   // (the rounds end with a barrier: every LDS add is in)
+        for (int r = tid; r < rows_valid; r += GM_NT) atomicAdd(p.ep.drs_out + row0 + r, drs_lds[r]);
+        __syncthreads();
+      }
     }
     };  // tile_body
     if constexpr (WG) {

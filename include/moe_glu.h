@@ -88,6 +88,16 @@ typedef struct {
      NaN values are skipped.  Other entry points ignore both fields. */
   float* amax_out;
   uint32_t rht_signs;       /* low 16 bits: the row signs of the backward rotation */
+  /* Gradients of the epilogue's own parameters, written by moe_group_gemm_dglu_bwd only
+     (nullable device fp32 buffers, 4-byte aligned, ADDED to atomically, so the caller zeroes
+     them or passes running sums; the summation order is unspecified):
+       dbias_out      [E][2I], plain (gate | up) order: per expert, the sum over its rows of
+                      dgu (the bf16 values as written) = dL/d(bias) of the FC1 + GLU forward;
+       drow_scale_out [M_cap]: for every routed row r, sum over j < I of G[r][j] a(g_c) u_c,
+                      G = dY2 W2^T (= dL/dy) and a(g_c) u_c the unscaled GLU output in fp32 =
+                      dL/d(row_scale[r]); rows past the routed ones are not touched. */
+  float* dbias_out;
+  float* drow_scale_out;
 } moe_epilogue_t;
 
 /* MXFP8 outputs ([BLOG] "Fusionando cuantización MXFP8 y NVFP4": the

@@ -34,6 +34,7 @@ for those choices.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass
 from typing import Optional
@@ -420,6 +421,44 @@ def rht16_amax(dgu_bits, counts, signs: int = 0) -> float:
             if rot.size:
                 amax = max(amax, float(rot.max()))
     return amax
+
+
+def bias_grad(dgu_bits, counts) -> np.ndarray:
+    """Gradient of the FC1 bias: z = x W1 + b1 gives dL/db1_e = the sum over
+    expert e's rows of dL/dz = dgu ("Boosting MoE Training Throughput with
+    Advanced Fusion Kernels": the backward epilogue produces dgu; its column
+    sums complete the backward step).  Reading: the sum of the bf16 values as
+    stored.  Returns float64 [E][2I] in plain (gate | up) order; an empty
+    expert gives zeros."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    v = bf16_bits_to_f64(np.asarray(dgu_bits))
+    out = np.zeros((len(counts), v.shape[1]))
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            out[e] = v[a:b].sum(axis=0)
+    return out
+
+
+def row_scale_grad(dy2_bits, counts, w2_bits, preact_bits, ep: Epilogue) -> np.ndarray:
+    """Gradient of the per-row scale: y_r = a(g_c) u_c rs_r gives dL/drs_r =
+    sum_j G[r][j] a(g_c)[r][j] u_c[r][j] with G = dY2_e W2_e^T = dL/dy (the
+    same GEMM as ``dgrad_dglu``) and g, u from the saved bf16
+    pre-activation.  Returns float64 [M] over the routed rows."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    M = int(off[-1])
+    out = np.zeros(M)
+    ep_u = dataclasses.replace(ep, bias=None, row_scale=None)     # the unscaled y
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        G = bf16_bits_to_f64(dy2_bits[a:b]) @ bf16_bits_to_f64(w2_bits[e]).T
+        yu = glu_from_preact(bf16_bits_to_f64(preact_bits[a:b]), ep_u)
+        out[a:b] = np.sum(G * yu, axis=1)
+    return out
 
 
 def wgrad(a_bits, counts, b_bits, dtype=np.float64):

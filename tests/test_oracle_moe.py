@@ -619,3 +619,83 @@ def test_rht16_amax_against_library_hadamard():
     blk = v[:16]
     R = O.sylvester_hadamard(16) @ S / 4
     assert np.isclose(np.linalg.norm(R @ blk), np.linalg.norm(blk))
+
+
+def _dyadic_chain(seed, act, ep_kw):
+    """A tiny chain whose pre-activations are exact in bf16 (x in {-1,0,1},
+    W1 in {-0.5,0,0.5}, b1 in {-0.25,0,0.25}: z is a multiple of 0.25 below
+    4.25 in magnitude), so the oracle's bf16 pre-activation equals the exact z."""
+    rng = np.random.default_rng(seed)
+    T, H, I, E = 5, 8, 8, 2
+    counts = np.array([3, 2])
+    x = rng.integers(-1, 2, (T, H)).astype(np.float64)
+    w1 = rng.integers(-1, 2, (E, H, 2 * I)) * 0.5
+    b1 = rng.integers(-1, 2, (E, 2 * I)) * 0.25
+    w2 = F.bf16_round(rng.standard_normal((E, I, H)) * 0.5)
+    dy2 = F.bf16_round(rng.standard_normal((T, H)))
+    rs = F.bf16_round(rng.uniform(0.5, 1.5, T))
+    ep = O.Epilogue(act=act, **ep_kw)
+    return counts, x, w1, b1, w2, dy2, rs, ep
+
+
+def _loss_rs(x, counts, w1, b1, w2, dy2, rs, ep):
+    off = np.concatenate([[0], np.cumsum(counts)])
+    L = 0.0
+    for e in range(len(counts)):
+        a, b = off[e], off[e + 1]
+        z = x[a:b] @ w1[e] + b1[e]
+        y = O.glu_from_preact(z, ep) * rs[a:b, None]
+        L += float(np.sum(dy2[a:b] * (y @ w2[e])))
+    return L
+
+
+@pytest.mark.parametrize("act,ep_kw", [("swiglu", dict(alpha=1.702)), ("geglu", {}),
+                                       ("srelu", dict(gate_lo=-1.0, gate_hi=1.0, up_offset=0.5))])
+def test_bias_and_row_scale_grads_against_finite_differences(act, ep_kw):
+    """dL/db1 and dL/drs of L = <dY2, FC2(GLU(X W1 + b1) * rs)> by central
+    differences in float64, against bias_grad (on the float64 dgu rounded to
+    bf16: bound = that rounding) and row_scale_grad."""
+    counts, x, w1, b1, w2, dy2, rs, ep = _dyadic_chain(5, act, ep_kw)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    z = np.concatenate([x[off[e]:off[e + 1]] @ w1[e] + b1[e] for e in range(2)])
+    assert np.array_equal(F.bf16_round(z), z)
+    G = np.concatenate([dy2[off[e]:off[e + 1]] @ w2[e].T for e in range(2)])
+    dz = O.dglu(G, z, ep, rs)
+    bits = F.f64_to_bf16_bits
+    db = O.bias_grad(bits(dz), counts)
+    drs = O.row_scale_grad(bits(dy2), counts, bits(w2), bits(z), ep)
+    checked = 0
+    for e in range(2):
+        for c in range(z.shape[1]):
+            h = 1e-6
+            bp, bm = b1.copy(), b1.copy()
+            bp[e, c] += h
+            bm[e, c] -= h
+            zr = z[off[e]:off[e + 1], c]
+            lo, hi = (ep.gate_lo, ep.gate_hi) if c < 8 else (ep.up_lo, ep.up_hi)
+            if np.any(np.abs(zr - lo) < 4 * h) or np.any(np.abs(zr - hi) < 4 * h) or (
+                    act == "srelu" and c < 8 and np.any(np.abs(zr) < 4 * h)):
+                continue
+            fd = (_loss_rs(x, counts, w1, bp, w2, dy2, rs, ep) -
+                  _loss_rs(x, counts, w1, bm, w2, dy2, rs, ep)) / (2 * h)
+            bound = 1e-6 * max(1.0, abs(fd)) + 2.0 ** -8 * np.sum(np.abs(dz[off[e]:off[e + 1], c]))
+            assert abs(db[e, c] - fd) <= bound, (e, c, db[e, c], fd)
+            checked += 1
+    assert checked >= 16
+    for r in range(x.shape[0]):
+        h = 1e-6
+        rp, rm = rs.copy(), rs.copy()
+        rp[r] += h
+        rm[r] -= h
+        fd = (_loss_rs(x, counts, w1, b1, w2, dy2, rp, ep) -
+              _loss_rs(x, counts, w1, b1, w2, dy2, rm, ep)) / (2 * h)
+        assert abs(drs[r] - fd) <= 1e-6 * max(1.0, abs(fd)), (r, drs[r], fd)
+
+
+def test_bias_grad_sums_rows_of_each_group():
+    v = np.arange(24, dtype=np.float64).reshape(6, 4) - 7
+    counts = np.array([2, 0, 3])          # rows 0-1, none, 2-4; row 5 unrouted
+    db = O.bias_grad(F.f64_to_bf16_bits(v), counts)
+    assert np.array_equal(db[0], v[0] + v[1])
+    assert np.array_equal(db[1], np.zeros(4))
+    assert np.array_equal(db[2], v[2] + v[3] + v[4])
