@@ -19,6 +19,11 @@ MXFP8 with 1x32 blocks and E8M0 scales):
 * e4m3fn (OCP 8-bit float, "fn" = finite, no infinity): exponent bias 7,
   largest finite value 448 = 1.75 * 2^8, S.1111.111 is NaN, subnormals are
   m * 2^-9 for m = 1..7.
+* e5m2 (OCP 8-bit float for gradients): exponent bias 15, largest finite
+  value 57344 = 1.75 * 2^15, S.11111.00 is infinity and S.11111.xx (xx != 0)
+  NaN, subnormals are m * 2^-16 for m = 1..3.  Used for the MXFP8 copies of
+  gradients (the E5M2 option of the MXFP8 recipe); the block scale rule is
+  the e4m3 one with 57344 in place of 448.
 * E8M0: an unsigned biased exponent, value 2^(byte - 127); 0xFF is NaN.
 """
 from __future__ import annotations
@@ -28,6 +33,8 @@ import numpy as np
 BF16_MIN_NORMAL_EXP = -126
 E4M3_MAX = 448.0
 E4M3_MIN_NORMAL_EXP = -6
+E5M2_MAX = 57344.0
+E5M2_MIN_NORMAL_EXP = -14
 E8M0_NAN = 0xFF
 
 
@@ -149,28 +156,89 @@ def e4m3_ulp(v) -> np.ndarray:
     return np.ldexp(1.0, p - 3)
 
 
+# ----------------------------------------------------------------------------- e5m2
+
+def e5m2_decode_table() -> np.ndarray:
+    """Value of each of the 256 e5m2 codes (float64; +-inf for S.11111.00, NaN for
+    the other S.11111.xx codes)."""
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 2) & 0x1F
+        m = c & 0x3
+        if e == 0x1F:
+            vals[c] = s * np.inf if m == 0 else np.nan
+        elif e == 0:
+            vals[c] = s * (m / 4.0) * 2.0 ** -14
+        else:
+            vals[c] = s * (1.0 + m / 4.0) * 2.0 ** (e - 15)
+    return vals
+
+
+_E5M2_TABLE = e5m2_decode_table()
+
+
+def e5m2_decode(codes) -> np.ndarray:
+    return _E5M2_TABLE[np.asarray(codes).astype(np.int64)]
+
+
+def e5m2_round(x) -> np.ndarray:
+    """Round float64 to the nearest e5m2 value, ties to even, saturating at +-57344
+    (2 stored mantissa bits: the quantum for floor(log2|x|) = p is
+    2^(max(p,-14)-2), subnormal quantum 2^-16).  The sign is kept."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    out = np.zeros_like(a)
+    nz = a > 0
+    p = np.maximum(_floor_log2(a[nz]), E5M2_MIN_NORMAL_EXP)
+    q = np.ldexp(1.0, p - 2)
+    out[nz] = np.minimum(np.rint(a[nz] / q) * q, E5M2_MAX)
+    return np.copysign(out, x)
+
+
+def f64_to_e5m2(x) -> np.ndarray:
+    """Encode float64 values to e5m2 codes (uint8), RNE, saturating, sign kept;
+    NaN gives 0x7F (0xFF with the sign bit set)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = e5m2_round(np.where(np.isnan(x), 0.0, x))
+    a = np.abs(r)
+    code = np.zeros(a.shape, dtype=np.int64)
+    nz = a > 0
+    p = np.maximum(_floor_log2(a[nz]), E5M2_MIN_NORMAL_EXP)
+    mant = np.rint(a[nz] / np.ldexp(1.0, p - 2)).astype(np.int64)   # 4..7 normal, 1..3 subnormal
+    code[nz] = np.where(mant >= 4, ((p + 15) << 2) + (mant - 4), mant)
+    code = code | np.where(np.signbit(r), 0x80, 0)
+    code = np.where(np.isnan(x), np.where(np.signbit(x), 0xFF, 0x7F), code)
+    return code.astype(np.uint8)
+
+
+FP8_FORMATS = {"e4m3": (E4M3_MAX, 8), "e5m2": (E5M2_MAX, 15)}   # (largest value, its exponent)
+
+
 # ----------------------------------------------------------------------------- E8M0 scale
 
-def mx_scale_exponent(amax) -> np.ndarray:
+def mx_scale_exponent(amax, fmt: str = "e4m3") -> np.ndarray:
     """Block scale exponent E for block maxima ``amax`` (float64, >= 0).
 
-    E is the smallest integer with amax / 2^E <= 448, i.e. ceil(log2(amax/448)),
-    clamped to [-127, 127].  An all-zero block gets E = -127.  This "round the
-    scale up" rule guarantees every scaled element is within e4m3's finite
-    range, so dequantize(quantize(v)) is within half an e4m3 ulp times 2^E of v.
-    Non-finite amax is reported as E = 128 (byte 0xFF, NaN).
+    E is the smallest integer with amax / 2^E <= vmax (448 for e4m3, 57344 for
+    e5m2), i.e. ceil(log2(amax/vmax)), clamped to [-127, 127].  An all-zero
+    block gets E = -127.  This "round the scale up" rule guarantees every
+    scaled element is within the element format's finite range, so
+    dequantize(quantize(v)) is within half an ulp times 2^E of v.  Non-finite
+    amax is reported as E = 128 (byte 0xFF, NaN).
     """
+    vmax, vexp = FP8_FORMATS[fmt]
     a = np.asarray(amax, dtype=np.float64)
     E = np.full(a.shape, -127, dtype=np.int64)
     fin = np.isfinite(a)
     pos = fin & (a > 0)
     ap = a[pos]
-    e = _floor_log2(ap) - 8          # 448 * 2^(floor(log2 a) - 8) lies in [0.875, 1.75) * a
-    # step up until amax <= 448 * 2^e, then down while the next lower power still fits
+    e = _floor_log2(ap) - vexp       # vmax * 2^(floor(log2 a) - vexp) lies in [0.875, 1.75) * a
+    # step up until amax <= vmax * 2^e, then down while the next lower power still fits
     for _ in range(3):
-        e = np.where(ap > E4M3_MAX * np.ldexp(1.0, e), e + 1, e)
+        e = np.where(ap > vmax * np.ldexp(1.0, e), e + 1, e)
     for _ in range(3):
-        e = np.where(ap <= E4M3_MAX * np.ldexp(1.0, e - 1), e - 1, e)
+        e = np.where(ap <= vmax * np.ldexp(1.0, e - 1), e - 1, e)
     E[pos] = np.clip(e, -127, 127)
     E[~fin] = 128
     return E
@@ -186,16 +254,20 @@ def e8m0_value(byte) -> np.ndarray:
     return np.where(b == E8M0_NAN, np.nan, np.ldexp(1.0, b - 127))
 
 
-def mx_quantize_block(v) -> tuple[np.ndarray, int]:
+def mx_quantize_block(v, fmt: str = "e4m3") -> tuple[np.ndarray, int]:
     """Quantise one block of values (float64, already bf16-rounded) to MXFP8.
 
-    Returns (e4m3 codes, E8M0 byte).  Elements are v * 2^-E rounded RNE to
-    e4m3fn; the multiply by a power of two is exact.
+    Returns (element codes, E8M0 byte).  Elements are v * 2^-E rounded RNE to
+    e4m3fn (or e5m2); the multiply by a power of two is exact.
     """
     v = np.asarray(v, dtype=np.float64)
     amax = np.max(np.abs(v)) if v.size else 0.0
-    E = int(mx_scale_exponent(np.array([amax]))[0])
+    E = int(mx_scale_exponent(np.array([amax]), fmt)[0])
     if E == 128:
         return np.full(v.shape, 0x7F, dtype=np.uint8), E8M0_NAN
-    codes = f64_to_e4m3(np.ldexp(v, -E))
-    return codes, E + 127
+    enc = f64_to_e4m3 if fmt == "e4m3" else f64_to_e5m2
+    return enc(np.ldexp(v, -E)), E + 127
+
+
+def fp8_decode(codes, fmt: str = "e4m3") -> np.ndarray:
+    return e4m3_decode(codes) if fmt == "e4m3" else e5m2_decode(codes)

@@ -500,9 +500,10 @@ def wgrad_abs(a_bits, counts, b_bits):
 MX_BLOCK = 32
 
 
-def mx_quantize_rows(v_bits):
+def mx_quantize_rows(v_bits, fmt: str = "e4m3"):
     """Row-wise MXFP8 ([BLOG] "Fusionando cuantización MXFP8…"): each run of 32
-    consecutive columns of a row is one block with its own E8M0 scale.
+    consecutive columns of a row is one block with its own E8M0 scale; the
+    elements are e4m3 codes, or e5m2 codes with ``fmt="e5m2"`` (gradients).
 
     v_bits [R][C] bf16 (C % 32 == 0).  Returns (q [R][C] uint8, s [R][C/32] uint8).
     """
@@ -512,7 +513,7 @@ def mx_quantize_rows(v_bits):
     s = np.zeros((R, C // MX_BLOCK), dtype=np.uint8)
     for r in range(R):
         for cb in range(C // MX_BLOCK):
-            codes, byte = mx_quantize_block(v[r, cb * MX_BLOCK:(cb + 1) * MX_BLOCK])
+            codes, byte = mx_quantize_block(v[r, cb * MX_BLOCK:(cb + 1) * MX_BLOCK], fmt)
             q[r, cb * MX_BLOCK:(cb + 1) * MX_BLOCK] = codes
             s[r, cb] = byte
     return q, s
@@ -527,7 +528,7 @@ def mx_scale_col_offsets(counts) -> np.ndarray:
     return so
 
 
-def mx_quantize_cols(v_bits, counts, m_cap: Optional[int] = None):
+def mx_quantize_cols(v_bits, counts, m_cap: Optional[int] = None, fmt: str = "e4m3"):
     """Column-wise (transposed) MXFP8 copy ([BLOG] "Fusionando cuantización
     MXFP8…": MXFP8 output plus a transposed version for back prop).
 
@@ -552,25 +553,26 @@ def mx_quantize_cols(v_bits, counts, m_cap: Optional[int] = None):
         for blk, r0 in enumerate(range(a, b, MX_BLOCK)):
             r1 = min(r0 + MX_BLOCK, b)
             for c in range(C):
-                codes, byte = mx_quantize_block(v[r0:r1, c])
+                codes, byte = mx_quantize_block(v[r0:r1, c], fmt)
                 col_q[c, r0:r1] = codes
                 col_s[c, so[e] + blk] = byte
     return col_q, col_s
 
 
-def mx_dequantize_rows(q, s):
-    from .formats import e4m3_decode, e8m0_value
+def mx_dequantize_rows(q, s, fmt: str = "e4m3"):
+    from .formats import e8m0_value, fp8_decode
     R, C = q.shape
-    vals = e4m3_decode(q)
+    vals = fp8_decode(q, fmt)
     sc = np.repeat(e8m0_value(s), MX_BLOCK, axis=1)[:, :C]
     return vals * sc
 
 
-def group_gemm_mx(aq, as_, counts, bq, bs, dtype=np.float64):
+def group_gemm_mx(aq, as_, counts, bq, bs, dtype=np.float64, a_fmt: str = "e4m3"):
     """MXFP8 x MXFP8 GroupGemm, as the exact dequantize-then-multiply definition.
 
-    aq [M][K] e4m3 codes with as_ [M][K/32] row scales; bq [E][N][K] e4m3 codes
-    (the weight stored K-contiguous per output column) with bs [E][N][K/32].
+    aq [M][K] e4m3 codes (e5m2 with ``a_fmt="e5m2"``, e.g. a gradient) with
+    as_ [M][K/32] row scales; bq [E][N][K] e4m3 codes (the weight stored
+    K-contiguous per output column) with bs [E][N][K/32].
     out_e = bf16( (deq A_e) @ (deq B_e)^T ).
     """
     counts = np.asarray(counts, dtype=np.int64)
@@ -582,7 +584,7 @@ def group_gemm_mx(aq, as_, counts, bq, bs, dtype=np.float64):
         a, b = int(off[e]), int(off[e + 1])
         if b == a:
             continue
-        A = mx_dequantize_rows(aq[a:b], as_[a:b]).astype(dtype)
+        A = mx_dequantize_rows(aq[a:b], as_[a:b], a_fmt).astype(dtype)
         B = mx_dequantize_rows(bq[e], bs[e]).astype(dtype)
         out[a:b] = f64_to_bf16_bits((A @ B.T).astype(np.float64))
     return out

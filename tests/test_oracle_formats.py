@@ -245,3 +245,94 @@ def test_mx_block_edge_cases():
     b = np.full(32, 448.0 * 4)
     codes, byte = F.mx_quantize_block(b)
     assert byte == 127 + 2 and np.all(codes == 0x7E)
+
+
+# ------------------------------------------------------------------ e5m2 (gradient format)
+_CODES5 = np.array([c for c in range(256) if np.isfinite(F.e5m2_decode_table()[c])])
+_VALS5 = F.e5m2_decode_table()[_CODES5]
+
+
+def test_e5m2_table_matches_ocp_values():
+    table = F.e5m2_decode_table()
+    for item in _golden()["e5m2"]:
+        code = int(item["code"], 16)
+        v = float(item["value"])
+        if math.isnan(v):
+            assert math.isnan(table[code])
+        else:
+            assert table[code] == v, (item, table[code])
+
+
+def test_e5m2_table_structure():
+    table = F.e5m2_decode_table()
+    assert len(_VALS5) == 248                      # 256 minus 2 infinities and 6 NaNs
+    pos = np.sort(np.unique(np.abs(_VALS5)))
+    assert pos[-1] == 57344.0 and pos[1] == 2.0 ** -16
+    assert np.isinf(table[0x7C]) and np.isinf(table[0xFC])
+
+
+def _e5m2_bruteforce(x: float):
+    fx = Fraction(x)
+    if abs(x) > 57344:
+        return math.copysign(57344.0, x)
+    d = [abs(Fraction(v) - fx) for v in _VALS5]
+    best = min(d)
+    idx = [i for i, di in enumerate(d) if di == best]
+    vals = {float(_VALS5[i]) for i in idx}
+    if len(vals) == 1:
+        return vals.pop()
+    return [float(_VALS5[i]) for i in idx if _CODES5[i] % 2 == 0][0]
+
+
+def test_e5m2_rne_dense_sweep():
+    rng = np.random.default_rng(23)
+    pos = np.sort(np.unique(np.abs(_VALS5)))
+    mids = (pos[:-1] + pos[1:]) / 2
+    xs = np.concatenate([rng.uniform(-57344, 57344, 1500), rng.uniform(-2.0 ** -12, 2.0 ** -12, 1500),
+                         rng.uniform(-8, 8, 1500), mids, -mids,
+                         _VALS5 + np.ldexp(np.abs(_VALS5), -6), _VALS5 - np.ldexp(np.abs(_VALS5), -6)])
+    got = F.e5m2_round(xs)
+    for x, g in zip(xs, got):
+        assert g == _e5m2_bruteforce(float(x)), x
+
+
+def test_e5m2_encode_decode_roundtrip_all_codes():
+    assert np.array_equal(F.f64_to_e5m2(_VALS5), _CODES5.astype(np.uint8))
+    assert F.f64_to_e5m2(np.array([1e9]))[0] == 0x7B        # saturates (finite)
+    assert F.f64_to_e5m2(np.array([-1e-12]))[0] == 0x80     # rounds to -0
+
+
+def test_e5m2_torch_cast_cross_check_in_range():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e5m2"):
+        pytest.skip("torch has no float8_e5m2")
+    rng = np.random.default_rng(24)
+    x = np.concatenate([rng.uniform(-57000, 57000, 10000), rng.uniform(-1, 1, 10000),
+                        rng.uniform(-1e-4, 1e-4, 5000)]).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(F.f64_to_e5m2(x.astype(np.float64)), t)
+
+
+def test_e5m2_scale_exponent_against_exact_ceil_log2():
+    rng = np.random.default_rng(25)
+    b = 57344.0 * np.exp2(np.arange(-120, 100, dtype=np.float64))
+    amax = np.concatenate([np.abs(rng.standard_normal(2000)) * np.exp2(rng.integers(-120, 120, 2000)),
+                           b, np.nextafter(b, np.inf), np.nextafter(b, 0)])
+    amax = F.bf16_round(amax)
+    amax = amax[amax > 0]
+    E = F.mx_scale_exponent(amax, "e5m2")
+    for a, e in zip(amax, E):
+        want = max(-127, min(127, _ceil_log2_fraction(Fraction(float(a)) / 57344)))
+        assert e == want, (a, e, want)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_mx_block_e5m2_roundtrip_within_half_ulp(seed):
+    rng = np.random.default_rng(seed + 40)
+    v = F.bf16_round(rng.standard_normal(32) * np.exp2(rng.integers(-30, 30)))
+    codes, byte = F.mx_quantize_block(v, "e5m2")
+    X = F.e8m0_value(byte)
+    back = F.e5m2_decode(codes) * X
+    assert np.max(np.abs(v)) / X <= 57344
+    p = np.maximum(np.floor(np.log2(np.maximum(np.abs(v) / X, 2.0 ** -30))), -14)
+    assert np.all(np.abs(back - v) <= 0.5 * np.exp2(p - 2) * X + 0.0)
