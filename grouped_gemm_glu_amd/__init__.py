@@ -25,7 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 # ----------------------------------------------------------------------------- ABI mirror
 MOE_OK = 0
 ACT = {"swiglu": 0, "geglu": 1, "geglu_tanh": 2, "srelu": 3}
-DT_BF16, DT_MXFP8 = 0, 1
+DT_BF16, DT_MXFP8, DT_MXFP8_E5M2 = 0, 1, 2
 B_KN, B_NK, B_PACKED = 0, 1, 2
 
 
@@ -41,7 +41,7 @@ class EpilogueT(ctypes.Structure):
 
 class MxOutT(ctypes.Structure):
     _fields_ = [("row_q", ctypes.c_void_p), ("row_s", ctypes.c_void_p),
-                ("col_q", ctypes.c_void_p), ("col_s", ctypes.c_void_p)]
+                ("col_q", ctypes.c_void_p), ("col_s", ctypes.c_void_p), ("e5m2", ctypes.c_int32)]
 
 
 class GroupsT(ctypes.Structure):
@@ -150,8 +150,9 @@ def groups(counts, M_cap: int, offsets_out=None, status_out=None) -> GroupsT:
                          _ptr(status_out)), counts, offsets_out, status_out)
 
 
-def mx_out(row_q=None, row_s=None, col_q=None, col_s=None) -> MxOutT:
-    return _keep(MxOutT(_ptr(row_q), _ptr(row_s), _ptr(col_q), _ptr(col_s)),
+def mx_out(row_q=None, row_s=None, col_q=None, col_s=None, e5m2: bool = False) -> MxOutT:
+    """MXFP8 output buffers; ``e5m2`` selects e5m2 element codes (gradients)."""
+    return _keep(MxOutT(_ptr(row_q), _ptr(row_s), _ptr(col_q), _ptr(col_s), 1 if e5m2 else 0),
                  row_q, row_s, col_q, col_s)
 
 

@@ -42,6 +42,7 @@ moe_status_t check_mx(const moe_mx_out_t* mx) {
   if (!mx) return MOE_OK;
   if ((mx->row_q == nullptr) != (mx->row_s == nullptr)) return MOE_ERR_NULL;
   if ((mx->col_q == nullptr) != (mx->col_s == nullptr)) return MOE_ERR_NULL;
+  if (mx->e5m2 != 0 && mx->e5m2 != 1) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -86,6 +87,7 @@ void fill_mx(GemmArgs* a, const moe_mx_out_t* mx, int cols, const moe_groups_t* 
   a->col_q = mx ? mx->col_q : nullptr;
   a->col_s = mx ? mx->col_s : nullptr;
   a->mx_cols = cols;
+  a->mx_e5 = mx ? mx->e5m2 : 0;
   a->col_s_ld = (g->M_cap + 31) / 32 + g->E;
 }
 
@@ -386,9 +388,10 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t
   if (!a_op || !b_op || !a_op->data || !b_op->data) return MOE_ERR_NULL;
   if ((st = check_mx(mx)) != MOE_OK) return st;
   if (N < 64 || N % 64 != 0 || K < 64 || K % 64 != 0) return MOE_ERR_SHAPE;
-  const bool mx_in = a_op->dtype == MOE_DT_MXFP8 || b_op->dtype == MOE_DT_MXFP8;
-  if (mx_in) {   // MXFP8 x MXFP8 only, weight from moe_pack_weight_mx
-    if (a_op->dtype != MOE_DT_MXFP8 || b_op->dtype != MOE_DT_MXFP8 ||
+  const bool a_e5 = a_op->dtype == MOE_DT_MXFP8_E5M2;
+  const bool mx_in = a_op->dtype == MOE_DT_MXFP8 || a_e5 || b_op->dtype != MOE_DT_BF16;
+  if (mx_in) {   // MXFP8 (A e4m3 or e5m2) x MXFP8 e4m3 only, weight from moe_pack_weight_mx
+    if ((a_op->dtype != MOE_DT_MXFP8 && !a_e5) || b_op->dtype != MOE_DT_MXFP8 ||
         b_op->layout != MOE_B_PACKED)
       return MOE_ERR_UNSUPPORTED;
     if (!a_op->scales || !b_op->scales) return MOE_ERR_NULL;
@@ -417,7 +420,7 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t
     a.ldb = K;
     a.b_estride = (long long)moe_packed_mx_weight_bytes(1, N, K);   // bytes = elements
     int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-    return launch_group_gemm_mx(a, grid, (hipStream_t)stream);
+    return launch_group_gemm_mx(a, a_e5, grid, (hipStream_t)stream);
   }
   int blay;
   switch (b_op->layout) {
@@ -497,14 +500,16 @@ moe_status_t moe_mxfp8_quantize(const void* v, int R, int C, const moe_groups_t*
   const int E = groups ? groups->E : 0;
   if (mx->row_q && R > 0) {
     hipLaunchKernelGGL(mx_rows_kernel, dim3(cus * 8), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(v), R, C, counts, E, mx->row_q, mx->row_s);
+                       static_cast<const uint16_t*>(v), R, C, counts, E, mx->row_q, mx->row_s,
+                       mx->e5m2);
   }
   if (mx->col_q && R > 0) {
     int s_ld = (R + 31) / 32 + (groups ? E : 0);
     long long by = (long long)(R + 31) / 32 + E;
     int gy = (int)(by < 65535 ? by : 65535);
     hipLaunchKernelGGL(mx_cols_kernel, dim3((C + 255) / 256, gy), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(v), R, C, counts, E, mx->col_q, mx->col_s, s_ld);
+                       static_cast<const uint16_t*>(v), R, C, counts, E, mx->col_q, mx->col_s, s_ld,
+                       mx->e5m2);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

@@ -227,28 +227,6 @@ __global__ __launch_bounds__(256) void glu_unfused_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- MXFP8 quantize
-__device__ __forceinline__ uint8_t mx_block_quant(const float* v, int nvalid, uint32_t* w) {
-  float amax = 0.0f;
-  bool has_nan = false;
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (i < nvalid) {
-      amax = fmaxf(amax, fabsf(v[i]));
-      if (v[i] != v[i]) has_nan = true;
-    }
-  int E = has_nan ? 128 : mx_scale_exponent(amax);
-  if (E == 128) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = 0x7F7F7F7Fu;
-    return 0xFF;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    w[i] = e4m3x4(ldexpf(v[4 * i], -E), ldexpf(v[4 * i + 1], -E), ldexpf(v[4 * i + 2], -E),
-                  ldexpf(v[4 * i + 3], -E));
-  return e8m0_byte(E);
-}
-
 __device__ __forceinline__ void store_q32(uint8_t* dst, const uint32_t* w, int nvalid) {
   uintptr_t a = reinterpret_cast<uintptr_t>(dst);
   if (nvalid == 32 && (a & 15) == 0) {
@@ -264,7 +242,7 @@ __device__ __forceinline__ void store_q32(uint8_t* dst, const uint32_t* w, int n
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ v, int R, int C,
                                                       const int* __restrict__ counts, int E,
                                                       uint8_t* __restrict__ q,
-                                                      uint8_t* __restrict__ s) {
+                                                      uint8_t* __restrict__ s, int e5) {
   __shared__ GroupScan gs;
   int Ruse = R;
   if (counts) {
@@ -289,7 +267,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
       }
     }
     uint32_t w[8];
-    uint8_t sb = mx_block_quant(x, 32, w);
+    uint8_t sb = mx_quant32(x, 32, w, e5 != 0);
     store_q32(q + (long long)r * C + cb * 32, w, 32);
     s[(long long)r * nb + cb] = sb;
   }
@@ -301,7 +279,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
 __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict__ v, int R, int C,
                                                       const int* __restrict__ counts, int E,
                                                       uint8_t* __restrict__ q,
-                                                      uint8_t* __restrict__ s, int s_ld) {
+                                                      uint8_t* __restrict__ s, int s_ld, int e5) {
   __shared__ GroupScan gs;
   int nblocks;
   if (counts) {
@@ -331,7 +309,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 32; ++i) x[i] = (i < nvalid) ? bf16_to_f32(v[(long long)(r0 + i) * C + c]) : 0.0f;
     uint32_t w[8];
-    uint8_t sb = mx_block_quant(x, nvalid, w);
+    uint8_t sb = mx_quant32(x, nvalid, w, e5 != 0);
     store_q32(q + (long long)c * R + r0, w, nvalid);
     s[(long long)c * s_ld + b] = sb;
   }
@@ -369,7 +347,7 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(const uint16_t* __restrict
       v[t] = n_pk < N ? bf16_to_f32(src_kn ? W[k * N + n] : W[(long long)n * K + k]) : 0.0f;
     }
     uint32_t w[8];
-    sword |= (uint32_t)mx_block_quant(v, 32, w) << (8 * b);
+    sword |= (uint32_t)mx_quant32(v, 32, w, false) << (8 * b);
     *reinterpret_cast<uint4*>(row + (((2 * b) ^ pack_key(r)) << 4)) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint4*>(row + (((2 * b + 1) ^ pack_key(r)) << 4)) = make_uint4(w[4], w[5], w[6], w[7]);
   }

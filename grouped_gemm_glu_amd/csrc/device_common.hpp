@@ -36,16 +36,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---------------------------------------------------------------- MXFP8
 // Block-scale exponent for a block maximum (OCP MX, E8M0 scale): the smallest
-// E with amax / 2^E <= 448 (the largest e4m3fn value, 1.75 * 2^8), clamped to
-// [-127, 127]; an all-zero block gives -127; a non-finite amax gives 128 (the
-// NaN scale byte 0xFF).  With amax = 1.m * 2^e, amax <= 1.75 * 2^(E+8) holds
-// for E = e - 8 exactly when the mantissa fraction is <= 0.75.
-__device__ __forceinline__ int mx_scale_exponent(float amax) {
+// E with amax / 2^E <= vmax = 1.75 * 2^vexp, the largest element value (e4m3fn:
+// 448, vexp 8; e5m2: 57344, vexp 15), clamped to [-127, 127]: amax = 1.f *
+// 2^e needs 2^(e - vexp) when f <= 1.75, else 2^(e - vexp + 1).  Zero or an
+// fp32 subnormal amax gives -127, a non-finite one 128 (NaN scale).
+__device__ __forceinline__ int mx_scale_exponent(float amax, int vexp = 8) {
   uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
   if (u >= 0x7F800000u) return 128;
   uint32_t ebits = u >> 23;
-  if (ebits == 0) return -127;                 // zero or subnormal: ceil(log2(amax/448)) < -127
-  int E = static_cast<int>(ebits) - 127 - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  if (ebits == 0) return -127;                 // zero or subnormal: ceil(log2(amax/vmax)) < -127
+  int E = static_cast<int>(ebits) - 127 - vexp + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
   return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
@@ -82,6 +82,41 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// Four fp32 values -> four e5m2 codes (byte k = value k) with v_cvt_pk_bf8_f32
+// (round to nearest even; the callers keep |x| <= 57344).
+__device__ __forceinline__ uint32_t e5m2x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true));
+}
+
+// Quantises one 32-value MX block (nvalid of the values real; the others must
+// be finite and are encoded too) to e4m3fn or, with e5, e5m2 codes (4 per
+// word of w) and returns its E8M0 scale byte.  A NaN among the valid values
+// makes the whole block NaN (scale 0xFF, every code 0x7F).
+__device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32_t* w, bool e5) {
+  float amax = 0.0f;
+  bool has_nan = false;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (i < nvalid) {
+      amax = fmaxf(amax, fabsf(v[i]));   // fmaxf drops NaN: tracked separately
+      if (v[i] != v[i]) has_nan = true;
+    }
+  const int E = has_nan ? 128 : mx_scale_exponent(amax, e5 ? 15 : 8);
+  if (E == 128) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0x7F7F7F7Fu;
+    return 0xFF;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = ldexpf(v[4 * i], -E), b = ldexpf(v[4 * i + 1], -E);
+    const float c = ldexpf(v[4 * i + 2], -E), d = ldexpf(v[4 * i + 3], -E);
+    w[i] = e5 ? e5m2x4(a, b, c, d) : e4m3x4(a, b, c, d);
+  }
+  return e8m0_byte(E);
 }
 
 // ---------------------------------------------------------------- activations

@@ -79,8 +79,9 @@ struct Stg {
 enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4, EPI_DGLU_G = 5 };
 enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 // operand element type: bf16, or MXFP8 (OCP e4m3 codes with one E8M0 scale
-// per 32 consecutive K values, consumed by the block-scaled MFMA)
-enum { AT_BF16 = 0, AT_MX = 1 };
+// per 32 consecutive K values, consumed by the block-scaled MFMA); AT_MX_A5:
+// the same with e5m2 codes for A (a gradient) and e4m3 for B
+enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2 };
 
 struct GemmArgs {
   const uint16_t* A;        // [M_cap][K] grouped rows, K contiguous
@@ -101,6 +102,7 @@ struct GemmArgs {
   uint8_t* col_q;
   uint8_t* col_s;
   int mx_cols;              // columns of the quantised output (row length of row_q)
+  int mx_e5;                // 1: the quantised copies hold e5m2 codes, 0: e4m3fn
   int col_s_ld;             // ceil(M_cap/32) + E
   int ntiles_n;
   // MXFP8 operands: A scales [M_cap][K/32]; B scales in the tile-blocked
@@ -172,30 +174,6 @@ __device__ __forceinline__ void store_bytes(uint8_t* dst, const uint32_t* w, int
   }
 }
 
-// Quantises 32 values (nvalid of them real) to e4m3 with one E8M0 scale.
-__device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32_t* w) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (i < nvalid) amax = fmaxf(amax, fabsf(v[i]));
-  // fmaxf drops NaN; a NaN anywhere in the block makes the block NaN
-  bool has_nan = false;
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (i < nvalid && v[i] != v[i]) has_nan = true;
-  int E = has_nan ? 128 : mx_scale_exponent(amax);
-  if (E == 128) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = 0x7F7F7F7Fu;
-    return 0xFF;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    w[i] = e4m3x4(ldexpf(v[4 * i], -E), ldexpf(v[4 * i + 1], -E), ldexpf(v[4 * i + 2], -E),
-                  ldexpf(v[4 * i + 3], -E));
-  return e8m0_byte(E);
-}
-
 // MXFP8 of a staged bf16 tile: stg[r][c] (row stride ld elements) holds rows
 // [0, rows_valid) x cols [0, ncols) of the output, whose global position is
 // grouped row grow0 + r, column col0 + c.  row-wise: blocks along the row;
@@ -223,7 +201,7 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
         }
       }
       uint32_t w[8];
-      uint8_t sb = mx_quant32(v, 32, w);
+      uint8_t sb = mx_quant32(v, 32, w, p.mx_e5 != 0);
       long long grow = grow0 + r;
       int gc = col0 + cb * 32;
       store_bytes(p.row_q + grow * p.mx_cols + gc, w, 32);
@@ -241,7 +219,7 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(stg.row(rb * 32 + i)[c]);
       uint32_t w[8];
-      uint8_t sb = mx_quant32(v, nvalid, w);
+      uint8_t sb = mx_quant32(v, nvalid, w, p.mx_e5 != 0);
       long long gc = col0 + c;
       store_bytes(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[gc * p.col_s_ld + scol0 + rb] = sb;
@@ -343,7 +321,10 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   // (4 k-steps of v_mfma_f32_32x32x16_bf16) or 128 e4m3 (2 k-steps of
   // v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8 stages also carry the tile's
   // E8M0 scales: 256 rows x 4 bytes for A and for B after the two tiles.
-  constexpr bool MXT = AT == AT_MX;
+  constexpr bool MXT = AT != AT_BF16;
+  // block-scaled MFMA format codes (0 = e4m3, 1 = e5m2) of the weight (the
+  // first source) and of the activations (the second source)
+  constexpr int FMT_A = AT == AT_MX_A5 ? 1 : 0;
   constexpr int ESZ = MXT ? 1 : 2;            // operand element bytes
   constexpr int KSTEPS = MXT ? 2 : 4;         // k-steps per K-tile
   static_assert(!MXT || (BLAY == BL_PACKED && (EPI == EPI_STORE || EPI == EPI_GLU ||
@@ -677,10 +658,10 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
             const int sB = (int)(scb[sset][j] >> sh), sA = (int)(sca[sset][i] >> sh);
             if (ks == 0)
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  bfx[buf][j], afx[buf][i], acc[i][j], 0, 0, 0, sB, 0, sA);
+                  bfx[buf][j], afx[buf][i], acc[i][j], 0, FMT_A, 0, sB, 0, sA);
             else
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  bfx[buf][j], afx[buf][i], acc[i][j], 0, 0, 2, sB, 2, sA);
+                  bfx[buf][j], afx[buf][i], acc[i][j], 0, FMT_A, 2, sB, 2, sA);
           }
         }
     };

@@ -14,8 +14,9 @@ moe_status_t launch_group_gemm_fwd(int epi, int blay, const GemmArgs& args, int 
                                    hipStream_t stream);
 moe_status_t launch_group_gemm_bwd(int epi, int blay, const GemmArgs& args, int grid,
                                    hipStream_t stream);
-// MXFP8 x MXFP8 GroupGemm (packed MXFP8 weight, bf16 output)
-moe_status_t launch_group_gemm_mx(const GemmArgs& args, int grid, hipStream_t stream);
+// MXFP8 x MXFP8 GroupGemm (packed MXFP8 weight, bf16 output); a_e5: A holds
+// e5m2 codes
+moe_status_t launch_group_gemm_mx(const GemmArgs& args, bool a_e5, int grid, hipStream_t stream);
 
 // Kernels whose epilogue applies the activation exist once per activation
 // (gemm_act_fwd.hip and gemm_act_bwd.hip are compiled once per value of

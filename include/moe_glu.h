@@ -111,12 +111,16 @@ typedef struct {
  *                                          row; group e's scales start at column
  *                                          sum_{j<e} ceil(m_j/32)
  * Any pointer may be NULL (that copy is skipped); row_q/row_s and col_q/col_s
- * go in pairs.  No alignment requirement.  (host struct) */
+ * go in pairs.  No alignment requirement.
+ * e5m2 = 1 selects OCP e5m2 elements instead (the gradient format of an
+ * MXFP8 recipe: largest value 57344 = 1.75 * 2^15, the scale rule with 57344
+ * in place of 448); 0 = e4m3fn.  (host struct) */
 typedef struct {
   uint8_t* row_q;
   uint8_t* row_s;
   uint8_t* col_q;
   uint8_t* col_s;
+  int32_t e5m2;
 } moe_mx_out_t;
 
 /* Expert groups.  The counts are the ONLY copy of the group sizes and stay in
@@ -134,7 +138,8 @@ typedef struct {
 /* Operand descriptor of moe_group_gemm_quant. */
 typedef enum {
   MOE_DT_BF16 = 0,
-  MOE_DT_MXFP8 = 1          /* e4m3fn bytes + E8M0 scales, 32-blocks along K */
+  MOE_DT_MXFP8 = 1,         /* e4m3fn bytes + E8M0 scales, 32-blocks along K */
+  MOE_DT_MXFP8_E5M2 = 2     /* e5m2 bytes + E8M0 scales (a gradient, e.g. dgu for dX); A only */
 } moe_dtype_t;
 
 typedef enum {

@@ -212,6 +212,15 @@ def f64_to_e5m2(x) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def e5m2_ulp(v) -> np.ndarray:
+    """Spacing of e5m2 numbers at |v| (|v| <= 57344): 2^(max(floor(log2|v|),-14)-2)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    p = np.full(a.shape, E5M2_MIN_NORMAL_EXP, dtype=np.int64)
+    nz = a > 0
+    p[nz] = np.maximum(_floor_log2(a[nz]), E5M2_MIN_NORMAL_EXP)
+    return np.ldexp(1.0, p - 2)
+
+
 FP8_FORMATS = {"e4m3": (E4M3_MAX, 8), "e5m2": (E5M2_MAX, 15)}   # (largest value, its exponent)
 
 

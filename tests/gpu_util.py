@@ -142,11 +142,12 @@ def packed_mx_layout(q_nk: np.ndarray, s_nk: np.ndarray):
     return out.reshape(-1), np.ascontiguousarray(sc).reshape(-1)
 
 
-def _mx_block_check(gq, gs, gv, rq, rs, rv, what, max_flip=0.02):
+def _mx_block_check(gq, gs, gv, rq, rs, rv, what, max_flip=0.02, fmt="e4m3"):
     """Blocks laid out as [..., nblk, 32] (codes, values) and [..., nblk] (scales).
     Blocks whose 32 source values are bit-identical on both sides must give
     identical bytes; the others (a bf16 rounding flip upstream) must still
-    dequantise to within one e4m3 step of the oracle value plus the flip."""
+    dequantise to within one element step (e4m3 or e5m2) of the oracle value
+    plus the flip."""
     same = np.all(gv == rv, axis=-1)
     assert np.array_equal(gq[same], rq[same]), f"{what}: codes differ on identical blocks"
     assert np.array_equal(gs[same], rs[same]), f"{what}: scales differ on identical blocks"
@@ -154,34 +155,35 @@ def _mx_block_check(gq, gs, gv, rq, rs, rv, what, max_flip=0.02):
     assert frac <= max_flip, f"{what}: {frac:.3%} of blocks have different source values"
     if np.any(~same):
         scale = F.e8m0_value(gs[~same])[..., None]
-        deq = F.e4m3_decode(gq[~same]) * scale
+        deq = F.fp8_decode(gq[~same], fmt) * scale
         ref = F.bf16_bits_to_f64(rv[~same])
         gval = F.bf16_bits_to_f64(gv[~same])
-        bound = F.e4m3_ulp(np.abs(ref) / scale) * scale + np.abs(gval - ref)
+        ulp = F.e4m3_ulp if fmt == "e4m3" else F.e5m2_ulp
+        bound = ulp(np.abs(ref) / scale) * scale + np.abs(gval - ref)
         assert np.all(np.abs(deq - ref) <= bound), f"{what}: flipped blocks out of bound"
 
 
-def assert_mx_rows(gpu_q, gpu_s, gpu_vals, ref_vals, what="mx rows", max_flip=0.02):
+def assert_mx_rows(gpu_q, gpu_s, gpu_vals, ref_vals, what="mx rows", max_flip=0.02, fmt="e4m3"):
     """Row-wise MXFP8 copy of a GPU bf16 tensor against the oracle's
     quantisation of the ORACLE's values (ref_vals); the GPU values only pick
     which blocks must match byte for byte.  max_flip bounds the fraction of
     blocks whose source values differ (a GEMM output whose bf16 rounding flips
     often, like dGLU's products, needs a large one)."""
     from oracle import moe as O
-    rq, rs = O.mx_quantize_rows(ref_vals)
+    rq, rs = O.mx_quantize_rows(ref_vals, fmt)
     R, C = ref_vals.shape
     nb = C // 32
     _mx_block_check(gpu_q.reshape(R, nb, 32), gpu_s.reshape(R, nb), gpu_vals.reshape(R, nb, 32),
                     rq.reshape(R, nb, 32), rs.reshape(R, nb), ref_vals.reshape(R, nb, 32), what,
-                    max_flip)
+                    max_flip, fmt)
 
 
 def assert_mx_cols(gpu_q, gpu_s, gpu_vals, ref_vals, counts, m_cap, what="mx cols",
-                   max_flip=0.02):
+                   max_flip=0.02, fmt="e4m3"):
     """Transposed MXFP8 copy (32-row blocks restarting at each group) against
     the oracle's quantisation of the oracle's values, as in assert_mx_rows."""
     from oracle import moe as O
-    rq, rs = O.mx_quantize_cols(ref_vals, counts, m_cap=m_cap)
+    rq, rs = O.mx_quantize_cols(ref_vals, counts, m_cap=m_cap, fmt=fmt)
     so = O.mx_scale_col_offsets(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     C = ref_vals.shape[1]
@@ -201,4 +203,4 @@ def assert_mx_cols(gpu_q, gpu_s, gpu_vals, ref_vals, counts, m_cap, what="mx col
         rqe = np.concatenate([rq[:, a:b], np.zeros((C, pad), np.uint8)], axis=1).reshape(C, nb, 32)
         _mx_block_check(gq, gpu_s[:, so[e]:so[e] + nb], blocks(gpu_vals[a:b]),
                         rqe, rs[:, so[e]:so[e] + nb], blocks(ref_vals[a:b]), f"{what} group {e}",
-                        max_flip)
+                        max_flip, fmt)
