@@ -276,7 +276,8 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
   if (!xg || !w1_packed || !ep) return MOE_ERR_NULL;
   if ((st = check_mx(mx)) != MOE_OK) return st;
   if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
-  if (ep->gated != 1) return MOE_ERR_UNSUPPORTED;
+  if (ep->gated != 0 && ep->gated != 1) return MOE_ERR_UNSUPPORTED;
+  const bool gated = ep->gated == 1;
   if (!aligned16(xg) || !aligned16(w1_packed) || (y && !aligned16(y)) ||
       (preact && !aligned16(preact)))
     return MOE_ERR_ALIGN;
@@ -288,18 +289,21 @@ moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
   fill_groups(&a, groups);
   a.A = static_cast<const uint16_t*>(xg);
   a.B = static_cast<const uint16_t*>(w1_packed);
-  a.b_estride = (long long)moe_packed_w1_bytes(1, H, I) / 2;
+  // gated: the gate/up-repacked W1 (N = 2I packed columns); non-gated: W1
+  // [E][H][I] packed by moe_pack_weight (N = I plain columns)
+  a.b_estride = gated ? (long long)moe_packed_w1_bytes(1, H, I) / 2
+                      : (long long)moe_packed_weight_bytes(1, I, H) / 2;
   a.ldb = H;
-  a.N = 2 * I;
+  a.N = gated ? 2 * I : I;
   a.K = H;
   a.I = I;
   a.C = static_cast<uint16_t*>(y);
   a.preact = static_cast<uint16_t*>(preact);
   fill_mx(&a, mx, I, groups);
-  a.ntiles_n = (2 * I + GM_BN - 1) / GM_BN;
+  a.ntiles_n = (a.N + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
-  return launch_activation_kernel((a.row_q || a.col_q) ? KIND_GLU_MXO : KIND_GLU, a, grid,
-                                  (hipStream_t)stream);
+  const int kind = !gated ? KIND_ACT : (a.row_q || a.col_q) ? KIND_GLU_MXO : KIND_GLU;
+  return launch_activation_kernel(kind, a, grid, (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_glu_fwd_mx(const moe_operand_t* xg, const moe_groups_t* groups,
@@ -350,7 +354,9 @@ moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, i
   if (!dy2 || !w2 || !w2->data || !preact || !ep) return MOE_ERR_NULL;
   if ((st = check_mx(mx)) != MOE_OK) return st;
   if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
-  if (ep->gated != 1 || w2->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((ep->gated != 0 && ep->gated != 1) || w2->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool gated = ep->gated == 1;
+  if (!gated && (ep->dbias_out || ep->drow_scale_out)) return MOE_ERR_UNSUPPORTED;
   if (w2->layout != MOE_B_NK && w2->layout != MOE_B_PACKED) return MOE_ERR_UNSUPPORTED;
   if (!aligned16(dy2) || !aligned16(w2->data) || !aligned16(preact) || (dgu && !aligned16(dgu)))
     return MOE_ERR_ALIGN;
@@ -371,13 +377,14 @@ moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, i
   a.I = I;
   a.C = static_cast<uint16_t*>(dgu);
   a.preact = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
-  fill_mx(&a, mx, 2 * I, groups);
+  fill_mx(&a, mx, gated ? 2 * I : I, groups);
   a.ntiles_n = (I + GM_BN - 1) / GM_BN;
   int grid = persistent_grid(cus, cu_margin, groups->M_cap, groups->E, a.ntiles_n);
   const bool grads = a.ep.dbias_out || a.ep.drs_out;
-  return launch_activation_kernel(grads ? (w2_packed ? KIND_DGLU_G_PACKED : KIND_DGLU_G_NK)
-                                        : (w2_packed ? KIND_DGLU_PACKED : KIND_DGLU_NK),
-                                  a, grid, (hipStream_t)stream);
+  const int kind = !gated ? (w2_packed ? KIND_DACT_PACKED : KIND_DACT_NK)
+                   : grads ? (w2_packed ? KIND_DGLU_G_PACKED : KIND_DGLU_G_NK)
+                           : (w2_packed ? KIND_DGLU_PACKED : KIND_DGLU_NK);
+  return launch_activation_kernel(kind, a, grid, (hipStream_t)stream);
 }
 
 moe_status_t moe_group_gemm_quant(const moe_operand_t* a_op, const moe_operand_t* b_op, int N,

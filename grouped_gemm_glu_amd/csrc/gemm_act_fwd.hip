@@ -1,6 +1,7 @@
 // FC1 + GLU kernels for one activation (MOE_ACT, a moe_act_t value given on
 // the compile line; the build compiles this file once per activation): bf16
-// or MXFP8 operands on the packed W1, with or without MXFP8 outputs.
+// or MXFP8 operands on the packed W1, with or without MXFP8 outputs; and the
+// non-gated form on the plain packed W1.
 #include "internal.hpp"
 
 #ifndef MOE_ACT
@@ -25,6 +26,7 @@ moe_status_t MOE_CAT(launch_act_fwd_, MOE_ACT)(int kind, const GemmArgs& a, int 
     case KIND_GLU_MXO: launch_glu<EPI_GLU_MX, AT_BF16>(a, grid, s); break;
     case KIND_MXIN_GLU: launch_glu<EPI_GLU, AT_MX>(a, grid, s); break;
     case KIND_MXIN_GLU_MXO: launch_glu<EPI_GLU_MX, AT_MX>(a, grid, s); break;
+    case KIND_ACT: launch_glu<EPI_ACT, AT_BF16>(a, grid, s); break;
     default: return MOE_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;

@@ -76,7 +76,11 @@ struct Stg {
 // EPI_DGLU_G: EPI_DGLU that also adds the gradients of the epilogue's own
 // parameters (bias, row scale); a kernel of its own, so that the plain
 // backward epilogue keeps its register allocation.
-enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4, EPI_DGLU_G = 5 };
+// EPI_ACT / EPI_DACT: the non-gated activation (N = I columns, no gate/up
+// pairs): forward y = a(z) * row_scale with z = acc + bias (z optionally
+// saved), backward dz = G * row_scale * a'(z) from the saved z.
+enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4, EPI_DGLU_G = 5,
+       EPI_ACT = 6, EPI_DACT = 7 };
 enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 // operand element type: bf16, or MXFP8 (OCP e4m3 codes with one E8M0 scale
 // per 32 consecutive K values, consumed by the block-scaled MFMA); AT_MX_A5:
@@ -950,6 +954,90 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       } else if (p.preact) {
         store_preact();
       }
+    } else if (EPI == EPI_ACT || EPI == EPI_DACT) {
+      // Per element, from the accumulator of output column n (plain order):
+      // forward  z = acc + bias[n], y = bf16(a(z) * rs), staged and stored like
+      //          the plain GroupGemm output (with its MXFP8 copies), then z in
+      //          a second staged round when the pre-activation is kept;
+      // backward dz = bf16(acc * rs * a'(z)), z (bf16) read back 8 bytes per
+      //          lane group, all 16 of a row block's loads in flight together.
+      constexpr bool FWD = EPI == EPI_ACT;
+      const int ld = GM_STG_LD_256;
+      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR};
+      const int cvalid_n = min(GM_BN, p.N - n0);
+      const uint16_t* bias_e = (FWD && p.ep.bias) ? p.ep.bias + (long long)e * p.N + n0 : nullptr;
+      const rsrc_t rsZ = make_rsrc(p.preact + (long long)row0 * p.N,
+                                   FWD ? 0 : (long long)rows_valid * p.N * 2);
+      float ymax = 0.0f;
+      auto stage_round = [&](auto rc) {   // 0: y (forward) or dz (backward); 1: z (forward)
+        constexpr int RD = decltype(rc)::value;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int m = wm * HR + 32 * i + lm;
+          uint2 zw[4][4];
+          if constexpr (!FWD) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint32_t col = (uint32_t)(n0 + wn * 128 + 32 * j + 8 * q + ln);
+                zw[j][q] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                    rsZ, ((uint32_t)m * (uint32_t)p.N + col) * 2u, 0, 0));
+              }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int n = wn * 128 + 32 * j + 8 * q + ln;
+              float o[4];
+              if constexpr (FWD) {
+                uint2 bw = make_uint2(0u, 0u);
+                if (bias_e && n < cvalid_n) bw = *reinterpret_cast<const uint2*>(bias_e + n);
+                const float bz[4] = {__uint_as_float(bw.x << 16), __uint_as_float(bw.x & 0xFFFF0000u),
+                                     __uint_as_float(bw.y << 16), __uint_as_float(bw.y & 0xFFFF0000u)};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                  const float z = acc[i][j][4 * q + s2] + bz[s2];
+                  o[s2] = RD == 0 ? act_fwd_t<ACT>(z, p.ep.alpha) * rsc[i] : z;
+                }
+              } else {
+                const float zv[4] = {__uint_as_float(zw[j][q].x << 16), __uint_as_float(zw[j][q].x & 0xFFFF0000u),
+                                     __uint_as_float(zw[j][q].y << 16), __uint_as_float(zw[j][q].y & 0xFFFF0000u)};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                  float a, da;
+                  act_fwd_bwd_t<ACT>(zv[s2], p.ep.alpha, a, da);
+                  o[s2] = acc[i][j][4 * q + s2] * rsc[i] * da;
+                }
+              }
+              const uint2 w = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+              if (FWD && RD == 0 && p.ep.amax_out && m < rows_valid && n < cvalid_n)
+                ymax = fmaxf(ymax, fmaxf(fmaxf(fabsf(__uint_as_float(w.x << 16)), fabsf(__uint_as_float(w.x & 0xFFFF0000u))),
+                                         fmaxf(fabsf(__uint_as_float(w.y << 16)), fabsf(__uint_as_float(w.y & 0xFFFF0000u)))));
+              *reinterpret_cast<uint2*>(wstg + (32 * i + lm) * ld + n) = w;
+            }
+        }
+      };
+      stage_round(std::integral_constant<int, 0>{});
+      __syncthreads();
+      if (p.C)
+        store_stage(stg, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
+      if (p.row_q || p.col_q) mx_from_stage(stg, rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
+      if (!FWD && p.ep.amax_out) {   // rotated amax of dz^T over the tile's valid 64-column chunks
+        uint32_t ok = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ok |= (n0 + 64 * k < p.N ? 1u : 0u) << k;
+        ymax = rht16_amax_stage(stg, rows_valid, ok, p.ep.rht_signs);
+      }
+      __syncthreads();
+      if (FWD && p.preact) {
+        stage_round(std::integral_constant<int, 1>{});
+        __syncthreads();
+        store_stage(stg, rows_valid, cvalid_n, GM_BN, p.preact + (long long)row0 * p.N + n0, p.N);
+        __syncthreads();
+      }
+      if (p.ep.amax_out) wave_amax_atomic(ymax, p.ep.amax_out, lane);
     } else if (EPI == EPI_STORE) {
       const int ld = GM_STG_LD_256;
 #pragma unroll

@@ -26,10 +26,13 @@ enum {
   KIND_GLU_MXO,          // the same with MXFP8 outputs
   KIND_MXIN_GLU,         // FC1 + GLU, MXFP8 operands
   KIND_MXIN_GLU_MXO,     // the same with MXFP8 outputs
-  KIND_DGLU_PACKED,      // dgrad + dGLU, packed W2
+  KIND_ACT,              // FC1 + non-gated activation, packed plain W1
+  KIND_DGLU_PACKED,      // dgrad + dGLU, packed W2 (this and the kinds below: backward)
   KIND_DGLU_NK,          // dgrad + dGLU, W2 as [I][H]
   KIND_DGLU_G_PACKED,    // the same two adding d(bias) and d(row_scale)
-  KIND_DGLU_G_NK
+  KIND_DGLU_G_NK,
+  KIND_DACT_PACKED,      // dgrad + non-gated activation derivative
+  KIND_DACT_NK
 };
 moe_status_t launch_activation_kernel(int kind, const GemmArgs& args, int grid, hipStream_t stream);
 #define MOE_DECLARE_ACT_LAUNCHERS(n)                                                              \

@@ -68,12 +68,15 @@ typedef enum {
  * rounded to bf16 (round-to-nearest-even).  (host struct) */
 typedef struct {
   int32_t act;              /* moe_act_t */
-  int32_t gated;            /* must be 1: the gated (GLU) form */
+  int32_t gated;            /* 1: the gated (GLU) form y = a(g_c) * u_c; 0: the non-gated form
+                               y = a(z) over I columns (no clamps, no up_offset; sReLU's
+                               plain form), see moe_group_gemm_glu_fwd */
   float alpha;              /* SwiGLU gate scale inside the sigmoid; 1 = plain SiLU */
   float gate_lo, gate_hi;   /* clamp bounds on g; -inf/+inf = off */
   float up_lo, up_hi;       /* clamp bounds on u; -inf/+inf = off */
   float up_offset;          /* added to the clamped up value; 0 = off */
-  const void* bias;         /* nullable: bf16 [E][2I] in PLAIN order (gate | up) */
+  const void* bias;         /* nullable: bf16 [E][2I] in PLAIN order (gate | up); [E][I] when
+                               non-gated */
   const float* row_scale;   /* nullable: fp32 [M_cap], multiplies y per row */
   /* Per-tensor amax for an NVFP4-style recipe ([BLOG] "Fusionando cuantización MXFP8 y
      NVFP4": the forward emits its output's amax, the backward the amax of the Hadamard
@@ -257,7 +260,10 @@ moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T
  *     y = bf16(GLU epilogue of z)        optional, [M_cap][I]
  *     mx = MXFP8 copies of y             optional (row-wise and/or transposed)
  * xg: bf16 [M_cap][H]; w1_packed from moe_repack_gate_up.
- * Requires H % 64 == 0, I % 64 == 0, ep->gated == 1.
+ * Non-gated form (ep->gated == 0): W1 [E][H][I] packed by moe_pack_weight
+ * (MOE_B_KN source, N = I, K = H), z and preact are [M_cap][I], y = bf16(a(z)
+ * * row_scale); bias [E][I].
+ * Requires H % 64 == 0, I % 64 == 0.
  * One persistent launch; tiles are scheduled from the device counts.
  * cu_margin: compute units left free for concurrent kernels (0 = use all). */
 moe_status_t moe_group_gemm_glu_fwd(const void* xg, const moe_groups_t* groups,
@@ -291,6 +297,9 @@ moe_status_t moe_group_gemm_glu_fwd_mx(const moe_operand_t* xg, const moe_groups
  *     dg = G * uc * rs * a'(gc) * [gate_lo <= g <= gate_hi]
  *     dgu = bf16([dg | du])              [M_cap][2I] plain order
  *     mx = MXFP8 copies of dgu           optional
+ * Non-gated form (ep->gated == 0): preact and dgu are [M_cap][I] and
+ * dgu = bf16(G * rs * a'(z)); the parameter gradients are not available
+ * (MOE_ERR_UNSUPPORTED), the rotated amax is.
  * ep->bias is ignored (already inside preact).  Requires H % 64 == 0,
  * I % 64 == 0. */
 moe_status_t moe_group_gemm_dglu_bwd(const void* dy2, const moe_operand_t* w2, int H, int I,

@@ -330,6 +330,29 @@ def dgrad_dglu(dy2_bits, counts, w2_bits, preact_bits, ep: Epilogue, dtype=np.fl
     return out
 
 
+def dgrad_dact(dy2_bits, counts, w2_bits, preact_bits, ep: Epilogue, dtype=np.float64):
+    """Backward of the non-gated form y = a(z) * rs (reading: sReLU, listed by
+    [BLOG] beside the GLUs, taken without a gate; the same for any
+    activation): dz = G * rs * a'(z) with G = dY2_e W2_e^T and z the saved bf16
+    pre-activation [M][I].  Returns dz bf16 bits [M][I]."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    M = int(off[-1])
+    E, I, H = w2_bits.shape
+    out = np.zeros((M, I), dtype=np.uint16)
+    rs_all = None if ep.row_scale is None else np.asarray(ep.row_scale, dtype=np.float64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        G = (_as_f(dy2_bits[a:b], dtype) @ _as_f(w2_bits[e], dtype).T).astype(np.float64)
+        if rs_all is not None:
+            G = G * rs_all[a:b, None]
+        z = bf16_bits_to_f64(preact_bits[a:b])
+        out[a:b] = f64_to_bf16_bits(G * activation_grad(z, ep.act, ep.alpha))
+    return out
+
+
 def dx(dgu_bits, counts, w1_bits, dtype=np.float64):
     """dX_e = dgu_e @ W1_e^T with the plain (un-repacked) W1 [E][H][2I]."""
     counts = np.asarray(counts, dtype=np.int64)

@@ -63,10 +63,16 @@ def test_host_argument_errors_return_before_launch():
     # misaligned operand
     assert G.raw_call("moe_group_gemm_glu_fwd", fake + 2, ctypes.byref(grp), fake, 256, 512,
                       ctypes.byref(ep), NULL, NULL, NULL, 0, NULL) == 3
-    # non-gated form is not a GLU
-    ep_ng = G.epilogue(gated=False)
+    # gated must be 0 (non-gated form) or 1
+    ep_bad = G.epilogue()
+    ep_bad.gated = 2
     assert G.raw_call("moe_group_gemm_glu_fwd", fake, ctypes.byref(grp), fake, 256, 512,
-                      ctypes.byref(ep_ng), NULL, NULL, NULL, 0, NULL) == 4
+                      ctypes.byref(ep_bad), NULL, NULL, NULL, 0, NULL) == 4
+    # the non-gated backward has no parameter gradients
+    ep_ng = G.epilogue(gated=False, dbias_out=fake)
+    w2op = G.operand(fake, layout=G.B_PACKED)
+    assert G.raw_call("moe_group_gemm_dglu_bwd", fake, ctypes.byref(w2op), 256, 512, ctypes.byref(grp),
+                      fake, ctypes.byref(ep_ng), fake, NULL, 0, NULL) == 4
     # MX outputs must come in (q, s) pairs
     mx = G.mx_out(row_q=fake)
     assert G.raw_call("moe_group_gemm_glu_fwd", fake, ctypes.byref(grp), fake, 256, 512,

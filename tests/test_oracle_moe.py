@@ -699,3 +699,54 @@ def test_bias_grad_sums_rows_of_each_group():
     assert np.array_equal(db[0], v[0] + v[1])
     assert np.array_equal(db[1], np.zeros(4))
     assert np.array_equal(db[2], v[2] + v[3] + v[4])
+
+
+@pytest.mark.parametrize("act", ["srelu", "swiglu", "geglu"])
+def test_non_gated_forward_and_backward(act):
+    """Non-gated y = a(z) * rs: the forward against a scalar loop, the
+    backward dz against central differences of L = <dY2, FC2(y)> in z on a
+    bf16-exact chain (z = x W1 + b1 exact in bf16)."""
+    rng = np.random.default_rng(31)
+    T, H, I = 5, 8, 8
+    counts = np.array([3, 2])
+    x = rng.integers(-1, 2, (T, H)).astype(np.float64)
+    w1 = rng.integers(-1, 2, (2, H, I)) * 0.5
+    b1 = rng.integers(-1, 2, (2, I)) * 0.25
+    w2 = F.bf16_round(rng.standard_normal((2, I, H)) * 0.5)
+    dy2 = F.bf16_round(rng.standard_normal((T, H)))
+    rs = F.bf16_round(rng.uniform(0.5, 1.5, T))
+    bits = F.f64_to_bf16_bits
+    ep = O.Epilogue(act=act, gated=False, bias=bits(b1), row_scale=rs)
+    pre, y = O.fc1_glu(bits(x), counts, bits(w1), ep)
+    off = [0, 3, 5]
+    for e in range(2):
+        for r in range(off[e], off[e + 1]):
+            for j in range(I):
+                z = sum(x[r, k] * w1[e, k, j] for k in range(H)) + b1[e, j]
+                assert F.bf16_bits_to_f64(pre[r, j]) == z
+                want = O.activation(np.array([z]), act, 1.0)[0] * rs[r]
+                assert F.bf16_bits_to_f64(y[r, j]) == F.bf16_round(np.array([want]))[0]
+    dz = F.bf16_bits_to_f64(O.dgrad_dact(bits(dy2), counts, bits(w2), pre, O.Epilogue(act=act, row_scale=rs)))
+    z_all = F.bf16_bits_to_f64(pre)
+
+    def loss(z):
+        L = 0.0
+        for e in range(2):
+            a, b = off[e], off[e + 1]
+            yy = O.activation(z[a:b], act, 1.0) * rs[a:b, None]
+            L += float(np.sum(dy2[a:b] * (yy @ w2[e])))
+        return L
+
+    checked = 0
+    for r in range(T):
+        for j in range(I):
+            if act == "srelu" and abs(z_all[r, j]) < 1e-3:
+                continue
+            h = 1e-6
+            zp, zm = z_all.copy(), z_all.copy()
+            zp[r, j] += h
+            zm[r, j] -= h
+            fd = (loss(zp) - loss(zm)) / (2 * h)
+            assert abs(dz[r, j] - fd) <= 2.0 ** -8 * abs(fd) + 1e-6, (r, j, dz[r, j], fd)
+            checked += 1
+    assert checked >= 20
