@@ -16,6 +16,8 @@ from tests.gpu_util import (assert_bf16_close, dev_bits, dev_i32, empty_bits, ex
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
+RHT_SIGNS = 0x5A3C
+
 
 @pytest.fixture(scope="module")
 def G():
@@ -59,10 +61,26 @@ def dsv3_run(G):
     G.moe_group_gemm_quant(G.operand(y), G.operand(w2f, layout=G.B_PACKED), H, I, grp, out2)
     G.moe_group_gemm_dglu_bwd(dy2, G.operand(w2d, layout=G.B_PACKED), H, I, grp, pre, ep, dgu)
     G.moe_group_gemm_quant(G.operand(dgu), G.operand(w1x, layout=G.B_PACKED), H, 2 * I, grp, dx)
+    # the same FC1 and dgrad launches asked for their epilogue extras: max|y|,
+    # the amax of the 16-row Hadamard rotation of dgu^T, d(bias), d(row_scale)
+    amax_y = torch.zeros(1, dtype=torch.float32, device="cuda")
+    amax_r = torch.zeros(1, dtype=torch.float32, device="cuda")
+    db = torch.zeros((E, 2 * I), dtype=torch.float32, device="cuda")
+    drs = torch.zeros(M, dtype=torch.float32, device="cuda")
+    y_x, dgu_r, dgu_g = empty_bits((M, I)), empty_bits((M, 2 * I)), empty_bits((M, 2 * I))
+    G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, G.epilogue("swiglu", amax_out=amax_y), y_x, None)
+    G.moe_group_gemm_dglu_bwd(dy2, G.operand(w2d, layout=G.B_PACKED), H, I, grp, pre,
+                              G.epilogue("swiglu", amax_out=amax_r, rht_signs=RHT_SIGNS), dgu_r)
+    G.moe_group_gemm_dglu_bwd(dy2, G.operand(w2d, layout=G.B_PACKED), H, I, grp, pre,
+                              G.epilogue("swiglu", dbias_out=db, drow_scale_out=drs), dgu_g)
     _sync()
     res = dict(d=d, dy2=dy2_h, off=off.cpu().numpy(), y=host_bits(y), pre=host_bits(pre),
-               out2=host_bits(out2), dgu=host_bits(dgu), dx=host_bits(dx))
-    del x, w1, w2, dy2, w1p, w1x, w2f, w2d
+               out2=host_bits(out2), dgu=host_bits(dgu), dx=host_bits(dx),
+               extras_same_outputs=(bool(torch.equal(y_x, y)), bool(torch.equal(dgu_r, dgu)),
+                                    bool(torch.equal(dgu_g, dgu))),
+               amax_y=float(amax_y.item()), amax_rht=float(amax_r.item()),
+               db=db.cpu().numpy().astype(np.float64), drs=drs.cpu().numpy().astype(np.float64))
+    del x, w1, w2, dy2, w1p, w1x, w2f, w2d, y_x, dgu_r, dgu_g
     return res
 
 
@@ -119,6 +137,78 @@ def test_dsv3_dx_sampled_rows(dsv3_run):
         dgu_r = O.dgrad_dglu(dsv3_run["dy2"][rr], [len(rr)], d["w2"][e:e + 1], pre_r, O.Epilogue())
         ref = O.dx(dgu_r, [len(rr)], d["w1"][e:e + 1])
         assert_bf16_close(dsv3_run["dx"][rr], ref, what=f"dsv3 dx expert {e}", normwise=2e-2)
+
+
+def test_dsv3_extras_leave_outputs_unchanged(dsv3_run):
+    assert dsv3_run["extras_same_outputs"] == (True, True, True)
+
+
+def test_dsv3_fc1_amax_is_max_abs_y(dsv3_run):
+    """max|y| over all 16384 rows: the bf16 values the call stored decide it
+    bit for bit (both sides take the maximum of the same numbers)."""
+    own = float(np.max(np.abs(F.bf16_bits_to_f64(dsv3_run["y"]))))
+    assert dsv3_run["amax_y"] == np.float32(own) and own > 0.0
+
+
+def _sylvester16():
+    h = np.array([[1.0]])
+    for _ in range(4):
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def test_dsv3_dglu_rht_amax_of_stored_dgu(dsv3_run):
+    """The rotated amax against the same rotation applied here to the dgu the
+    GPU stored: runs of 16 rows restarting at each group (zero-padded), each
+    row i negated when bit i of the signs is set, H16 / 4.  The GPU rotates in
+    fp32 (4 butterfly stages on bf16 inputs), so it may differ by the fp32
+    rounding of those sums: 4 stages x 2^-24 x 16 max|dgu| / 4."""
+    counts = dsv3_run["d"]["counts"]
+    v = F.bf16_bits_to_f64(dsv3_run["dgu"])
+    s = np.array([-1.0 if (RHT_SIGNS >> i) & 1 else 1.0 for i in range(16)])
+    R = _sylvester16() * s[None, :] / 4.0
+    off = np.concatenate([[0], np.cumsum(counts)])
+    want = 0.0
+    for e in range(len(counts)):
+        blk = v[off[e]:off[e + 1]]
+        pad = (-len(blk)) % 16
+        X = np.concatenate([blk, np.zeros((pad, blk.shape[1]))]).reshape(-1, 16, blk.shape[1])
+        want = max(want, float(np.max(np.abs(R[None] @ X))))
+    tol = 4 * 2.0 ** -24 * 16 * float(np.max(np.abs(v))) / 4
+    assert want > 0 and abs(dsv3_run["amax_rht"] - want) <= tol, (dsv3_run["amax_rht"], want, tol)
+
+
+def test_dsv3_dbias_is_column_sums_of_dgu(dsv3_run):
+    """d(bias) at full size: per-expert column sums of the dgu the GPU stored,
+    up to the order of fp32 additions (n 2^-24 sum|v|)."""
+    counts = dsv3_run["d"]["counts"]
+    v = F.bf16_bits_to_f64(dsv3_run["dgu"])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    for e in range(len(counts)):
+        blk = v[off[e]:off[e + 1]]
+        bound = len(blk) * 2.0 ** -24 * np.abs(blk).sum(axis=0) + 1e-30
+        assert np.all(np.abs(dsv3_run["db"][e] - blk.sum(axis=0)) <= bound), f"expert {e}"
+
+
+def test_dsv3_drow_scale_sampled_rows(dsv3_run):
+    """d(row_scale) on sampled rows against the oracle's (its own G and its own
+    pre-activation), within fp32 accumulation plus the bf16 rounding flips of
+    the pre-activation: 2e-4 of sum_j |G a u|."""
+    d = dsv3_run["d"]
+    counts = d["counts"]
+    rows = sample_rows(counts, per_group=1, seed=6)
+    experts = expert_of_rows(counts, rows)
+    ep = O.Epilogue()
+    for e in np.unique(experts):
+        rr = rows[experts == e]
+        pre_r, _ = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], ep)
+        dy = dsv3_run["dy2"][rr]
+        want = O.row_scale_grad(dy, [len(rr)], d["w2"][e:e + 1], pre_r, ep)
+        Gm = F.bf16_bits_to_f64(dy) @ F.bf16_bits_to_f64(d["w2"][e]).T
+        yu = O.glu_from_preact(F.bf16_bits_to_f64(pre_r), ep)
+        bound = 2e-4 * np.sum(np.abs(Gm * yu), axis=1) + 1e-9
+        err = np.abs(dsv3_run["drs"][rr] - want)
+        assert np.all(err <= bound), (e, err.max(), bound.min())
 
 
 def test_gptoss_route_and_fc1_sampled_rows(G):

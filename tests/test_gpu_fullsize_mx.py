@@ -1,0 +1,204 @@
+"""The MXFP8 forward at the DeepSeek-V3-like expert share's full size (16384
+routed rows, H 7168, I 2048, 32 ragged experts, student-t activations), in
+the launches bench.py times, checked on sampled outputs the oracle computes
+one by one:
+
+- FC1 + SwiGLU writing the pre-activation, y and y's row-wise and transposed
+  MXFP8 copies in its epilogue (sampled rows; sampled 32-row column blocks,
+  among them every sampled group's ragged last block);
+- rows of x quantised on the GPU (bit-exact on sampled rows);
+- FC1 + SwiGLU on MXFP8 x and MXFP8 W1 (sampled rows x sampled columns);
+- FC2 on the MXFP8 rows of y and MXFP8 W2 (sampled rows x sampled columns).
+
+The oracle's MXFP8 quantiser is a plain per-block loop, so only the weight
+rows the sampled columns need are quantised.  At K = 7168 the fp32
+accumulation flips the bf16 rounding of y more often than at the small test
+sizes; blocks whose source values differ are held to the dequantisation
+bound instead of byte equality, and at most a quarter of them may differ.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import formats as F
+from oracle import moe as O
+from tests.gpu_util import (assert_bf16_close, assert_mx_cols, assert_mx_rows, dev_bits, dev_i32,
+                            empty_bits, empty_bytes, expert_of_rows, host_bits, sample_rows)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+MAX_FLIP = 0.25
+
+
+@pytest.fixture(scope="module")
+def G():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_gemm_glu_amd as G
+    G.moe_init(0)
+    return G
+
+
+@pytest.fixture(scope="module")
+def run(G):
+    import torch
+    d = W.dsv3(with_w2=True, x_kind="student_t")
+    E, M, H, I = d["E"], d["M"], d["H"], d["I"]
+    counts = d["counts"]
+    x, w1, w2 = dev_bits(d["x"]), dev_bits(d["w1"]), dev_bits(d["w2"])
+    grp = G.groups(dev_i32(counts), M)
+    ep = G.epilogue("swiglu")
+    # FC1 (bf16) with the MXFP8 copies of y
+    w1p = empty_bits((G.moe_packed_w1_bytes(E, H, I) // 2,))
+    G.moe_repack_gate_up(w1, E, H, I, w1p)
+    y, pre = empty_bits((M, I)), empty_bits((M, 2 * I))
+    row_q, row_s = empty_bytes((M, I)), empty_bytes((M, I // 32))
+    col_q, col_s = empty_bytes((I, M)), empty_bytes((I, (M + 31) // 32 + E))
+    G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, y, pre,
+                             G.mx_out(row_q=row_q, row_s=row_s, col_q=col_q, col_s=col_s))
+    # FC2 on the MXFP8 rows of y
+    w2q = empty_bytes((G.moe_packed_mx_weight_bytes(E, H, I),))
+    w2s = empty_bytes((G.moe_packed_mx_scale_bytes(E, H, I),))
+    G.moe_pack_weight_mx(w2, E, H, I, G.B_KN, w2q, w2s)
+    out2 = empty_bits((M, H))
+    G.moe_group_gemm_quant(G.operand(row_q, dtype=G.DT_MXFP8, scales=row_s),
+                           G.operand(w2q, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=w2s),
+                           H, I, grp, out2)
+    # FC1 on MXFP8 x and MXFP8 W1
+    xq, xs = empty_bytes((M, H)), empty_bytes((M, H // 32))
+    G.moe_mxfp8_quantize(x, M, H, None, G.mx_out(row_q=xq, row_s=xs))
+    w1q = empty_bytes((G.moe_packed_mx_weight_bytes(E, 2 * I, H),))
+    w1s = empty_bytes((G.moe_packed_mx_scale_bytes(E, 2 * I, H),))
+    G.moe_repack_gate_up_mx(w1, E, H, I, w1q, w1s)
+    y_mx, pre_mx = empty_bits((M, I)), empty_bits((M, 2 * I))
+    G.moe_group_gemm_glu_fwd_mx(G.operand(xq, dtype=G.DT_MXFP8, scales=xs), grp,
+                                G.operand(w1q, dtype=G.DT_MXFP8, layout=G.B_PACKED, scales=w1s),
+                                H, I, ep, y_mx, pre_mx)
+    torch.cuda.synchronize()
+    res = dict(d=d, y=host_bits(y), pre=host_bits(pre), row_q=row_q.cpu().numpy(),
+               row_s=row_s.cpu().numpy(), col_q=col_q.cpu().numpy(), col_s=col_s.cpu().numpy(),
+               out2=host_bits(out2), xq=xq.cpu().numpy(), xs=xs.cpu().numpy(),
+               y_mx=host_bits(y_mx), pre_mx=host_bits(pre_mx))
+    del x, w1, w2, w1p, w2q, w2s, w1q, w1s
+    return res
+
+
+def _experts_sampled(counts, n_random, seed):
+    """First, last, largest and smallest non-empty experts plus random ones."""
+    counts = np.asarray(counts)
+    nz = np.flatnonzero(counts > 0)
+    pick = {int(nz[0]), int(nz[-1]), int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])}
+    rng = np.random.default_rng(seed)
+    pick.update(int(e) for e in rng.choice(nz, size=min(n_random, len(nz)), replace=False))
+    return sorted(pick)
+
+
+def test_fc1_y_and_preact_sampled_rows(run):
+    d = run["d"]
+    counts = d["counts"]
+    rows = sample_rows(counts, per_group=1, seed=11)
+    experts = expert_of_rows(counts, rows)
+    for e in np.unique(experts):
+        rr = rows[experts == e]
+        pre, y = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
+        assert_bf16_close(run["y"][rr], y, what=f"y expert {e}")
+        assert_bf16_close(run["pre"][rr], pre, what=f"preact expert {e}")
+
+
+def test_fc1_mx_row_copies_sampled_rows(run):
+    d = run["d"]
+    counts, I = d["counts"], d["I"]
+    rows = sample_rows(counts, per_group=1, seed=12, max_rows=48)
+    experts = expert_of_rows(counts, rows)
+    gy, ry = [], []
+    for e in np.unique(experts):
+        rr = rows[experts == e]
+        _, y = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
+        gy.append(rr)
+        ry.append(y)
+    rr, ry = np.concatenate(gy), np.concatenate(ry)
+    assert_mx_rows(run["row_q"][rr], run["row_s"][rr], run["y"][rr], ry, what="row copies",
+                   max_flip=MAX_FLIP)
+
+
+def test_fc1_mx_col_copies_sampled_blocks(run):
+    """32-row blocks of the transposed copy: the last (ragged) block of each
+    sampled group and the first block of the largest one, all 2048 columns."""
+    d = run["d"]
+    counts = d["counts"]
+    off = O.exclusive_offsets(counts)
+    so = O.mx_scale_col_offsets(counts)
+    experts = _experts_sampled(counts, 5, seed=13)
+    big = int(np.argmax(counts))
+    blocks = [(e, (int(counts[e]) - 1) // 32) for e in experts] + [(big, 0)]
+    for e, j in blocks:
+        a = int(off[e]) + 32 * j
+        n = min(32, int(off[e + 1]) - a)
+        _, ry = O.fc1_glu(d["x"][a:a + n], [n], d["w1"][e:e + 1], O.Epilogue())
+        assert_mx_cols(run["col_q"][:, a:a + n], run["col_s"][:, so[e] + j:so[e] + j + 1],
+                       run["y"][a:a + n], ry, [n], n, what=f"col copies expert {e} block {j}",
+                       max_flip=MAX_FLIP)
+
+
+def test_x_quantize_sampled_rows_bit_exact(run):
+    d = run["d"]
+    rows = sample_rows(d["counts"], per_group=1, seed=14, max_rows=32)
+    q, s = O.mx_quantize_rows(d["x"][rows])
+    assert np.array_equal(run["xq"][rows], q) and np.array_equal(run["xs"][rows], s)
+
+
+def _abs_bound(aq, as_, bq, bs):
+    """2^-14 sum_k |a_k b_k| from the dequantised operands (the block-scaled
+    MFMA's accumulation is not strict fp32)."""
+    A = np.abs(O.mx_dequantize_rows(aq, as_))
+    B = np.abs(O.mx_dequantize_rows(bq, bs))
+    return (A @ B.T) * 2.0 ** -14
+
+
+def test_fc1_mx_inputs_sampled_rows_and_columns(run):
+    """y and the pre-activation of the MXFP8-input FC1 at 24 sampled columns
+    (gate and up halves) of sampled rows: the oracle dequantises the sampled
+    rows of x and the W1^T rows those columns use, then multiplies."""
+    d = run["d"]
+    counts, H, I = d["counts"], d["H"], d["I"]
+    cols = np.sort(np.concatenate([[0, I - 1], np.random.default_rng(15).choice(
+        np.arange(1, I - 1), 22, replace=False)]))
+    rows = sample_rows(counts, per_group=1, seed=16, max_rows=40)
+    experts = expert_of_rows(counts, rows)
+    for e in _experts_sampled(counts, 4, seed=17):
+        rr = rows[experts == e]
+        if len(rr) == 0:
+            continue
+        aq, as_ = O.mx_quantize_rows(d["x"][rr])
+        wt = np.ascontiguousarray(d["w1"][e].T[np.concatenate([cols, I + cols])])   # [2c][H]
+        q, s = O.mx_quantize_rows(wt)
+        rp, ry = O.fc1_glu_mx(aq, as_, [len(rr)], q[None], s[None], O.Epilogue())
+        zb = _abs_bound(aq, as_, q, s)
+        c = len(cols)
+        assert_bf16_close(run["pre_mx"][rr][:, np.concatenate([cols, I + cols])], rp,
+                          what=f"mx-input preact expert {e}", extra=zb)
+        zr = np.abs(F.bf16_bits_to_f64(rp))
+        ey = 1.2 * zr[:, c:] * zb[:, :c] + (zr[:, :c] + 1.0) * zb[:, c:]
+        assert_bf16_close(run["y_mx"][rr][:, cols], ry, what=f"mx-input y expert {e}", extra=ey)
+
+
+def test_fc2_mx_sampled_rows_and_columns(run):
+    """FC2 on the MXFP8 rows of y at 32 sampled output columns: the oracle
+    quantises its own y rows and the W2 columns used, dequantises, multiplies."""
+    d = run["d"]
+    counts, H = d["counts"], d["H"]
+    hs = np.sort(np.concatenate([[0, H - 1], np.random.default_rng(18).choice(
+        np.arange(1, H - 1), 30, replace=False)]))
+    rows = sample_rows(counts, per_group=1, seed=19, max_rows=40)
+    experts = expert_of_rows(counts, rows)
+    for e in _experts_sampled(counts, 4, seed=20):
+        rr = rows[experts == e]
+        if len(rr) == 0:
+            continue
+        _, ry = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
+        yq, ys = O.mx_quantize_rows(ry)
+        bq, bs = O.mx_quantize_rows(np.ascontiguousarray(d["w2"][e].T[hs]))      # [h][I]
+        ref = O.group_gemm_mx(yq, ys, [len(rr)], bq[None], bs[None])
+        assert_bf16_close(run["out2"][rr][:, hs], ref, what=f"fc2 mx expert {e}",
+                          extra=_abs_bound(yq, ys, bq, bs))
