@@ -129,8 +129,24 @@ struct GemmArgs {
 __device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 __device__ __forceinline__ int swz_off(int r, int c) { return r * 128 + ((c ^ swz_key(r)) << 4); }
 
+// Weight-gradient operand tiles keep their [reduction rows][columns] layout:
+// 64 rows of 256 bf16 columns, 512 bytes per row, 16-byte chunk c of row r at
+// chunk c ^ 4 (r % 4).  A transposed fragment read names 4 consecutive rows
+// x 4 chunks per half wave; the key sends those 16 pieces to 16 different
+// 16-byte bank groups.
+__device__ __forceinline__ int wg_off(int r, int c) { return r * 512 + ((c ^ ((r & 3) << 2)) << 4); }
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// LDS transpose read (8 bytes per lane): lane j of each 16-lane group gets
+// element j % 4 of the 4-element pieces named by lanes j/4 + 4 i of its group,
+// i = 0..3, in that order.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
 
 // Raw buffer descriptor over [base, base + bytes) (bytes clamped to 2^32 - 1).
 // gfx9 descriptor word 3: 32-bit data format, no swizzle, no stride.
@@ -336,10 +352,13 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
                 "MXFP8 inputs: packed B; plain store or GLU epilogue");
   static_assert(2 * GM_TILE_BYTES + 2048 <= GM_STAGE_ALLOC, "scale slots");
   // Weight gradients reduce over a group's rows: both operands are stored
-  // [rows][columns] with the reduction dimension as the row index, so both
-  // go through the register transpose (the N-contiguous path).
+  // [rows][columns] with the reduction dimension as the row index.  They go
+  // to LDS as they are (LDS-DMA, wg_off layout) and the MFMA fragments come
+  // out of the LDS transpose read.  Other N-contiguous B operands go through
+  // a register transpose.
   constexpr bool WG = EPI == EPI_WGRAD;
   static_assert(!WG || (BLAY == BL_KN && !MXT), "weight gradient: N-contiguous bf16 operands");
+  constexpr bool KNR = BLAY == BL_KN && !WG;
   // Two distinct stage arrays: the compiler can then see that the LDS-DMA
   // writes of the next stage never alias the fragment reads of the current
   // one, and does not wait for the prefetch before computing.
@@ -493,9 +512,6 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     const int kn_c = (tid + zt) & 31, kn_g = (tid + zt) >> 5;
     const uint32_t kn_voff =
         (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
-    const uint32_t kn_voff_a =
-        WG ? (uint32_t)(kn_g * 8) * a_stride + (uint32_t)min(mt * GM_BM + kn_c * 8, p.wg_P - 8) * 2u
-           : 0u;
 
     f32x16 acc[MI][4];
 #pragma unroll
@@ -534,8 +550,36 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         lds_dma16(rs, lds_tile + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16), koff);
       }
     };
+    // weight gradient: K-tile kt (rows kt*64 .. + 63 of the group) of an
+    // operand stored [rows][columns], columns from byte col0b on, into the
+    // wg_off layout.  Instruction j of wave w fills rows 2 (8 w + j) and the
+    // next one; lane l lands on row + l / 32, physical chunk l % 32, so it
+    // fetches logical chunk (l % 32) ^ 4 (row % 4).  The descriptor starts at
+    // the K-tile's first row and ends at the group's last row, so rows past
+    // the group read zero.  Columns past the matrix edge read other bytes of
+    // the operand; they only reach output columns the epilogue drops.
+    auto issue_wg = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t stride, uint32_t col0b) {
+      const int hr = lane_t >> 5, pw = lane_t & 31;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 2 * (8 * wave + j) + hr;
+        const int c = pw ^ ((r & 3) << 2);
+        lds_dma16(rs, lds_tile + (8 * wave + j) * 1024,
+                  (uint32_t)r * stride + col0b + (uint32_t)(c << 4), 0u);
+      }
+    };
     auto issue_direct = [&](int kt, uint8_t* sa) {
       const bool in = kt < nk_t;
+      if constexpr (WG) {
+        const long long r0 = (long long)kt * 64;
+        const rsrc_t rak = in ? make_rsrc(Ab + ((long long)row0 + r0) * a_stride,
+                                          ((long long)m_e - r0) * a_stride)
+                              : rsZ;
+        const rsrc_t rbk = in ? make_rsrc(Bb + r0 * b_stride, ((long long)m_e - r0) * b_stride) : rsZ;
+        issue_wg(rak, sa, a_stride, (uint32_t)(mt * GM_BM) * 2u);
+        issue_wg(rbk, sa + GM_TILE_BYTES, b_stride, (uint32_t)n0 * 2u);
+        return;
+      }
       if (!WG)
         issue_tile(std::integral_constant<int, TBM>{}, in ? rsA : rsZ, sa, a_stride,
                    (uint32_t)kt * 128u);
@@ -555,7 +599,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
             r * 4u, (uint32_t)kt * 1024u, 0, 0);
       }
     };
-    u32x4 rb[8], ra[8];
+    u32x4 rb[8];
     auto kn_load = [&](int kt) {
       const bool in = kt < nk_t;
       const int ktc = in ? kt : 0;
@@ -564,12 +608,6 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       for (int i = 0; i < 8; ++i)
         rb[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsB : rsZ, kn_voff,
                                                       (uint32_t)((krow + i) * b_stride), 0);
-      if (WG) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          ra[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsA : rsZ, kn_voff_a,
-                                                        (uint32_t)((krow + i) * a_stride), 0);
-      }
     };
     // r[i] holds 8 columns at k = 8*kn_g + i; transposed to 8 k-values per column
     auto kn_put = [&](const u32x4 (&r)[8], uint8_t* t) {
@@ -585,10 +623,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
             make_uint4(o[0], o[1], o[2], o[3]);
       }
     };
-    auto kn_store = [&](uint8_t* stage) {
-      kn_put(rb, stage + GM_TILE_BYTES);
-      if (WG) kn_put(ra, stage);
-    };
+    auto kn_store = [&](uint8_t* stage) { kn_put(rb, stage + GM_TILE_BYTES); };
 
     // Fragments are double-buffered one k-step ahead.  A K-tile is 4 k-steps
     // of 16 MFMAs per wave.  The barrier that hands a stage back to the DMA
@@ -611,7 +646,28 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       const uint8_t* sb = sa + GM_TILE_BYTES;
       const int h = lane_t >> 5;
       const int ra = wm * HR + (lane_t & 31), rbw = wn * 128 + (lane_t & 31);
-      if constexpr (!MXT) {
+      if constexpr (WG) {
+        // lane l names row ks*16 + 8 (l/32) + 4 t + (l%16)/4 at column
+        // c0 + 16 ((l/16) % 2) + 4 (l % 4) and so receives column c0 + l % 32
+        // at rows ks*16 + 8 (l/32) + 4 t .. + 3: two reads (t = 0, 1) give
+        // the 8 k values of the MFMA fragment
+        // (each address is one byte offset from the stage base: a longer
+        // chain of pointer steps hides from the compiler which stage array a
+        // read touches, and it then waits for the other stage's DMA)
+        const int rr = ks * 16 + 8 * h + ((lane_t & 15) >> 2);
+        const int cl = 16 * ((lane_t >> 4) & 1) + 4 * (lane_t & 3);
+        auto rd = [&](int tile, int c0) {
+          const int c = c0 + cl;
+          const int o = tile + wg_off(rr, c >> 3) + 2 * (c & 7);
+          const s16x4 lo = lds_read_tr16(sa + o), hi = lds_read_tr16(sa + (o + 4 * 512));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        af[buf][0] = rd(0, wm * HR);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bfr[buf][j] = rd(GM_TILE_BYTES, wn * 128 + 32 * j);
+#pragma unroll
+        for (int i = 1; i < MI; ++i) af[buf][i] = rd(0, wm * HR + 32 * i);
+      } else if constexpr (!MXT) {
         const int ch = ks * 2 + h;
         auto rd_a = [&](int i) {
           af[buf][i] = *reinterpret_cast<const bf16x8*>(sa + swz_off(ra + i * 32, ch));
@@ -670,7 +726,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         }
     };
     // LDS reads issued by the frag_load just before a k-step
-    constexpr int DS_STEP = MXT ? 2 * (MI + 4) : MI + 4;
+    constexpr int DS_STEP = (MXT || WG) ? 2 * (MI + 4) : MI + 4;
     constexpr int NMF = 4 * MI;                 // MFMAs per k-step
     // NMF MFMAs; the LDS reads issued just before are spread over them from
     // the first MFMA on (two per MFMA where there are more reads than
@@ -695,7 +751,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       mfmas(buf, sset, ks);
       static_for<NMF>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
-        if constexpr (g < DS_STEP) __builtin_amdgcn_sched_group_barrier(0x100, MXT ? 2 : 1, 0);
+        if constexpr (g < DS_STEP) __builtin_amdgcn_sched_group_barrier(0x100, (MXT || WG) ? 2 : 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, NVM / NMF + (g < NVM % NMF ? 1 : 0), 0);  // DMA
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // MFMA
       });
@@ -721,28 +777,28 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // LDS access names its array directly.  With an odd tile count the last
     // step computes a zero tile.
     issue_direct(0, lds0);
-    if (BLAY == BL_KN) {
+    if (KNR) {
       kn_load(0);
       kn_store(lds0);
     }
     stage_barrier();
     issue_direct(1, lds1);
-    if (BLAY == BL_KN) kn_load(1);
+    if (KNR) kn_load(1);
     __builtin_amdgcn_sched_barrier(0);
     frag_load(lds0, 0, 0, 0);
     for (int kt = 0; kt < nk_t; kt += 2) {
       first_steps(lds0, 0);
-      if (BLAY == BL_KN) kn_store(lds1);
+      if (KNR) kn_store(lds1);
       stage_barrier();
       issue_direct(kt + 2, lds0);
-      if (BLAY == BL_KN) kn_load(kt + 2);
+      if (KNR) kn_load(kt + 2);
       frag_load(lds1, 0, 0, 1);
       mfma_step_dma(1, 0, KSTEPS - 1);   // last k-step of K-tile kt
       first_steps(lds1, 1);
-      if (BLAY == BL_KN) kn_store(lds0);
+      if (KNR) kn_store(lds0);
       stage_barrier();
       issue_direct(kt + 3, lds1);
-      if (BLAY == BL_KN) kn_load(kt + 3);
+      if (KNR) kn_load(kt + 3);
       frag_load(lds0, 0, 0, 0);
       mfma_step_dma(1, 1, KSTEPS - 1);   // last k-step of K-tile kt + 1
     }
