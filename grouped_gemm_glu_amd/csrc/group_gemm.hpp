@@ -825,34 +825,49 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     }
 
     if constexpr (WG) {
-      // fp32 C_e rows mt*256 + m (rows past wg_P are outside the descriptor
-      // and dropped), 4 consecutive columns per lane and 16-byte stores;
-      // accumulate adds the current contents first.
-      const long long PQ = (long long)p.wg_P * p.N;
-      const rsrc_t rsC = make_rsrc(p.Cf + (long long)e * PQ, PQ * 4);
-      const int lh = (lane >> 5) + z0;
+      // fp32 C_e rows mt*256 + m, passed per 32-row block through the wave's
+      // own 16.5 KB of the stage arrays (rows of 128 fp32 + 16 bytes of
+      // padding) so that each store writes 2 rows x 512 contiguous bytes:
+      // whole cache lines instead of 32 rows x 32 bytes, a quarter of the L2
+      // write requests.  Rows past wg_P are outside the descriptor and
+      // dropped; columns past N are skipped; accumulate adds the current
+      // contents first.
       if (!(p.accumulate && m_e == 0)) {
+        constexpr int SLD = 128 * 4 + 16;               // staged row pitch (bytes)
+        uint8_t* wst = (wm ? lds1 : lds0) + wn * (32 * SLD) + z0;
+        const long long PQ = (long long)p.wg_P * p.N;
+        const rsrc_t rsC = make_rsrc(p.Cf + (long long)e * PQ, PQ * 4);
+        const int lh = (lane >> 5) + z0;
+        const int q0 = n0 + wn * 128 + 4 * (lane & 31) + z0;   // read-back: chunk lane % 32
+        const bool col_ok = q0 < p.N;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          const uint32_t rowb = (uint32_t)(mt * GM_BM + wm * HR + 32 * i + lm) * (uint32_t)p.N * 4u;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-              const int q0 = n0 + wn * 128 + 32 * j + 8 * rq + 4 * lh;
-              if (q0 < p.N) {
-                const uint32_t off = rowb + (uint32_t)q0 * 4u;
-                float4 v = make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
-                                       acc[i][j][4 * rq + 3]);
-                if (p.accumulate) {
-                  const float4 o = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsC, off, 0, 0));
-                  v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsC, off, 0, 0);
+            for (int rq = 0; rq < 4; ++rq)
+              *reinterpret_cast<float4*>(wst + lm * SLD + (32 * j + 8 * rq + 4 * lh) * 4) =
+                  make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                              acc[i][j][4 * rq + 3]);
+          const int row_base = mt * GM_BM + wm * HR + 32 * i;
+#pragma unroll
+          for (int s2 = 0; s2 < 16; ++s2) {
+            const int r = 2 * s2 + lh;
+            float4 v = *reinterpret_cast<const float4*>(wst + r * SLD + (lane & 31) * 16);
+            const uint32_t off = ((uint32_t)(row_base + r) * (uint32_t)p.N + (uint32_t)q0) * 4u;
+            if (col_ok) {
+              if (p.accumulate) {
+                const float4 o =
+                    __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsC, off, 0, 0));
+                v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
               }
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsC, off, 0, 0);
             }
+          }
         }
       }
+      // the next tile's first DMA rewrites lds0: every wave's staging reads done
+      __syncthreads();
     } else if (EPI == EPI_GLU || EPI == EPI_GLU_MX) {
       // y goes straight from registers to HBM, no LDS and no barrier.  Pair
       // wn of this tile: gate = blocks j = 0, 1; up = blocks j = 2, 3.  For
