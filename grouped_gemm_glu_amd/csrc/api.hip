@@ -247,22 +247,39 @@ moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T
   hipStream_t s = (hipStream_t)stream;
   const int TK = T * k;
   if (logits) {
-    if (T > 0)
-      hipLaunchKernelGGL(topk_kernel, dim3((T + 255) / 256), dim3(256), 0, s, logits, T, E, k,
-                         topk_ids_out);
+    if (T > 0) {
+      // one token per 16, 32 or 64 lanes
+      const int L = E <= 16 ? 16 : (E <= 32 ? 32 : 64);
+      const int per_block = 4 * (64 / L);
+      const dim3 grid((T + per_block - 1) / per_block);
+      if (L == 16)
+        hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, s, logits, T, E, k, topk_ids_out);
+      else if (L == 32)
+        hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(256), 0, s, logits, T, E, k, topk_ids_out);
+      else
+        hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), 0, s, logits, T, E, k, topk_ids_out);
+    }
   } else if (topk_ids != topk_ids_out && TK > 0) {
     if (hipMemcpyAsync(topk_ids_out, topk_ids, (size_t)TK * 4, hipMemcpyDeviceToDevice, s) !=
         hipSuccess)
       return MOE_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, topk_ids_out, TK, k, E, counts,
-                     offsets, dst, src);
-  if (x && TK > 0) {
-    long long chunks = (long long)TK * (H / 8);
-    long long blocks = (chunks + 255) / 256;
-    int grid = (int)(blocks < 4096 ? blocks : 4096);
-    hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), src, TK, H, static_cast<uint16_t*>(xg));
+  // chunks of C pairs (C >= 2E, so that the per-chunk counts fit in src; see
+  // group_count_kernel)
+  int C = 1024;
+  while (C < 2 * E) C *= 2;
+  const int nchunks = (TK + C - 1) / C;
+  if (nchunks > 1) {
+    hipLaunchKernelGGL(group_count_kernel, dim3(nchunks), dim3(256), 0, s, topk_ids_out, TK, E, C, src);
+    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks, E, src, counts, offsets);
+  }
+  // (with no pairs the single rank workgroup still writes zero counts)
+  hipLaunchKernelGGL(group_rank_kernel, dim3(nchunks > 1 ? nchunks : 1), dim3(256), 0, s,
+                     topk_ids_out, TK, E, C, nchunks > 1 ? src : nullptr, dst, counts, offsets);
+  if (TK > 0) {
+    const int grid = min((TK + 3) / 4, cus * 32);   // 4 pairs (one per wave) per workgroup step
+    hipLaunchKernelGGL(group_scatter_kernel, dim3(grid), dim3(256), 0, s, topk_ids_out, TK, k, E, dst,
+                       src, static_cast<const uint16_t*>(x), H, static_cast<uint16_t*>(xg));
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

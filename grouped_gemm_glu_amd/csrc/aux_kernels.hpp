@@ -87,89 +87,247 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- routing
-// Top-k of one token's logits ([MEGA] §2.1), ties to the lower expert id:
-// a candidate enters when it beats the current k-th entry, or equals it with a
-// lower id.  One thread per token.
+// Top-k of one token's logits ([MEGA] §2.1), ties to the lower expert id.
+// The order is (logit descending, id ascending) with NaN below every number
+// (numpy's sort order).  One token per group of L lanes (64 / L tokens per
+// wave); lane l of a group holds logits l, l + L, ... (at most 16, E <= 1024).
+// Each of the k rounds takes every lane's best untaken value, reduces it over
+// the group with xor shuffles, and marks the winner taken in its owner lane.
+__device__ __forceinline__ bool topk_before(float v, int e, float w, int f) {
+  const bool vn = v != v, wn = w != w;
+  if (vn) return wn && e < f;
+  if (wn) return true;
+  return v > w || (v == w && e < f);
+}
+template <int L>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int* __restrict__ ids_out) {
-  int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  float val[16];
-  int id[16];
-  for (int j = 0; j < 16; ++j) { val[j] = -INFINITY; id[j] = 0x7FFFFFFF; }
-  const float* lg = logits + (long long)t * E;
-  for (int e = 0; e < E; ++e) {
-    float v = lg[e];
-    bool better = (v > val[k - 1]) || (v == val[k - 1] && e < id[k - 1]);
-    if (!better) continue;
-    int pos = k - 1;
-    while (pos > 0 && ((v > val[pos - 1]) || (v == val[pos - 1] && e < id[pos - 1]))) {
-      val[pos] = val[pos - 1];
-      id[pos] = id[pos - 1];
-      --pos;
-    }
-    val[pos] = v;
-    id[pos] = e;
+  const int lane = threadIdx.x & 63;
+  const int gl = lane % L;
+  const long long tok = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / L) + lane / L;
+  const bool tv = tok < T;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = gl + L * i;
+    v[i] = (tv && e < E) ? logits[tok * E + e] : __builtin_nanf("");
   }
-  for (int j = 0; j < k; ++j) ids_out[(long long)t * k + j] = id[j];
+  uint32_t taken = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = __builtin_nanf("");
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = gl + L * i;
+      const bool cand = e < E && !((taken >> i) & 1u) && topk_before(v[i], e, bv, be);
+      bv = cand ? v[i] : bv;
+      be = cand ? e : be;
+    }
+#pragma unroll
+    for (int off = L / 2; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      const bool b = topk_before(ov, oe, bv, be);
+      bv = b ? ov : bv;
+      be = b ? oe : be;
+    }
+    if (be % L == gl) taken |= 1u << (be / L);
+    if (tv && gl == 0) ids_out[tok * k + j] = be;
+  }
 }
 
-// Counting sort of the T*k (token, slot) pairs by expert, stable in (t, j)
-// order ([MEGA] §4.3: rows for one expert contiguous).  One workgroup of 1024
-// threads: LDS histogram, exclusive scan, then each wave ranks the pairs of
-// its experts with ballots (order-independent of scheduling, so bit-exact).
-__global__ __launch_bounds__(1024) void group_kernel(const int* __restrict__ ids, int TK, int k,
-                                                     int E, int* __restrict__ counts,
-                                                     int* __restrict__ offsets,
-                                                     int* __restrict__ dst, int* __restrict__ src) {
-  __shared__ int hist[kMaxExperts];
-  __shared__ int off[kMaxExperts + 1];
+// Grouping: a counting sort of the T*k (token, slot) pairs by expert, stable in
+// (t, j) order ([MEGA] §4.3: rows for one expert contiguous).  Pairs whose id
+// is outside [0, E) are not grouped.  Chunks of C pairs (C = max(1024, a power
+// of two >= 2E), one workgroup each):
+//   group_count_kernel  per-chunk expert counts -> cnt[c][e]
+//   group_scan_kernel   counts, offsets, and cnt[c][e] = the number of pairs
+//                       of expert e in the chunks before c
+//   group_rank_kernel   dst[p] = that base + the pair's rank among the chunk's
+//                       earlier pairs of its expert
+//   group_scatter_kernel src[dst[p]] = token of p, and the gathered rows
+// A single chunk skips the first two: the rank kernel scans its own counts.
+// With several chunks cnt lives in src, which holds T*k >= chunks x E entries
+// (T*k > C (chunks - 1) >= 2E (chunks - 1)), and is overwritten only by the
+// scatter, after the rank kernel has read it.  Ranks depend only on the pair
+// order, so the result is bit-exact.
+__global__ __launch_bounds__(256) void group_count_kernel(const int* __restrict__ ids, int TK,
+                                                          int E, int C, int* __restrict__ cnt) {
+  __shared__ int h[kMaxExperts];
   const int t = threadIdx.x;
-  for (int e = t; e < E; e += 1024) hist[e] = 0;
+  for (int e = t; e < E; e += 256) h[e] = 0;
   __syncthreads();
-  for (int p = t; p < TK; p += 1024) {
-    int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  const int p1 = min(TK, (blockIdx.x + 1) * C);
+  for (int p0 = blockIdx.x * C; p0 < p1; p0 += 2048) {
+    int e8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + 256 * j + t;
+      e8[j] = p < p1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (e8[j] >= 0 && e8[j] < E) atomicAdd(&h[e8[j]], 1);
   }
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) { off[e] = run; run += hist[e]; }
-    off[E] = run;
-  }
-  __syncthreads();
-  for (int e = t; e < E; e += 1024) counts[e] = hist[e];
-  for (int e = t; e <= E; e += 1024) offsets[e] = off[e];
-  const int lane = t & 63, wave = t >> 6;
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = wave; e < E; e += 16) {
-    int base = off[e];
-    for (int c = 0; c < TK; c += 64) {
-      int p = c + lane;
-      bool m = p < TK && ids[p] == e;
-      unsigned long long mask = __ballot(m);
-      if (m) {
-        int r = base + __popcll(mask & below);
-        dst[p] = r;
-        src[r] = p / k;
+  for (int e = t; e < E; e += 256) cnt[(long long)blockIdx.x * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(1024) void group_scan_kernel(int nchunks, int E, int* __restrict__ cnt,
+                                                          int* __restrict__ counts,
+                                                          int* __restrict__ offsets) {
+  __shared__ long long wave_tmp[16];
+  const int t = threadIdx.x;
+  int tot = 0;
+  if (t < E) {
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {   // 8 loads in flight
+      int v8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v8[j] = c0 + j < nchunks ? cnt[(long long)(c0 + j) * E + t] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (c0 + j < nchunks) cnt[(long long)(c0 + j) * E + t] = tot;
+        tot += v8[j];
       }
-      base += __popcll(mask);
+    }
+  }
+  const int incl = block_incl_scan<1024, int>(tot, wave_tmp);
+  if (t < E) {
+    counts[t] = tot;
+    offsets[t] = incl - tot;
+  }
+  if (t == 1023) offsets[E] = incl;   // threads past E hold 0: incl is the total
+}
+
+// One chunk per workgroup of 4 waves; wave w ranks the chunk's quarter w, 64
+// pairs at a time: a ballot loop over the distinct experts of the 64 pairs
+// gives every lane its rank among the lanes below with the same expert and
+// the lowest such lane (the leader) the 64 pairs' count of that expert; the
+// leaders read and advance their experts' counters (distinct addresses) and
+// every lane takes its leader's base by a lane permute.  The chunk's first row
+// of expert e is offsets[e] + base[chunk][e]; base == nullptr: the only chunk,
+// whose expert bases come from a scan of its own counts, which also gives
+// counts and offsets.
+__global__ __launch_bounds__(256) void group_rank_kernel(const int* __restrict__ ids, int TK, int E,
+                                                         int C, const int* __restrict__ base,
+                                                         int* __restrict__ dst, int* __restrict__ counts,
+                                                         int* __restrict__ offsets) {
+  __shared__ int ctr[4][kMaxExperts];
+  __shared__ long long wave_tmp[16];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int q = C / 4;
+  const int s0 = min(TK, blockIdx.x * C + wave * q);
+  const int s1 = min(TK, s0 + q);
+  for (int i = t; i < 4 * kMaxExperts; i += 256) (&ctr[0][0])[i] = 0;
+  __syncthreads();
+  for (int p0 = s0; p0 < s1; p0 += 512) {
+    int e8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + 64 * j + lane;
+      e8[j] = p < s1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (e8[j] >= 0 && e8[j] < E) atomicAdd(&ctr[wave][e8[j]], 1);
+  }
+  __syncthreads();
+  if (base == nullptr) {
+    // experts 4t .. 4t + 3: chunk totals, a block scan of their sums, and the
+    // running prefix inside the thread's four
+    int tot4[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * t + i;
+      tot4[i] = e < E ? ctr[0][e] + ctr[1][e] + ctr[2][e] + ctr[3][e] : 0;
+      sum += tot4[i];
+    }
+    const int incl = block_incl_scan<256, int>(sum, wave_tmp);
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * t + i;
+      if (e < E) {
+        counts[e] = tot4[i];
+        offsets[e] = run;
+        for (int w = 0; w < 4; ++w) {
+          const int c = ctr[w][e];
+          ctr[w][e] = run;
+          run += c;
+        }
+      }
+    }
+    if (t == 255) offsets[E] = incl;
+  } else {
+    for (int e = t; e < E; e += 256) {   // per-wave bases from the chunk's base
+      int run = offsets[e] + base[(long long)blockIdx.x * E + e];
+      for (int w = 0; w < 4; ++w) {
+        const int c = ctr[w][e];
+        ctr[w][e] = run;
+        run += c;
+      }
+    }
+  }
+  __syncthreads();
+  int* my = ctr[wave];
+  for (int p0 = s0; p0 < s1; p0 += 512) {
+    int e8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + 64 * j + lane;
+      e8[j] = p < s1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + 64 * j + lane;
+      const int e = e8[j];
+      const bool valid = e >= 0 && e < E;
+      unsigned long long pending = __ballot(valid);
+      int rank = 0, leader = 0, n_e = 0;
+      // (selects, not branches: the loop body stays one basic block)
+      while (pending) {
+        const int ld = __builtin_ctzll(pending);
+        const int el = __builtin_amdgcn_readlane(e, ld);
+        const bool in = e == el;
+        const unsigned long long m = __ballot(in);
+        pending &= ~m;
+        const int rk = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        rank = in ? rk : rank;
+        leader = in ? ld : leader;
+        n_e = lane == ld ? __popcll(m) : n_e;
+      }
+      int b = 0;
+      if (valid && lane == leader) {
+        b = my[e];
+        my[e] = b + n_e;
+      }
+      b = __shfl(b, leader, 64);
+      if (valid) dst[p] = b + rank;
     }
   }
 }
 
-// xg[r] = x[src[r]]: one 16-byte chunk per thread.
-__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ x,
-                                                     const int* __restrict__ src, int R, int H,
-                                                     uint16_t* __restrict__ xg) {
+// src[dst[p]] = p / k for the grouped pairs p, and with x given the gathered
+// row xg[dst[p]] = x[p / k]: one wave per pair, 16 bytes per lane.
+__global__ __launch_bounds__(256) void group_scatter_kernel(const int* __restrict__ ids, int TK,
+                                                            int k, int E, const int* __restrict__ dst,
+                                                            int* __restrict__ src,
+                                                            const uint16_t* __restrict__ x, int H,
+                                                            uint16_t* __restrict__ xg) {
+  const int lane = threadIdx.x & 63;
   const int cpr = H >> 3;
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  long long total = (long long)R * cpr;
-  for (; i < total; i += (long long)gridDim.x * blockDim.x) {
-    int r = (int)(i / cpr), ch = (int)(i - (long long)r * cpr);
-    int s = src[r];
-    *reinterpret_cast<uint4*>(xg + (long long)r * H + ch * 8) =
-        *reinterpret_cast<const uint4*>(x + (long long)s * H + ch * 8);
+  for (int p = blockIdx.x * 4 + (threadIdx.x >> 6); p < TK; p += gridDim.x * 4) {
+    const int e = ids[p];
+    if (e < 0 || e >= E) continue;
+    const int r = dst[p], tok = p / k;
+    if (lane == 0) src[r] = tok;
+    if (x) {
+      const uint4* __restrict__ srow = reinterpret_cast<const uint4*>(x + (long long)tok * H);
+      uint4* __restrict__ drow = reinterpret_cast<uint4*>(xg + (long long)r * H);
+#pragma unroll 8
+      for (int c = lane; c < cpr; c += 64) drow[c] = srow[c];
+    }
   }
 }
 

@@ -15,7 +15,7 @@ namespace moe {
 
 template <int EPI, int BLAY>
 static void launch_dglu(const GemmArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((group_gemm_kernel<EPI, BLAY, AT_BF16, MOE_ACT>), dim3(grid), dim3(GM_NT), 0, s, a);
+  hipLaunchKernelGGL((group_gemm_kernel<EPI, BLAY, AT_BF16, MOE_ACT>), dim3(grid), dim3(64 * gm_waves(EPI, BLAY, AT_BF16)), 0, s, a);
 }
 
 moe_status_t MOE_CAT(launch_act_bwd_, MOE_ACT)(int kind, const GemmArgs& a, int grid,

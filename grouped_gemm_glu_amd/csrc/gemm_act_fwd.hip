@@ -15,7 +15,7 @@ namespace moe {
 
 template <int EPI, int AT>
 static void launch_glu(const GemmArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((group_gemm_kernel<EPI, BL_PACKED, AT, MOE_ACT>), dim3(grid), dim3(GM_NT), 0, s,
+  hipLaunchKernelGGL((group_gemm_kernel<EPI, BL_PACKED, AT, MOE_ACT>), dim3(grid), dim3(64 * gm_waves(EPI, BL_PACKED, AT)), 0, s,
                      a);
 }
 

@@ -7,7 +7,7 @@ namespace moe {
 
 template <int EPI, int BLAY>
 static moe_status_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((group_gemm_kernel<EPI, BLAY>), dim3(grid), dim3(GM_NT), 0, s, a);
+  hipLaunchKernelGGL((group_gemm_kernel<EPI, BLAY>), dim3(grid), dim3(64 * gm_waves(EPI, BLAY, AT_BF16)), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

@@ -9,10 +9,10 @@ namespace moe {
 
 moe_status_t launch_group_gemm_mx(const GemmArgs& a, bool a_e5, int grid, hipStream_t s) {
   if (a_e5)
-    hipLaunchKernelGGL((group_gemm_kernel<EPI_STORE, BL_PACKED, AT_MX_A5>), dim3(grid), dim3(GM_NT), 0,
+    hipLaunchKernelGGL((group_gemm_kernel<EPI_STORE, BL_PACKED, AT_MX_A5>), dim3(grid), dim3(64 * gm_waves(EPI_STORE, BL_PACKED, AT_MX_A5)), 0,
                        s, a);
   else
-    hipLaunchKernelGGL((group_gemm_kernel<EPI_STORE, BL_PACKED, AT_MX>), dim3(grid), dim3(GM_NT), 0,
+    hipLaunchKernelGGL((group_gemm_kernel<EPI_STORE, BL_PACKED, AT_MX>), dim3(grid), dim3(64 * gm_waves(EPI_STORE, BL_PACKED, AT_MX)), 0,
                        s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

@@ -9,8 +9,10 @@
 // a group is partial and handled by clamped loads and masked stores ([MEGA]
 // §5.3).
 //
-// Tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave owning
-// a 128 x 128 sub-tile as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16.  Operands
+// Tile 256 x 256 x 64.  The bf16 kernels on packed weights run 8 waves (two
+// per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles, 2 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 each; the others 4 waves in a 2 x 2 grid of
+// 128 x 128 sub-tiles (4 x 4 blocks).  Operands
 // are staged in LDS as [rows][64] bf16, 128 bytes per row, with the 16-byte
 // chunk index XOR-swizzled by ((r ^ (r >> 3)) & 7) so that the fragment reads
 // (8 consecutive rows, one chunk) and the transposed weight writes (rows 8
@@ -48,7 +50,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr int GM_BM = 256;
 constexpr int GM_BN = 256;
 constexpr int GM_BK = 64;
-constexpr int GM_NT = 256;
 constexpr int GM_TILE_BYTES = GM_BM * GM_BK * 2;              // one operand tile: 32 KB
 constexpr int GM_STAGE_BYTES = 2 * GM_TILE_BYTES;             // A + B
 constexpr int GM_MAIN_BYTES = 2 * GM_STAGE_BYTES;             // two stages: 128 KB
@@ -86,6 +87,18 @@ enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 // per 32 consecutive K values, consumed by the block-scaled MFMA); AT_MX_A5:
 // the same with e5m2 codes for A (a gradient) and e4m3 for B
 enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2 };
+
+// Waves per workgroup.  4: a 2 x 2 grid of waves, one per SIMD, each owning
+// a 128 x 128 sub-tile.  8: a 4 x 2 grid of 64 x 128 sub-tiles, two waves per
+// SIMD, so that one wave's MFMAs run while the other waits on its loads or at
+// the stage barrier (the bf16 step kernels on packed weights: 3-4% faster on
+// the DeepSeek-V3-like share, same results bit for bit).
+constexpr int gm_waves(int epi, int blay, int at) {
+  return (at == AT_BF16 && blay == BL_PACKED &&
+          (epi == EPI_GLU || epi == EPI_STORE || epi == EPI_DGLU))
+             ? 8
+             : 4;
+}
 
 struct GemmArgs {
   const uint16_t* A;        // [M_cap][K] grouped rows, K contiguous
@@ -200,12 +213,13 @@ __device__ __forceinline__ void store_bytes(uint8_t* dst, const uint32_t* w, int
 // col-wise: blocks of 32 rows starting at the tile's first row (a tile always
 // starts a block because tiles start at group row multiples of 256), scale
 // column scol0 + r / 32.
+template <int NT>
 __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, int ncols, int grow0,
                               int col0, const GemmArgs& p, int scol0) {
   const int t = threadIdx.x + opaque_zero();
   if (p.row_q) {
     const int nb = ncols >> 5;
-    for (int it = t; it < stg.rows() * nb; it += GM_NT) {
+    for (int it = t; it < stg.rows() * nb; it += NT) {
       int r = it / nb, cb = it - r * nb;
       if (r >= rows_valid) continue;
       float v[32];
@@ -230,7 +244,7 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
   }
   if (p.col_q) {
     const int nrb = (rows_valid + 31) >> 5;
-    for (int it = t; it < ncols * (stg.rows() >> 5); it += GM_NT) {
+    for (int it = t; it < ncols * (stg.rows() >> 5); it += NT) {
       int c = it % ncols, rb = it / ncols;
       if (rb >= nrb) continue;
       int nvalid = rows_valid - rb * 32;
@@ -283,11 +297,12 @@ __device__ __forceinline__ void fwht16(float (&v)[16]) {
 // at each group's first row); rows from rows_valid on count as zero, and row
 // i of every run is negated first when bit i of signs is set.  One item is
 // 4 columns x 16 rows, read as 16 conflict-free 8-byte rows.
+template <int NT>
 __device__ __forceinline__ float rht16_amax_stage(const Stg& stg, int rows_valid, uint32_t chunk_ok,
                                                   uint32_t signs) {
   const int t = threadIdx.x + opaque_zero();
   float amax = 0.0f;
-  for (int it = t; it < (stg.rows() / 16) * 64; it += GM_NT) {
+  for (int it = t; it < (stg.rows() / 16) * 64; it += NT) {
     const int ch = it & 63, r0 = (it >> 6) * 16;
     if (r0 >= rows_valid || !((chunk_ok >> (ch >> 4)) & 1u)) continue;
     uint2 w[16];
@@ -318,12 +333,13 @@ __device__ __forceinline__ float rht16_amax_stage(const Stg& stg, int rows_valid
 }
 
 // Coalesced store of a staged bf16 tile (ncols % 8 == 0 assumed per 8-chunk validity).
+template <int NT>
 __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
                                             int ncols_valid, int ncols_tile, uint16_t* dst,
                                             long long dst_ld) {
   const int t = threadIdx.x + opaque_zero();
   const int cpr = ncols_tile >> 3;  // 16-byte chunks per row
-  for (int it = t; it < stg.rows() * cpr; it += GM_NT) {
+  for (int it = t; it < stg.rows() * cpr; it += NT) {
     int r = it / cpr, ch = it - r * cpr;
     if (r < rows_valid && ch * 8 < ncols_valid) {
       uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
@@ -336,7 +352,7 @@ __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
 // ACT: the activation of the GLU and dGLU epilogues (one kernel per
 // activation, so the epilogue holds no dispatch); unused by the others.
 template <int EPI, int BLAY, int AT = AT_BF16, int ACT = ACT_SWIGLU>
-__global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_kernel(GemmArgs p) {
   // Operand rows are staged as 128-byte K slices whatever the type: 64 bf16
   // (4 k-steps of v_mfma_f32_32x32x16_bf16) or 128 e4m3 (2 k-steps of
   // v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8 stages also carry the tile's
@@ -359,6 +375,9 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   constexpr bool WG = EPI == EPI_WGRAD;
   static_assert(!WG || (BLAY == BL_KN && !MXT), "weight gradient: N-contiguous bf16 operands");
   constexpr bool KNR = BLAY == BL_KN && !WG;
+  constexpr int NW = gm_waves(EPI, BLAY, AT);   // waves per workgroup (4 or 8)
+  constexpr int NTH = 64 * NW;           // threads
+  static_assert(NW == 4 || (!WG && !MXT && !KNR), "8 waves: bf16 operands, K-contiguous B");
   // Two distinct stage arrays: the compiler can then see that the LDS-DMA
   // writes of the next stage never alias the fragment reads of the current
   // one, and does not wait for the prefetch before computing.
@@ -372,13 +391,13 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
 
-  build_group_scan<GM_NT>(gs, p.counts, p.E, p.M_cap, GM_BM, WG ? 0 : GM_BM / 2, p.offsets_out,
+  build_group_scan<NTH>(gs, p.counts, p.E, p.M_cap, GM_BM, WG ? 0 : GM_BM / 2, p.offsets_out,
                           p.status_out, blockIdx.x == 0);
   if (WG) {
     // Every expert owns the same number of output tiles but its tiles cost
     // m_e: hand them out largest group first (ties: lower id), the order kept
     // in mxs_off (the MX scale prefix is not needed here).
-    for (int ee = tid; ee < p.E; ee += GM_NT) {
+    for (int ee = tid; ee < p.E; ee += NTH) {
       const int ce = gs.row_off[ee + 1] - gs.row_off[ee];
       int rank = 0;
       for (int j = 0; j < p.E; ++j) {
@@ -460,14 +479,16 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     const int n0 = nt * GM_BN;
     const int nk_t = WG ? (m_e + 63) / 64 : nk;      // K-tiles of this tile
 
-    // The tile body for MI 32-row MFMA blocks per wave: MI = 4 is the 256-row
-    // tile (waves 128 x 128); a group's last m-tile with at most 128 valid
-    // rows runs with MI = 2 as a 128-row tile (waves 64 x 128), half the MFMA
-    // work of the padded 256-row tile.  Weight-gradient tiles are always full.
+    // The tile body for MI 32-row MFMA blocks per wave, NW / 2 wave rows:
+    // the 256-row tile (4 waves: MI = 4, waves 128 x 128; 8 waves: MI = 2,
+    // waves 64 x 128); a group's last m-tile with at most 128 valid rows runs
+    // with half the MI as a 128-row tile, half the MFMA work of the padded
+    // 256-row tile.  Weight-gradient tiles are always full.
     auto tile_body = [&](auto mic) {
     constexpr int MI = decltype(mic)::value;
     constexpr int HR = 32 * MI;                 // rows per wave row
-    constexpr int TBM = 2 * HR;                 // tile rows
+    constexpr int TBM = (NW / 2) * HR;          // tile rows
+    constexpr int SHR = TBM / 2;                // staged rows per LDS stage array
 
     // Per-tile opaque zero: main-loop addressing is recomputed for each tile,
     // so it is not live across the epilogue.
@@ -522,18 +543,17 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // direct global -> LDS of one ROWS x 64 operand tile (swizzled layout).
-    // Instruction j of wave w fills rows 8 (NJ w + j) .. + 7 (NJ = ROWS / 32);
+    // Instruction j of wave w fills rows 8 (NJ w + j) .. + 7 (NJ = ROWS / 8 NW);
     // lane (rl, pc) lands on row 8 (NJ w + j) + rl, physical chunk pc, so it
-    // fetches logical chunk pc ^ key(row), key = rl ^ (j & 3) (NJ is a
-    // multiple of 4).
+    // fetches logical chunk pc ^ key(row), key = rl ^ ((NJ w + j) & 3).
     const int rl_t = lane_t >> 3, pc_t = lane_t & 7;
     auto issue_tile = [&](auto rowsc, const rsrc_t& rs, uint8_t* lds_tile, uint32_t stride,
                           uint32_t koff) {
-      constexpr int NJ = decltype(rowsc)::value / 32;
+      constexpr int NJ = decltype(rowsc)::value / (8 * NW);
       const uint32_t vrow = (uint32_t)(wave * 8 * NJ + rl_t) * stride;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int c = pc_t ^ (rl_t ^ (j & 3));
+        const int c = pc_t ^ (rl_t ^ ((wave * NJ + j) & 3));
         const uint32_t voff = vrow + (uint32_t)(j * 8) * stride + (uint32_t)(c << 4);
         lds_dma16(rs, lds_tile + (wave * NJ + j) * 1024, voff, koff);
       }
@@ -545,8 +565,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // streams 1 KB contiguously
     auto issue_block = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t koff) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int blk = wave * 8 + j;
+      for (int j = 0; j < 32 / NW; ++j) {
+        const int blk = wave * (32 / NW) + j;
         lds_dma16(rs, lds_tile + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16), koff);
       }
     };
@@ -746,7 +766,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     // issued as a burst right after the barrier, the four waves' DMA
     // instructions queue at the address unit and hold up the MFMAs issued
     // behind them.
-    constexpr int NVM = WG ? 16 : TBM / 32 + 8;
+    constexpr int NVM = WG ? 16 : (TBM + GM_BN) / (8 * NW);
     auto mfma_step_dma = [&](int buf, int sset, int ks) {
       mfmas(buf, sset, ks);
       static_for<NMF>([&](auto gc) {
@@ -813,9 +833,11 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     //   tile column n = wn*128 + 32 j + 8 (r/4) + 4 (lane/32) + r%4,
     // i.e. each lane holds runs of 4 consecutive columns of one row.
     const int z0 = opaque_zero();
-    // this wave's rows (wm*128 ..) live in stage array wm
-    uint16_t* wstg = reinterpret_cast<uint16_t*>(wm ? lds1 : lds0) + z0;
+    // this wave's rows (wm*HR ..) live in stage array 0 (tile rows below SHR)
+    // or 1, from staged row slm - lm on
+    uint16_t* wstg = reinterpret_cast<uint16_t*>(wm * HR >= SHR ? lds1 : lds0) + z0;
     const int lm = (lane & 31) + z0;
+    const int slm = (wm * HR) % SHR + lm;
     const int ln = 4 * (lane >> 5) + z0;
     float rsc[MI];
 #pragma unroll
@@ -918,7 +940,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       // stage the pre-activation: gate at columns 0..127, up at 128..255
       auto stage_preact = [&](int i, int jj, int pp, int h, const float (&g)[4], const float (&u)[4]) {
         const int c = wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
-        uint16_t* srow = wstg + (32 * i + lm) * GM_STG_LD_256;
+        uint16_t* srow = wstg + (32 * i + slm) * GM_STG_LD_256;
         *reinterpret_cast<uint2*>(srow + c) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
         *reinterpret_cast<uint2*>(srow + 128 + c) =
             make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
@@ -958,7 +980,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
                 }
                 if (MXO) {   // y staged for the MXFP8 round (128 columns)
                   const int c = wn * 64 + 32 * jj + 8 * (2 * pp + h) + 4 * lh;
-                  *reinterpret_cast<uint2*>(wstg + (32 * i + lm) * GM_STG_LD_128 + c) =
+                  *reinterpret_cast<uint2*>(wstg + (32 * i + slm) * GM_STG_LD_128 + c) =
                       make_uint2(yw[h][0], yw[h][1]);
                 } else if (p.preact) {
                   stage_preact(i, jj, pp, h, g, u);
@@ -980,11 +1002,11 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       auto store_preact = [&]() {
         __syncthreads();
         const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0,
-                      GM_STG_LD_256, HR};
+                      GM_STG_LD_256, SHR};
         uint16_t* prow0 = p.preact + (long long)row0 * ld2 + nt * 128;
         const int t = tid + z0;
 #pragma unroll 4
-        for (int it = t; it < TBM * 32; it += GM_NT) {
+        for (int it = t; it < TBM * 32; it += NTH) {
           const int r = it >> 5, ch = it & 31, cc = (ch & 15) * 8;
           if (r < rows_valid && cc < cvalid_n) {
             const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
@@ -1018,8 +1040,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       }
       if (MXO) {
         __syncthreads();
-        mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0,
-                          GM_STG_LD_128, HR},
+        mx_from_stage<NTH>(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0,
+                          GM_STG_LD_128, SHR},
                       rows_valid, cvalid_n, row0, nt * 128, p, gs.mxs_off[e] + mt * 8);
         __syncthreads();
       } else if (p.preact) {
@@ -1034,7 +1056,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       //          lane group, all 16 of a row block's loads in flight together.
       constexpr bool FWD = EPI == EPI_ACT;
       const int ld = GM_STG_LD_256;
-      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR};
+      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, SHR};
       const int cvalid_n = min(GM_BN, p.N - n0);
       const uint16_t* bias_e = (FWD && p.ep.bias) ? p.ep.bias + (long long)e * p.N + n0 : nullptr;
       const rsrc_t rsZ = make_rsrc(p.preact + (long long)row0 * p.N,
@@ -1086,26 +1108,26 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
               if (FWD && RD == 0 && p.ep.amax_out && m < rows_valid && n < cvalid_n)
                 ymax = fmaxf(ymax, fmaxf(fmaxf(fabsf(__uint_as_float(w.x << 16)), fabsf(__uint_as_float(w.x & 0xFFFF0000u))),
                                          fmaxf(fabsf(__uint_as_float(w.y << 16)), fabsf(__uint_as_float(w.y & 0xFFFF0000u)))));
-              *reinterpret_cast<uint2*>(wstg + (32 * i + lm) * ld + n) = w;
+              *reinterpret_cast<uint2*>(wstg + (32 * i + slm) * ld + n) = w;
             }
         }
       };
       stage_round(std::integral_constant<int, 0>{});
       __syncthreads();
       if (p.C)
-        store_stage(stg, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
-      if (p.row_q || p.col_q) mx_from_stage(stg, rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
+        store_stage<NTH>(stg, rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
+      if (p.row_q || p.col_q) mx_from_stage<NTH>(stg, rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
       if (!FWD && p.ep.amax_out) {   // rotated amax of dz^T over the tile's valid 64-column chunks
         uint32_t ok = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) ok |= (n0 + 64 * k < p.N ? 1u : 0u) << k;
-        ymax = rht16_amax_stage(stg, rows_valid, ok, p.ep.rht_signs);
+        ymax = rht16_amax_stage<NTH>(stg, rows_valid, ok, p.ep.rht_signs);
       }
       __syncthreads();
       if (FWD && p.preact) {
         stage_round(std::integral_constant<int, 1>{});
         __syncthreads();
-        store_stage(stg, rows_valid, cvalid_n, GM_BN, p.preact + (long long)row0 * p.N + n0, p.N);
+        store_stage<NTH>(stg, rows_valid, cvalid_n, GM_BN, p.preact + (long long)row0 * p.N + n0, p.N);
         __syncthreads();
       }
       if (p.ep.amax_out) wave_amax_atomic(ymax, p.ep.amax_out, lane);
@@ -1119,7 +1141,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_sched_barrier(0);
             const int n = wn * 128 + 32 * j + 8 * q + ln;
-            *reinterpret_cast<uint2*>(wstg + (32 * i + lm) * ld + n) =
+            *reinterpret_cast<uint2*>(wstg + (32 * i + slm) * ld + n) =
                 make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                            pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
           }
@@ -1127,10 +1149,10 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       __syncthreads();
       const int cvalid_n = min(GM_BN, p.N - n0);
       if (p.C)
-        store_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR},
+        store_stage<NTH>(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, SHR},
                     rows_valid, cvalid_n, GM_BN, p.C + (long long)row0 * p.N + n0, p.N);
       if (p.row_q || p.col_q)
-        mx_from_stage(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR},
+        mx_from_stage<NTH>(Stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, SHR},
                       rows_valid, cvalid_n, row0, n0, p, gs.mxs_off[e] + mt * 8);
       __syncthreads();
     } else {  // EPI_DGLU: acc = G = dL/dy for columns n0 .. n0+255 of I
@@ -1148,14 +1170,14 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       // 64 columns each, and goes out as four 128-byte row segments.
       const rsrc_t rsPre = make_rsrc(p.preact + (long long)row0 * ld2,
                                      (long long)rows_valid * ld2 * 2);
-      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, HR};
+      const Stg stg{reinterpret_cast<uint16_t*>(lds0) + z0, reinterpret_cast<uint16_t*>(lds1) + z0, ld, SHR};
       // d(row_scale): per block j and row block, each lane sums G * a(g_c) *
       // u_c (dL/dy times the unscaled y) over its 16 columns and adds that
       // to the row's LDS slot; after the tile one global atomic per row
       constexpr bool PG = EPI == EPI_DGLU_G;
       const bool want_drs = PG && p.ep.drs_out != nullptr;
       if (want_drs) {
-        for (int r = tid; r < TBM; r += GM_NT) drs_lds[r] = 0.0f;
+        for (int r = tid; r < TBM; r += NTH) drs_lds[r] = 0.0f;
         __syncthreads();
       }
       auto do_block = [&](auto jc) {
@@ -1176,7 +1198,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          uint16_t* srow = wstg + (32 * i + lm) * ld;
+          uint16_t* srow = wstg + (32 * i + slm) * ld;
           float drs_part = 0.0f;
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
@@ -1245,7 +1267,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         auto chunk_col = [&](int k) { return n0 + 128 * (k & 1) + 64 * round; };
         if (p.ep.amax_out) {
           const uint32_t ok = (chunk_col(0) < p.I ? 5u : 0u) | (chunk_col(1) < p.I ? 10u : 0u);
-          hmax = fmaxf(hmax, rht16_amax_stage(stg, rows_valid, ok, p.ep.rht_signs));
+          hmax = fmaxf(hmax, rht16_amax_stage<NTH>(stg, rows_valid, ok, p.ep.rht_signs));
         }
         if (PG && p.ep.dbias_out) {
           // d(bias): thread t sums staged column t (chunk t / 64) over the
@@ -1257,7 +1279,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const uint16_t* col = (hh ? stg.h1 : stg.h0) + k * 64 + (t & 63);
-              const int nr = min(HR, rows_valid - hh * HR);
+              const int nr = min(SHR, rows_valid - hh * SHR);
               int r = 0;
               for (; r + 8 <= nr; r += 8) {
 #pragma unroll
@@ -1272,7 +1294,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
         if (p.C) {
           const int t = tid + z0;
 #pragma unroll 4
-          for (int it = t; it < TBM * 32; it += GM_NT) {
+          for (int it = t; it < TBM * 32; it += NTH) {
             const int r = it >> 5, k = (it >> 3) & 3, pc = it & 7;
             const int c = chunk_col(k) + pc * 8;
             if (r < rows_valid && c < p.I) {
@@ -1286,7 +1308,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
           for (int k = 0; k < 4; ++k) {
             const int nv = min(64, p.I - chunk_col(k));
             if (nv > 0)
-              mx_from_stage(Stg{stg.h0 + k * 64, stg.h1 + k * 64, ld, HR}, rows_valid, nv, row0,
+              mx_from_stage<NTH>(Stg{stg.h0 + k * 64, stg.h1 + k * 64, ld, SHR}, rows_valid, nv, row0,
                             (k < 2 ? 0 : p.I) + chunk_col(k), p, gs.mxs_off[e] + mt * 8);
           }
         }
@@ -1294,7 +1316,7 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
       }
       if (p.ep.amax_out) wave_amax_atomic(hmax, p.ep.amax_out, lane);
       if (want_drs) {   // (the rounds end with a barrier: every LDS add is in)
-        for (int r = tid; r < rows_valid; r += GM_NT) atomicAdd(p.ep.drs_out + row0 + r, drs_lds[r]);
+        for (int r = tid; r < rows_valid; r += NTH) atomicAdd(p.ep.drs_out + row0 + r, drs_lds[r]);
         __syncthreads();
       }
     }
@@ -1302,8 +1324,8 @@ __global__ __launch_bounds__(GM_NT, 1) void group_gemm_kernel(GemmArgs p) {
     if constexpr (WG) {
       tile_body(std::integral_constant<int, 4>{});
     } else {
-      if (rows_valid <= 128) tile_body(std::integral_constant<int, 2>{});
-      else tile_body(std::integral_constant<int, 4>{});
+      if (rows_valid <= 128) tile_body(std::integral_constant<int, 8 / NW>{});
+      else tile_body(std::integral_constant<int, 16 / NW>{});
     }
   }
 }

@@ -246,8 +246,10 @@ moe_status_t moe_unpack_gate_up(const void* w1_packed, int E, int H, int I, void
  * row of pair (t, j); src [T*k], the token of each grouped row.  Within an
  * expert the pairs keep ascending (t, j) order, so the result is unique and
  * deterministic.  If x (bf16 [T][H]) and xg (bf16 [T*k][H]) are given, xg
- * receives the gathered rows xg[r] = x[src[r]].  Requires k <= E <= 1024,
- * k <= 16, T*k < 2^31, H % 8 == 0. */
+ * receives the gathered rows xg[r] = x[src[r]].  Given topk_ids outside
+ * [0, E) are not grouped: their dst entries and the rows of src and xg from
+ * offsets[E] on are left as they were.  Requires k <= E <= 1024, k <= 16,
+ * T*k < 2^31, H % 8 == 0. */
 moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T, int E, int k,
                              int32_t* topk_ids_out, int32_t* counts, int32_t* offsets,
                              int32_t* dst, int32_t* src, const void* x, int H, void* xg,

@@ -89,12 +89,30 @@ def _route_case(G, logits, k, x=None):
             src.cpu().numpy(), None if xg is None else host_bits(xg))
 
 
-@pytest.mark.parametrize("case", ["tiny", "tiny_empty", "gptoss", "ties"])
+@pytest.mark.parametrize("case", ["tiny", "tiny_empty", "gptoss", "ties", "wide", "specials"])
 def test_route_group_bit_exact(G, case):
-    if case == "ties":
+    if case == "specials":
+        # NaN ranks below every number (numpy's sort order, as in the oracle),
+        # infinities and signed zeros tie-break by expert id
+        rng = np.random.default_rng(9)
+        logits = rng.integers(-2, 3, size=(500, 40)).astype(np.float32)
+        pick = rng.random(logits.shape)
+        logits[pick < 0.05] = np.nan
+        logits[(pick >= 0.05) & (pick < 0.1)] = np.inf
+        logits[(pick >= 0.1) & (pick < 0.15)] = -np.inf
+        logits[(pick >= 0.15) & (pick < 0.2)] = -0.0
+        logits[7] = np.nan                      # a token with only NaN logits
+        x, k = None, 5
+    elif case == "ties":
         rng = np.random.default_rng(5)
         logits = rng.integers(-2, 3, size=(300, 9)).astype(np.float32)
         x, k = None, 3
+    elif case == "wide":
+        # 1000 experts (more than a wave has lanes), 3001 x 7 pairs (the
+        # per-wave segments end inside a 64-pair chunk), skewed logits
+        rng = np.random.default_rng(17)
+        logits = (rng.standard_normal((3001, 1000)) + np.linspace(0, 3, 1000)).astype(np.float32)
+        x, k = None, 7
     elif case == "gptoss":
         d = W.gptoss(with_weights=False)
         logits, x, k = d["logits"], d["x"], d["k"]
