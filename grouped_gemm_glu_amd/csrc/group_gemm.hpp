@@ -91,11 +91,11 @@ enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2 };
 // Waves per workgroup.  4: a 2 x 2 grid of waves, one per SIMD, each owning
 // a 128 x 128 sub-tile.  8: a 4 x 2 grid of 64 x 128 sub-tiles, two waves per
 // SIMD, so that one wave's MFMAs run while the other waits on its loads or at
-// the stage barrier (the bf16 step kernels on packed weights: 3-4% faster on
+// the stage barrier (the bf16 kernels on packed weights: 3-4% faster on
 // the DeepSeek-V3-like share, same results bit for bit).
 constexpr int gm_waves(int epi, int blay, int at) {
   return (at == AT_BF16 && blay == BL_PACKED &&
-          (epi == EPI_GLU || epi == EPI_STORE || epi == EPI_DGLU))
+          (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU))
              ? 8
              : 4;
 }
@@ -243,20 +243,33 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
     }
   }
   if (p.col_q) {
+    // items of two adjacent columns x 32 rows: one 4-byte LDS read per row
+    // (ncols is a multiple of 32); the row blocks of a column pair are
+    // consecutive items, so neighbouring lanes store neighbouring 32-byte
+    // pieces of a column
     const int nrb = (rows_valid + 31) >> 5;
-    for (int it = t; it < ncols * (stg.rows() >> 5); it += NT) {
-      int c = it % ncols, rb = it / ncols;
+    const int nc2 = ncols >> 1;
+    const int nrbt = stg.rows() >> 5;
+    for (int it = t; it < nc2 * nrbt; it += NT) {
+      const int rb = it % nrbt, c2 = it / nrbt;
       if (rb >= nrb) continue;
       int nvalid = rows_valid - rb * 32;
       if (nvalid > 32) nvalid = 32;
-      float v[32];
+      float v0[32], v1[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(stg.row(rb * 32 + i)[c]);
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(stg.row(rb * 32 + i) + 2 * c2);
+        v0[i] = __uint_as_float(w2 << 16);
+        v1[i] = __uint_as_float(w2 & 0xFFFF0000u);
+      }
       uint32_t w[8];
-      uint8_t sb = mx_quant32(v, nvalid, w, p.mx_e5 != 0);
-      long long gc = col0 + c;
+      const long long gc = col0 + 2 * c2;
+      uint8_t sb = mx_quant32(v0, nvalid, w, p.mx_e5 != 0);
       store_bytes(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[gc * p.col_s_ld + scol0 + rb] = sb;
+      sb = mx_quant32(v1, nvalid, w, p.mx_e5 != 0);
+      store_bytes(p.col_q + (gc + 1) * p.M_cap + grow0 + rb * 32, w, nvalid);
+      p.col_s[(gc + 1) * p.col_s_ld + scol0 + rb] = sb;
     }
   }
 }
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   constexpr bool KNR = BLAY == BL_KN && !WG;
   constexpr int NW = gm_waves(EPI, BLAY, AT);   // waves per workgroup (4 or 8)
   constexpr int NTH = 64 * NW;           // threads
-  static_assert(NW == 4 || (!WG && !MXT && !KNR), "8 waves: bf16 operands, K-contiguous B");
+  static_assert(NW == 4 || (!WG && !MXT && !KNR), "8 waves: bf16 operands, packed B");
   // Two distinct stage arrays: the compiler can then see that the LDS-DMA
   // writes of the next stage never alias the fragment reads of the current
   // one, and does not wait for the prefetch before computing.
