@@ -199,6 +199,7 @@ def main():
 
     # ---- the same step as one hipGraph replay (no host sync inside)
     graph_ms = None
+    graph_pair = None
     try:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -218,6 +219,10 @@ def main():
         b.record()
         torch.cuda.synchronize()
         graph_ms = a.elapsed_time(b) / args.steps
+        # the same comparison interleaved (same clock and thermal state)
+        pg = paired_ms(torch, {"eager": step, "graph": g.replay})
+        graph_pair = {"eager_ms": round(pg["eager"], 4), "graph_ms": round(pg["graph"], 4),
+                      "timing": "interleaved, best of 3 rounds of 10"}
     except Exception as exc:  # reported, never hides the eager number
         log(f"graph capture failed: {exc!r}")
 
@@ -307,6 +312,7 @@ def main():
                      "algorithmic_flops_per_launch": fc1_flops},
         "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "graph_vs_eager": graph_pair,
         "unfused_b1": b1,
         "secondary": extra,
         "cpu_baseline": cpu,

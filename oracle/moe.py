@@ -68,15 +68,33 @@ def route_topk(logits: np.ndarray, k: int):
         # sort by (-logit, expert id): lexsort sorts by the last key first
         order = np.lexsort((expert_idx, -logits[t].astype(np.float64)))
         ids[t] = order[:k]
-    flat = ids.reshape(-1)
-    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    counts, offsets, dst, src = group_pairs(ids, E)
+    return ids, counts, offsets, dst, src
+
+
+def group_pairs(ids: np.ndarray, E: int):
+    """Contiguous per-expert grouping of the (token, slot) pairs of ids [T][k]
+    ([MEGA] §4.3): expert e owns grouped rows [offsets[e], offsets[e+1]), its
+    pairs in ascending (t, j) order.  Pairs whose id lies outside [0, E) are
+    not grouped: their dst is -1 and they own no row.
+
+    Returns counts [E], offsets [E+1], dst [T][k] and src [offsets[E]] (the
+    token of each grouped row).
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat = ids.reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int32)
     offsets = np.zeros(E + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(counts)
-    pair_order = np.argsort(flat, kind="stable")     # grouped row r holds pair pair_order[r]
-    dst = np.empty(T * k, dtype=np.int32)
-    dst[pair_order] = np.arange(T * k, dtype=np.int32)
+    # grouped row r holds pair pair_order[r]: the valid pairs sorted stably by expert
+    vidx = np.flatnonzero(valid)
+    pair_order = vidx[np.argsort(flat[valid], kind="stable")]
+    dst = np.full(T * k, -1, dtype=np.int32)
+    dst[pair_order] = np.arange(len(pair_order), dtype=np.int32)
     src = (pair_order // k).astype(np.int32)
-    return ids, counts, offsets, dst.reshape(T, k), src
+    return counts, offsets, dst.reshape(T, k), src
 
 
 def exclusive_offsets(counts) -> np.ndarray:

@@ -128,6 +128,36 @@ def test_route_group_bit_exact(G, case):
         assert np.array_equal(xg, O.gather_rows(x, rsrc))
 
 
+def test_route_group_given_ids_with_invalid_entries(G):
+    # caller-given top-k ids with some outside [0, E): those pairs are not
+    # grouped, their dst entries and the rows of src and xg from offsets[E] on
+    # stay as they were
+    import torch
+    rng = np.random.default_rng(23)
+    T, E, k, H = 5000, 12, 3, 64           # 15000 pairs: several grouping chunks
+    ids_h = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+    ids_h[rng.random((T, k)) < 0.01] = 4096
+    x = rng.integers(0, 2 ** 16, size=(T, H)).astype(np.uint16)
+    d_ids = torch.from_numpy(ids_h).cuda()
+    out_ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offs = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    dst = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    src = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    xg = torch.full((T * k, H), 0x1234, dtype=torch.int16, device="cuda")
+    G.moe_route_group(None, d_ids, T, E, k, out_ids, counts, offs, dst, src, dev_bits(x), H, xg)
+    _sync()
+    rcounts, roffs, rdst, rsrc = O.group_pairs(ids_h, E)
+    n = int(roffs[-1])
+    assert np.array_equal(out_ids.cpu().numpy(), ids_h)
+    assert np.array_equal(counts.cpu().numpy(), rcounts) and np.array_equal(offs.cpu().numpy(), roffs)
+    assert np.array_equal(dst.cpu().numpy(), np.where(rdst < 0, -7, rdst))
+    s_d = src.cpu().numpy()
+    assert np.array_equal(s_d[:n], rsrc) and np.all(s_d[n:] == -7)
+    xg_d = host_bits(xg)
+    assert np.array_equal(xg_d[:n], O.gather_rows(x, rsrc)) and np.all(xg_d[n:] == 0x1234)
+
+
 # ---------------------------------------------------------------- FC1 + GLU
 def _fc1_gpu(G, x, counts, w1, I, ep_kw, m_cap=None, preact=True, mx=False, bias=None,
              row_scale=None, cu_margin=0, amax_init=None):

@@ -52,6 +52,28 @@ def test_route_matches_bruteforce(T, E, k, seed):
     assert dst.tolist() == bdst and src.tolist() == bsrc
 
 
+@pytest.mark.parametrize("T,E,k,seed", [(9, 5, 3, 0), (40, 7, 2, 1), (1, 3, 1, 2)])
+def test_group_pairs_with_invalid_ids_bruteforce(T, E, k, seed):
+    # ids outside [0, E) (negative, E, far above) are left out of the grouping
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)
+    ids[0, 0] = 1000
+    counts, off, dst, src = O.group_pairs(ids, E)
+    rows = []                                  # (expert, t, j) in grouped order
+    for e in range(E):
+        for t in range(T):
+            for j in range(k):
+                if ids[t, j] == e:
+                    rows.append((e, t, j))
+    assert counts.tolist() == [sum(1 for r in rows if r[0] == e) for e in range(E)]
+    assert off.tolist() == [sum(1 for r in rows if r[0] < e) for e in range(E + 1)]
+    assert src.tolist() == [t for _, t, _ in rows]
+    bdst = [[-1] * k for _ in range(T)]
+    for r, (_, t, j) in enumerate(rows):
+        bdst[t][j] = r
+    assert dst.tolist() == bdst
+
+
 def test_route_invariants_gptoss():
     d = W.gptoss(with_weights=False)
     ids, counts, off, dst, src = O.route_topk(d["logits"], d["k"])
