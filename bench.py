@@ -246,6 +246,37 @@ def main():
               "fused_speedup": round(pm["b1"] / pm["fused"], 3),
               "timing": "interleaved, best of 3 rounds of 10"}
         del w1t_plain, z
+        # the backward counterpart: dgrad GroupGemm writing dL/dy in bf16, then
+        # the unfused dGLU pass (and, with MXFP8 outputs, the standalone
+        # quantize/transpose of dgu), against the fused dgrad + dGLU
+        gmat = torch.empty((M, I), dtype=torch.int16, device=dev)
+        op_dy2 = G.operand(dy2)
+        dq = torch.empty((M, 2 * I), dtype=torch.uint8, device=dev)
+        ds = torch.empty((M, 2 * I // 32), dtype=torch.uint8, device=dev)
+        dcq = torch.empty((2 * I, M), dtype=torch.uint8, device=dev)
+        dcs = torch.empty((2 * I, (M + 31) // 32 + E), dtype=torch.uint8, device=dev)
+        mx_dgu = G.mx_out(row_q=dq, row_s=ds, col_q=dcq, col_s=dcs)
+
+        def b1_bwd():
+            G.moe_group_gemm_quant(op_dy2, op_w2d, I, H, grp, gmat)
+            G.moe_dglu_unfused(gmat, pre, grp, I, ep, dgu)
+
+        def b1_bwd_mx():
+            b1_bwd()
+            G.moe_mxfp8_quantize(dgu, M, 2 * I, grp, mx_dgu)
+
+        def fused_bwd_mx():
+            G.moe_group_gemm_dglu_bwd(dy2, op_w2d, H, I, grp, pre, ep, dgu, mx_dgu)
+
+        pb = paired_ms(torch, {"fused": dglu, "b1": b1_bwd, "fused_mx": fused_bwd_mx,
+                               "b1_mx": b1_bwd_mx})
+        b1["dgrad_dglu_fused_ms"] = round(pb["fused"], 4)
+        b1["dgrad_dglu_unfused_ms"] = round(pb["b1"], 4)
+        b1["dgrad_dglu_fused_speedup"] = round(pb["b1"] / pb["fused"], 3)
+        b1["dgrad_dglu_mx_fused_ms"] = round(pb["fused_mx"], 4)
+        b1["dgrad_dglu_mx_unfused_ms"] = round(pb["b1_mx"], 4)
+        b1["dgrad_dglu_mx_fused_speedup"] = round(pb["b1_mx"] / pb["fused_mx"], 3)
+        del gmat, dq, ds, dcq, dcs
 
     fc1_tflops = fc1_flops / (fc1_ms * 1e-3) / 1e12
     value = step_flops / (ms_per_step * 1e-3) / 1e12

@@ -80,6 +80,7 @@ _SIGS = {
                               ctypes.POINTER(GroupsT), _P, ctypes.POINTER(MxOutT), _I, _P], _I),
     "moe_group_gemm_wgrad": ([_P, _P, _I, _I, ctypes.POINTER(GroupsT), _P, _I, _I, _P], _I),
     "moe_glu_unfused": ([_P, ctypes.POINTER(GroupsT), _I, ctypes.POINTER(EpilogueT), _P, _P], _I),
+    "moe_dglu_unfused": ([_P, _P, ctypes.POINTER(GroupsT), _I, ctypes.POINTER(EpilogueT), _P, _P], _I),
     "moe_mxfp8_quantize": ([_P, _I, _I, ctypes.POINTER(GroupsT), ctypes.POINTER(MxOutT), _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -262,6 +263,12 @@ def moe_glu_unfused(z, grp: GroupsT, I, ep: EpilogueT, y, stream=None):
     _check("moe_glu_unfused",
            _lib.moe_glu_unfused(_ptr(z), ctypes.byref(grp), I, ctypes.byref(ep), _ptr(y),
                                 _stream(stream)))
+
+
+def moe_dglu_unfused(g, z, grp: GroupsT, I, ep: EpilogueT, dgu, stream=None):
+    _check("moe_dglu_unfused",
+           _lib.moe_dglu_unfused(_ptr(g), _ptr(z), ctypes.byref(grp), I, ctypes.byref(ep), _ptr(dgu),
+                                 _stream(stream)))
 
 
 def moe_mxfp8_quantize(v, R, C, grp: Optional[GroupsT], mx: MxOutT, stream=None):

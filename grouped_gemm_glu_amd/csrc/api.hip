@@ -508,6 +508,24 @@ moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+moe_status_t moe_dglu_unfused(const void* g, const void* z, const moe_groups_t* groups, int I,
+                              const moe_epilogue_t* ep, void* dgu, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!g || !z || !dgu || !ep) return MOE_ERR_NULL;
+  if (I < 64 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if (ep->gated != 1) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(g) || !aligned16(z) || !aligned16(dgu)) return MOE_ERR_ALIGN;
+  EpiParams e;
+  if ((st = fill_epilogue(ep, &e)) != MOE_OK) return st;
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  hipLaunchKernelGGL(dglu_unfused_kernel, dim3(cus * 8), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(z), groups->counts,
+                     groups->E, groups->M_cap, I, e, static_cast<uint16_t*>(dgu));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 moe_status_t moe_mxfp8_quantize(const void* v, int R, int C, const moe_groups_t* groups,
                                 const moe_mx_out_t* mx, void* stream) {
   if (!v || !mx) return MOE_ERR_NULL;

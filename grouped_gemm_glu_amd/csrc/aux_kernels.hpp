@@ -332,9 +332,19 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(const int* __restric
 }
 
 // ---------------------------------------------------------------- unfused GLU
-// y = GLU epilogue of the plain-order FC1 output z [M_cap][2I] (+ bias), one
-// 8-column chunk per thread per step; rows beyond the groups are skipped.
-// Each workgroup scans the counts to find row ranges and experts.
+// The unfused baseline passes (B1): each workgroup scans the counts to find
+// the routed rows (and a row's expert for the bias), then takes rows
+// blockIdx.x, blockIdx.x + gridDim.x, ..., one 8-column chunk per thread.
+__device__ __forceinline__ int expert_of_row(const GroupScan& gs, int E, int r) {
+  int lo = 0, hi = E;   // last e with row_off[e] <= r (and rows in it)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (gs.row_off[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// y = GLU epilogue of the plain-order FC1 output z [M_cap][2I] (+ bias).
 __global__ __launch_bounds__(256) void glu_unfused_kernel(const uint16_t* __restrict__ z,
                                                           const int* __restrict__ counts, int E,
                                                           int M_cap, int I, EpiParams ep,
@@ -343,44 +353,84 @@ __global__ __launch_bounds__(256) void glu_unfused_kernel(const uint16_t* __rest
   build_group_scan<256>(gs, counts, E, M_cap, 1, 0, nullptr, nullptr, false);
   const int M = gs.row_off[E];
   const int cpr = I >> 3;
-  long long total = (long long)M * cpr;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (long long)gridDim.x * 256) {
-    int r = (int)(i / cpr), ch = (int)(i - (long long)r * cpr);
+  for (int r = blockIdx.x; r < M; r += gridDim.x) {
     const uint16_t* zr = z + (long long)r * 2 * I;
-    uint4 gv = *reinterpret_cast<const uint4*>(zr + ch * 8);
-    uint4 uv = *reinterpret_cast<const uint4*>(zr + I + ch * 8);
-    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(&gv);
-    const uint16_t* u16 = reinterpret_cast<const uint16_t*>(&uv);
-    float bg[8] = {0, 0, 0, 0, 0, 0, 0, 0}, bu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (ep.bias) {
-      int lo = 0, hi = E;  // expert of row r: last e with row_off[e] <= r and rows in it
-      while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (gs.row_off[mid] <= r) lo = mid; else hi = mid;
+    const uint16_t* b = ep.bias ? ep.bias + (long long)expert_of_row(gs, E, r) * 2 * I : nullptr;
+    const float rs = ep.row_scale ? ep.row_scale[r] : 1.0f;
+    for (int ch = threadIdx.x; ch < cpr; ch += 256) {
+      uint4 gv = *reinterpret_cast<const uint4*>(zr + ch * 8);
+      uint4 uv = *reinterpret_cast<const uint4*>(zr + I + ch * 8);
+      const uint16_t* g16 = reinterpret_cast<const uint16_t*>(&gv);
+      const uint16_t* u16 = reinterpret_cast<const uint16_t*>(&uv);
+      float bg[8] = {0, 0, 0, 0, 0, 0, 0, 0}, bu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (b) {
+        uint4 bgv = *reinterpret_cast<const uint4*>(b + ch * 8);
+        uint4 buv = *reinterpret_cast<const uint4*>(b + I + ch * 8);
+        const uint16_t* bg16 = reinterpret_cast<const uint16_t*>(&bgv);
+        const uint16_t* bu16 = reinterpret_cast<const uint16_t*>(&buv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) { bg[q] = bf16_to_f32(bg16[q]); bu[q] = bf16_to_f32(bu16[q]); }
       }
-      const uint16_t* b = ep.bias + (long long)lo * 2 * I;
-      uint4 bgv = *reinterpret_cast<const uint4*>(b + ch * 8);
-      uint4 buv = *reinterpret_cast<const uint4*>(b + I + ch * 8);
-      const uint16_t* bg16 = reinterpret_cast<const uint16_t*>(&bgv);
-      const uint16_t* bu16 = reinterpret_cast<const uint16_t*>(&buv);
+      uint4 out;
+      uint16_t* o16 = reinterpret_cast<uint16_t*>(&out);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) { bg[q] = bf16_to_f32(bg16[q]); bu[q] = bf16_to_f32(bu16[q]); }
+      for (int q = 0; q < 8; ++q) {
+        float g = bf16_to_f32(g16[q]) + bg[q];
+        float u = bf16_to_f32(u16[q]) + bu[q];
+        float gc = fminf(fmaxf(g, ep.gate_lo), ep.gate_hi);
+        float uc = fminf(fmaxf(u, ep.up_lo), ep.up_hi) + ep.up_offset;
+        float v = act_fwd(ep.act, gc, ep.alpha) * uc;
+        if (ep.row_scale) v *= rs;
+        o16[q] = f32_to_bf16(v);
+      }
+      *reinterpret_cast<uint4*>(y + (long long)r * I + ch * 8) = out;
     }
-    float rs = ep.row_scale ? ep.row_scale[r] : 1.0f;
-    uint4 out;
-    uint16_t* o16 = reinterpret_cast<uint16_t*>(&out);
+  }
+}
+
+// d(gate | up) [M_cap][2I] from dL/dy G [M_cap][I] (bf16, the plain dgrad
+// GroupGemm's output) and the saved pre-activation z [M_cap][2I]: the same
+// arithmetic as the fused dGLU epilogue, on the bf16-rounded G.
+__global__ __launch_bounds__(256) void dglu_unfused_kernel(const uint16_t* __restrict__ G,
+                                                           const uint16_t* __restrict__ z,
+                                                           const int* __restrict__ counts, int E,
+                                                           int M_cap, int I, EpiParams ep,
+                                                           uint16_t* __restrict__ dgu) {
+  __shared__ GroupScan gs;
+  build_group_scan<256>(gs, counts, E, M_cap, 1, 0, nullptr, nullptr, false);
+  const int M = gs.row_off[E];
+  const int cpr = I >> 3;
+  for (int r = blockIdx.x; r < M; r += gridDim.x) {
+    const uint16_t* zr = z + (long long)r * 2 * I;
+    const uint16_t* gr = G + (long long)r * I;
+    uint16_t* dr = dgu + (long long)r * 2 * I;
+    const float rs = ep.row_scale ? ep.row_scale[r] : 1.0f;
+    for (int ch = threadIdx.x; ch < cpr; ch += 256) {
+      uint4 Gv = *reinterpret_cast<const uint4*>(gr + ch * 8);
+      uint4 gv = *reinterpret_cast<const uint4*>(zr + ch * 8);
+      uint4 uv = *reinterpret_cast<const uint4*>(zr + I + ch * 8);
+      const uint16_t* G16 = reinterpret_cast<const uint16_t*>(&Gv);
+      const uint16_t* g16 = reinterpret_cast<const uint16_t*>(&gv);
+      const uint16_t* u16 = reinterpret_cast<const uint16_t*>(&uv);
+      uint4 og, ou;
+      uint16_t* og16 = reinterpret_cast<uint16_t*>(&og);
+      uint16_t* ou16 = reinterpret_cast<uint16_t*>(&ou);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      float g = bf16_to_f32(g16[q]) + bg[q];
-      float u = bf16_to_f32(u16[q]) + bu[q];
-      float gc = fminf(fmaxf(g, ep.gate_lo), ep.gate_hi);
-      float uc = fminf(fmaxf(u, ep.up_lo), ep.up_hi) + ep.up_offset;
-      float v = act_fwd(ep.act, gc, ep.alpha) * uc;
-      if (ep.row_scale) v *= rs;
-      o16[q] = f32_to_bf16(v);
+      for (int q = 0; q < 8; ++q) {
+        const float Gq = bf16_to_f32(G16[q]) * rs;
+        const float g = bf16_to_f32(g16[q]), u = bf16_to_f32(u16[q]);
+        const float gc = fminf(fmaxf(g, ep.gate_lo), ep.gate_hi);
+        const float uc = fminf(fmaxf(u, ep.up_lo), ep.up_hi) + ep.up_offset;
+        float a, da;
+        act_fwd_bwd(ep.act, gc, ep.alpha, a, da);
+        const bool gin = (g >= ep.gate_lo) && (g <= ep.gate_hi);
+        const bool uin = (u >= ep.up_lo) && (u <= ep.up_hi);
+        og16[q] = f32_to_bf16(gin ? Gq * uc * da : 0.0f);
+        ou16[q] = f32_to_bf16(uin ? Gq * a : 0.0f);
+      }
+      *reinterpret_cast<uint4*>(dr + ch * 8) = og;
+      *reinterpret_cast<uint4*>(dr + I + ch * 8) = ou;
     }
-    *reinterpret_cast<uint4*>(y + (long long)r * I + ch * 8) = out;
   }
 }
 

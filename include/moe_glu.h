@@ -344,6 +344,19 @@ moe_status_t moe_group_gemm_wgrad(const void* a, const void* b, int P, int Q,
 moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
                              const moe_epilogue_t* ep, void* y, void* stream);
 
+/* Unfused dGLU pass (the baseline of the fused backward epilogue, [BLOG]
+ * "Optimizando GLU vía epílogos GEMM fusionados": the activation gradient as a
+ * memory-bound pass after the GEMM).  g: dL/dy bf16 [M_cap][I] as the plain
+ * dgrad GroupGemm wrote it (moe_group_gemm_quant of dY2 with W2); z: the saved
+ * pre-activation bf16 [M_cap][2I] (plain order, post-bias); dgu: bf16
+ * [M_cap][2I] output, d(gate) in columns [0, I), d(up) in [I, 2I).  Same
+ * arithmetic as moe_group_gemm_dglu_bwd's epilogue (row scale, clamp
+ * gradients, activation derivative) on the bf16-rounded g.  Routed rows only
+ * (offsets from the device counts); gated forms only (ep->gated = 1, else
+ * MOE_ERR_UNSUPPORTED).  Requires I % 64 == 0; g, z, dgu 16-byte aligned. */
+moe_status_t moe_dglu_unfused(const void* g, const void* z, const moe_groups_t* groups, int I,
+                              const moe_epilogue_t* ep, void* dgu, void* stream);
+
 /* Standalone MXFP8 quantize/transpose (baseline, and offline weight prep) of
  * a bf16 [R][C] matrix.  Row-wise blocks run along C.  Column-wise blocks run
  * down 32 rows; with groups (counts over the first rows, M_cap = R) they

@@ -46,6 +46,16 @@ def test_host_argument_errors_return_before_launch():
     ep = G.epilogue()
     fake = 1 << 20                         # never dereferenced: checks fail first
     grp = G.GroupsT(fake, 4, 1024, None, None)
+    # unfused dGLU: null, shape, alignment, the non-gated form
+    assert G.raw_call("moe_dglu_unfused", NULL, fake, ctypes.byref(grp), 256, ctypes.byref(ep),
+                      fake, NULL) == 1
+    assert G.raw_call("moe_dglu_unfused", fake, fake, ctypes.byref(grp), 100, ctypes.byref(ep),
+                      fake, NULL) == 2
+    assert G.raw_call("moe_dglu_unfused", fake + 2, fake, ctypes.byref(grp), 256,
+                      ctypes.byref(ep), fake, NULL) == 3
+    ep_plain = G.epilogue("srelu", gated=False)
+    assert G.raw_call("moe_dglu_unfused", fake, fake, ctypes.byref(grp), 256,
+                      ctypes.byref(ep_plain), fake, NULL) == 4
     # null required pointers
     assert G.raw_call("moe_group_gemm_glu_fwd", NULL, ctypes.byref(grp), fake, 256, 512,
                       ctypes.byref(ep), NULL, NULL, NULL, 0, NULL) == 1

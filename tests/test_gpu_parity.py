@@ -469,6 +469,31 @@ def test_glu_unfused_with_bias_against_oracle(G):
     assert_bf16_close(host_bits(y), ref, what="glu_unfused")
 
 
+@pytest.mark.parametrize("act,clamp", [("swiglu", False), ("swiglu", True), ("geglu", False),
+                                       ("srelu", False)])
+def test_dglu_unfused_against_oracle(G, act, clamp):
+    # rows past the routed ones (M_cap > sum of counts) are left untouched
+    import torch
+    counts = np.array([70, 0, 33, 129])
+    E, I = 4, 256
+    M = int(counts.sum())
+    m_cap = M + 21
+    rng = np.random.default_rng(43)
+    g = W.to_bf16_bits((rng.standard_normal((m_cap, I)) * 0.1).astype(np.float32))
+    z = W.to_bf16_bits((rng.standard_normal((m_cap, 2 * I)) * 4).astype(np.float32))
+    rs = (0.5 + rng.random(m_cap)).astype(np.float32)
+    kw = dict(alpha=1.702, gate_lo=-7.0, gate_hi=7.0, up_lo=-7.0, up_hi=7.0) if clamp else {}
+    dgu = torch.full((m_cap, 2 * I), 0x1234, dtype=torch.int16, device="cuda")
+    G.moe_dglu_unfused(dev_bits(g), dev_bits(z), G.groups(dev_i32(counts), m_cap), I,
+                       G.epilogue(act, row_scale=torch.from_numpy(rs).cuda(), **kw), dgu)
+    _sync()
+    ref = F.f64_to_bf16_bits(O.dglu(F.bf16_bits_to_f64(g[:M]), F.bf16_bits_to_f64(z[:M]),
+                                    O.Epilogue(act=act, **kw), row_scale=rs[:M]))
+    out = host_bits(dgu)
+    assert_bf16_close(out[:M], ref, what=f"dglu_unfused {act}")
+    assert np.all(out[M:] == 0x1234)
+
+
 def test_mxfp8_quantize_standalone_bit_exact(G):
     rng = np.random.default_rng(51)
     R, C = 77, 96
