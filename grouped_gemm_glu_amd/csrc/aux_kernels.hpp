@@ -435,16 +435,6 @@ __global__ __launch_bounds__(256) void dglu_unfused_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------- MXFP8 quantize
-__device__ __forceinline__ void store_q32(uint8_t* dst, const uint32_t* w, int nvalid) {
-  uintptr_t a = reinterpret_cast<uintptr_t>(dst);
-  if (nvalid == 32 && (a & 15) == 0) {
-    uint4* d = reinterpret_cast<uint4*>(dst);
-    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  } else {
-    for (int i = 0; i < nvalid; ++i) dst[i] = static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3)));
-  }
-}
 
 // Row-wise: one thread per (row, 32-column block) over rows [0, R_used).
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ v, int R, int C,
@@ -476,7 +466,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
     }
     uint32_t w[8];
     uint8_t sb = mx_quant32(x, 32, w, e5 != 0);
-    store_q32(q + (long long)r * C + cb * 32, w, 32);
+    store_codes32(q + (long long)r * C + cb * 32, w, 32);
     s[(long long)r * nb + cb] = sb;
   }
 }
@@ -518,7 +508,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict
     for (int i = 0; i < 32; ++i) x[i] = (i < nvalid) ? bf16_to_f32(v[(long long)(r0 + i) * C + c]) : 0.0f;
     uint32_t w[8];
     uint8_t sb = mx_quant32(x, nvalid, w, e5 != 0);
-    store_q32(q + (long long)c * R + r0, w, nvalid);
+    store_codes32(q + (long long)c * R + r0, w, nvalid);
     s[(long long)c * s_ld + b] = sb;
   }
 }

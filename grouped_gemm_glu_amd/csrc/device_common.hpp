@@ -119,6 +119,36 @@ __device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32
   return e8m0_byte(E);
 }
 
+// 32 codes (w, little-endian) to dst, which has any alignment.  A full block
+// at a non-4-byte-aligned address (a transposed block starting at a group's
+// first row) goes out as h = 4 - (dst % 4) head bytes, 7 aligned dwords
+// (each two neighbouring words of w funnel-shifted by h bytes) and 4 - h tail
+// bytes, instead of 32 byte stores; a partial block (a group's last) byte by
+// byte.
+__device__ __forceinline__ void store_codes32(uint8_t* dst, const uint32_t* w, int nvalid) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+  auto byte = [&](int i) { return static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3))); };
+  if (nvalid == 32 && (a & 15) == 0) {
+    uint4* d = reinterpret_cast<uint4*>(dst);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else if (nvalid == 32 && (a & 3) == 0) {
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = w[i];
+  } else if (nvalid == 32) {
+    const int h = 4 - (int)(a & 3);   // 1..3
+    for (int i = 0; i < h; ++i) dst[i] = byte(i);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + h);
+    const uint32_t sr = 8u * (uint32_t)h, sl = 32u - sr;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) d[k] = (w[k] >> sr) | (w[k + 1] << sl);
+    for (int i = h + 28; i < 32; ++i) dst[i] = byte(i);
+  } else {
+    for (int i = 0; i < nvalid; ++i) dst[i] = byte(i);
+  }
+}
+
 // ---------------------------------------------------------------- activations
 enum { ACT_SWIGLU = 0, ACT_GEGLU = 1, ACT_GEGLU_TANH = 2, ACT_SRELU = 3 };
 

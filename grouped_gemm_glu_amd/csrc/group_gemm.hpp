@@ -192,20 +192,6 @@ __device__ __forceinline__ int opaque_zero() {
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------- MX helpers
-__device__ __forceinline__ void store_bytes(uint8_t* dst, const uint32_t* w, int nvalid) {
-  uintptr_t a = reinterpret_cast<uintptr_t>(dst);
-  if (nvalid == 32 && (a & 15) == 0) {
-    uint4* d = reinterpret_cast<uint4*>(dst);
-    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  } else if (nvalid == 32 && (a & 3) == 0) {
-    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = w[i];
-  } else {
-    for (int i = 0; i < nvalid; ++i) dst[i] = static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3)));
-  }
-}
 
 // MXFP8 of a staged bf16 tile: stg[r][c] (row stride ld elements) holds rows
 // [0, rows_valid) x cols [0, ncols) of the output, whose global position is
@@ -238,7 +224,7 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
       uint8_t sb = mx_quant32(v, 32, w, p.mx_e5 != 0);
       long long grow = grow0 + r;
       int gc = col0 + cb * 32;
-      store_bytes(p.row_q + grow * p.mx_cols + gc, w, 32);
+      store_codes32(p.row_q + grow * p.mx_cols + gc, w, 32);
       p.row_s[grow * (p.mx_cols >> 5) + (gc >> 5)] = sb;
     }
   }
@@ -265,10 +251,10 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
       uint32_t w[8];
       const long long gc = col0 + 2 * c2;
       uint8_t sb = mx_quant32(v0, nvalid, w, p.mx_e5 != 0);
-      store_bytes(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
+      store_codes32(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[gc * p.col_s_ld + scol0 + rb] = sb;
       sb = mx_quant32(v1, nvalid, w, p.mx_e5 != 0);
-      store_bytes(p.col_q + (gc + 1) * p.M_cap + grow0 + rb * 32, w, nvalid);
+      store_codes32(p.col_q + (gc + 1) * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[(gc + 1) * p.col_s_ld + scol0 + rb] = sb;
     }
   }
