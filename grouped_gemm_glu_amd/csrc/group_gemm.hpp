@@ -199,15 +199,19 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // col-wise: blocks of 32 rows starting at the tile's first row (a tile always
 // starts a block because tiles start at group row multiples of 256), scale
 // column scol0 + r / 32.
-template <int NT>
-__device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, int ncols, int grow0,
-                              int col0, const GemmArgs& p, int scol0) {
+// gcol(c): the global column of staged column c (a multiple of 32 apart from
+// c's offset in its 32-column block), or -1 where the staged column is not
+// output; ncols is a multiple of 32.
+template <int NT, typename GCol>
+__device__ __forceinline__ void mx_from_stage_map(const Stg& stg, int rows_valid, int ncols, int grow0,
+                                                  const GemmArgs& p, int scol0, GCol gcol) {
   const int t = threadIdx.x + opaque_zero();
   if (p.row_q) {
     const int nb = ncols >> 5;
     for (int it = t; it < stg.rows() * nb; it += NT) {
       int r = it / nb, cb = it - r * nb;
-      if (r >= rows_valid) continue;
+      const int gc = gcol(cb * 32);
+      if (r >= rows_valid || gc < 0) continue;
       float v[32];
       const uint4* s = reinterpret_cast<const uint4*>(stg.row(r) + cb * 32);
 #pragma unroll
@@ -223,22 +227,21 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
       uint32_t w[8];
       uint8_t sb = mx_quant32(v, 32, w, p.mx_e5 != 0);
       long long grow = grow0 + r;
-      int gc = col0 + cb * 32;
       store_codes32(p.row_q + grow * p.mx_cols + gc, w, 32);
       p.row_s[grow * (p.mx_cols >> 5) + (gc >> 5)] = sb;
     }
   }
   if (p.col_q) {
-    // items of two adjacent columns x 32 rows: one 4-byte LDS read per row
-    // (ncols is a multiple of 32); the row blocks of a column pair are
-    // consecutive items, so neighbouring lanes store neighbouring 32-byte
-    // pieces of a column
+    // items of two adjacent columns x 32 rows: one 4-byte LDS read per row;
+    // the row blocks of a column pair are consecutive items, so neighbouring
+    // lanes store neighbouring 32-byte pieces of a column
     const int nrb = (rows_valid + 31) >> 5;
     const int nc2 = ncols >> 1;
     const int nrbt = stg.rows() >> 5;
     for (int it = t; it < nc2 * nrbt; it += NT) {
       const int rb = it % nrbt, c2 = it / nrbt;
-      if (rb >= nrb) continue;
+      const long long gc = gcol(2 * c2);
+      if (rb >= nrb || gc < 0) continue;
       int nvalid = rows_valid - rb * 32;
       if (nvalid > 32) nvalid = 32;
       float v0[32], v1[32];
@@ -249,7 +252,6 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
         v1[i] = __uint_as_float(w2 & 0xFFFF0000u);
       }
       uint32_t w[8];
-      const long long gc = col0 + 2 * c2;
       uint8_t sb = mx_quant32(v0, nvalid, w, p.mx_e5 != 0);
       store_codes32(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[gc * p.col_s_ld + scol0 + rb] = sb;
@@ -258,6 +260,12 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
       p.col_s[(gc + 1) * p.col_s_ld + scol0 + rb] = sb;
     }
   }
+}
+// staged columns [0, ncols) are global columns col0 ..
+template <int NT>
+__device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, int ncols, int grow0,
+                                              int col0, const GemmArgs& p, int scol0) {
+  mx_from_stage_map<NT>(stg, rows_valid, ncols, grow0, p, scol0, [=](int c) { return col0 + c; });
 }
 
 // Wave maximum of a non-negative float (no NaN), raised into *dst with one
@@ -1303,13 +1311,16 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
           }
         }
         if (p.row_q || p.col_q) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int nv = min(64, p.I - chunk_col(k));
-            if (nv > 0)
-              mx_from_stage<NTH>(Stg{stg.h0 + k * 64, stg.h1 + k * 64, ld, SHR}, rows_valid, nv, row0,
-                            (k < 2 ? 0 : p.I) + chunk_col(k), p, gs.mxs_off[e] + mt * 8);
-          }
+          // the four staged 64-column chunks in one pass: chunk k is output
+          // column (k < 2 ? 0 : I) + chunk_col(k) on, if inside I (I % 64 == 0)
+          const int g0 = chunk_col(0) < p.I ? chunk_col(0) : -1;
+          const int g1 = chunk_col(1) < p.I ? chunk_col(1) : -1;
+          const int g2 = g0 < 0 ? -1 : p.I + g0, g3 = g1 < 0 ? -1 : p.I + g1;
+          mx_from_stage_map<NTH>(stg, rows_valid, 256, row0, p, gs.mxs_off[e] + mt * 8, [=](int c) {
+            const int k = c >> 6;
+            const int g = k == 0 ? g0 : (k == 1 ? g1 : (k == 2 ? g2 : g3));
+            return g < 0 ? -1 : g + (c & 63);
+          });
         }
         __syncthreads();
       }
