@@ -71,12 +71,15 @@ def test_pack_weight_bit_exact(G, layout, E, N, K):
 def _route_case(G, logits, k, x=None):
     import torch
     T, E = logits.shape
-    d_logits = torch.from_numpy(logits).cuda()
-    ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    # (buffers of at least one row, so that T = 0 still passes non-null pointers)
+    Tb = max(T, 1)
+    d_logits = torch.zeros((Tb, E), dtype=torch.float32, device="cuda")
+    d_logits[:T] = torch.from_numpy(logits).cuda()
+    ids = torch.full((Tb, k), -7, dtype=torch.int32, device="cuda")
     counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
     offs = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
-    dst = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
-    src = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    dst = torch.full((Tb, k), -7, dtype=torch.int32, device="cuda")
+    src = torch.full((Tb * k,), -7, dtype=torch.int32, device="cuda")
     xg = None
     H = 0
     if x is not None:
@@ -85,13 +88,23 @@ def _route_case(G, logits, k, x=None):
     G.moe_route_group(d_logits, None, T, E, k, ids, counts, offs, dst, src,
                       None if x is None else dev_bits(x), H, xg)
     _sync()
-    return (ids.cpu().numpy(), counts.cpu().numpy(), offs.cpu().numpy(), dst.cpu().numpy(),
-            src.cpu().numpy(), None if xg is None else host_bits(xg))
+    return (ids[:T].cpu().numpy(), counts.cpu().numpy(), offs.cpu().numpy(), dst[:T].cpu().numpy(),
+            src[:T * k].cpu().numpy(), None if xg is None else host_bits(xg))
 
 
-@pytest.mark.parametrize("case", ["tiny", "tiny_empty", "gptoss", "ties", "wide", "specials"])
+@pytest.mark.parametrize("case", ["tiny", "tiny_empty", "gptoss", "ties", "wide", "specials",
+                                  "one_chunk", "one_past_chunk", "max_experts", "no_tokens"])
 def test_route_group_bit_exact(G, case):
-    if case == "specials":
+    # grouping runs in chunks of max(1024, 2E rounded up to a power of two)
+    # pairs: one full chunk, one pair past it, E = 1024 (chunks of 2048), T = 0
+    edge = {"one_chunk": (512, 16, 2), "one_past_chunk": (1025, 7, 1),
+            "max_experts": (700, 1024, 3), "no_tokens": (0, 8, 2)}
+    if case in edge:
+        T_, E_, k = edge[case]
+        rng = np.random.default_rng(T_ + E_)
+        logits = rng.standard_normal((T_, E_)).astype(np.float32)
+        x = W.to_bf16_bits(rng.standard_normal((T_, 64)).astype(np.float32)) if T_ else None
+    elif case == "specials":
         # NaN ranks below every number (numpy's sort order, as in the oracle),
         # infinities and signed zeros tie-break by expert id
         rng = np.random.default_rng(9)
