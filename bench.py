@@ -626,7 +626,8 @@ def bench_tiny(G, torch):
     """The tiny routed case (512 tokens, 4 experts, top-2, hidden 256,
     intermediate 512): launch-bound, so reported as microseconds per forward
     (route + fused FC1) against B1 (route + GEMM + GLU pass), eager and as one
-    graph replay."""
+    graph replay, and the FC1 step alone (one fused launch against GEMM + GLU
+    pass) as a graph replay."""
     import workloads as W
     d = W.tiny()
     T, E, k, H, I = d["T"], d["E"], d["k"], d["H"], d["I"]
@@ -660,9 +661,21 @@ def bench_tiny(G, torch):
         G.moe_group_gemm_quant(op_x, op_w1t, 2 * I, H, grp, z)
         G.moe_glu_unfused(z, grp, I, ep, y)
 
+    # the FC1 step alone on the routed rows: one fused launch vs GEMM -> GLU pass
+    fused()
+    torch.cuda.synchronize()
+
+    def fc1_only():
+        G.moe_group_gemm_glu_fwd(xg, grp, w1p, H, I, ep, y)
+
+    def b1_only():
+        G.moe_group_gemm_quant(op_x, op_w1t, 2 * I, H, grp, z)
+        G.moe_glu_unfused(z, grp, I, ep, y)
+
     res = {"fused_us": round(_ev_ms(torch, fused, 50) * 1e3, 2),
            "b1_us": round(_ev_ms(torch, b1, 50) * 1e3, 2)}
-    for name, fn in (("fused", fused), ("b1", b1)):
+    for name, fn in (("fused", fused), ("b1", b1), ("fc1_only_fused", fc1_only),
+                     ("fc1_only_b1", b1_only)):
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -674,6 +687,7 @@ def bench_tiny(G, torch):
             fn()
         res[f"{name}_graph_us"] = round(_ev_ms(torch, g.replay, 50) * 1e3, 2)
     res["fused_speedup_graph"] = round(res["b1_graph_us"] / res["fused_graph_us"], 3)
+    res["fc1_only_speedup_graph"] = round(res["fc1_only_b1_graph_us"] / res["fc1_only_fused_graph_us"], 3)
     return res
 
 
