@@ -66,17 +66,33 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
       *reinterpret_cast<uint4*>(&tile[r][c * 8]) = v;
     }
   } else {  // PACK_KN and PACK_GATEUP: source [K][N]-major rows, 8 consecutive n per chunk
+    // thread t: k rows 8 kg .. + 7 (kg = t / 32) x n chunk cc = t % 32 (8 values);
+    // eight 16-byte loads (a wave reads 2 x 512 contiguous bytes per load),
+    // an 8 x 8 transpose of the 16-bit values in registers, eight 16-byte
+    // LDS writes tile[n][8 kg .. + 7]
     const uint16_t* w = src + (long long)e * K * N;
-    for (int it = t; it < 2048; it += 256) {
-      const int kk = it >> 5, cc = it & 31, r0 = cc * 8, pr = nb * 256 + r0;
+    const int kg = t >> 5, cc = t & 31, r0 = cc * 8, pr = nb * 256 + r0;
+    uint32_t in[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (pr < N) {
         const int col = mode == PACK_GATEUP ? plain_col_of_packed(pr, I) : pr;
-        v = *reinterpret_cast<const uint4*>(w + (long long)(kb * 64 + kk) * N + col);
+        v = *reinterpret_cast<const uint4*>(w + (long long)(kb * 64 + kg * 8 + i) * N + col);
       }
-      const uint16_t* pv = reinterpret_cast<const uint16_t*>(&v);
+      in[i][0] = v.x; in[i][1] = v.y; in[i][2] = v.z; in[i][3] = v.w;
+    }
+    // out word d of n = r0 + j: k = 8 kg + 2d (low half), 8 kg + 2d + 1 (high)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) tile[r0 + q][kk] = pv[q];
+    for (int j = 0; j < 8; ++j) {
+      uint32_t o[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = (in[2 * d][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        const uint32_t hi = (in[2 * d + 1][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        o[d] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(&tile[r0 + j][kg * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
   __syncthreads();
