@@ -802,7 +802,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     };
     // Two K-tiles per iteration, stage arrays used in a fixed order so every
     // LDS access names its array directly.  With an odd tile count the last
-    // step computes a zero tile.
+    // K-tile (in lds0) runs after the loop, with no DMA (the loop's last
+    // prefetch into lds1 reads zeros and is drained before the epilogue).
     issue_direct(0, lds0);
     if (KNR) {
       kn_load(0);
@@ -813,7 +814,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     if (KNR) kn_load(1);
     __builtin_amdgcn_sched_barrier(0);
     frag_load(lds0, 0, 0, 0);
-    for (int kt = 0; kt < nk_t; kt += 2) {
+    const int nk_even = nk_t & ~1;
+    for (int kt = 0; kt < nk_even; kt += 2) {
       first_steps(lds0, 0);
       if (KNR) kn_store(lds1);
       stage_barrier();
@@ -828,6 +830,10 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       if (KNR) kn_load(kt + 3);
       frag_load(lds0, 0, 0, 0);
       mfma_step_dma(1, 1, KSTEPS - 1);   // last k-step of K-tile kt + 1
+    }
+    if (nk_t & 1) {   // the odd last K-tile, landed in lds0 (waited for in the loop)
+      first_steps(lds0, 0);
+      mfma_step(1, 0, KSTEPS - 1);
     }
     // the loop leaves one DMA (a K-tile past the end: zeros) and one set of
     // fragment reads in flight; the epilogue reuses both stage arrays
