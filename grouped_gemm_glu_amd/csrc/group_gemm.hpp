@@ -268,19 +268,18 @@ __device__ __forceinline__ void mx_from_stage(const Stg& stg, int rows_valid, in
   mx_from_stage_map<NT>(stg, rows_valid, ncols, grow0, p, scol0, [=](int c) { return col0 + c; });
 }
 
-// Wave maximum of a non-negative float (no NaN), raised into *dst with one
-// atomic per wave: for such values the float order is the order of their
-// bits as unsigned integers.  Swizzle in bitmask mode pairs lane ^ xm within
-// each half of the wave.
-__device__ __forceinline__ void wave_amax_atomic(float v, float* dst, int lane) {
+// Wave maximum of a non-negative float (no NaN), as its bits: for such
+// values the float order is the order of their bits as unsigned integers.
+// Swizzle in bitmask mode pairs lane ^ xm within each half of the wave; the
+// result is wave-uniform (a scalar register).
+__device__ __forceinline__ uint32_t wave_max_bits(float v) {
   uint32_t b = __float_as_uint(v);
   b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (1 << 10) | 0x1F));
   b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (2 << 10) | 0x1F));
   b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (4 << 10) | 0x1F));
   b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (8 << 10) | 0x1F));
   b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (16 << 10) | 0x1F));
-  b = max((uint32_t)__builtin_amdgcn_readlane((int)b, 0), (uint32_t)__builtin_amdgcn_readlane((int)b, 32));
-  if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(dst), b);
+  return max((uint32_t)__builtin_amdgcn_readlane((int)b, 0), (uint32_t)__builtin_amdgcn_readlane((int)b, 32));
 }
 
 // In-place Walsh-Hadamard butterflies of 16 values (Sylvester order, not
@@ -432,6 +431,10 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // LDS-DMA lane coordinates: a wave instruction fills 8 rows x 128 B
   const int rl = lane >> 3, pc = lane & 7;
 
+  // the amax epilogues' running wave maximum (bits of a non-negative float):
+  // raised into amax_out with one atomic per wave after the last tile, not
+  // once per tile, so no tile's main loop waits on a contended atomic
+  uint32_t amax_bits = 0u;
   for (int tile = slot; tile < total_tiles; tile += P) {
     // ---- decode (expert, m-tile, n-tile).  Half tiles: expert e owns ids
     // [half_off[e] * NT, half_off[e+1] * NT), one per n-tile of its last
@@ -1049,7 +1052,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       }
       if (wave_on) {
         body();
-        if (p.ep.amax_out) wave_amax_atomic(ymax, p.ep.amax_out, lane);   // NaN dropped by fmaxf
+        if (p.ep.amax_out) amax_bits = max(amax_bits, wave_max_bits(ymax));   // NaN dropped by fmaxf
       }
       if (MXO) {
         __syncthreads();
@@ -1143,7 +1146,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
         store_stage<NTH>(stg, rows_valid, cvalid_n, GM_BN, p.preact + (long long)row0 * p.N + n0, p.N);
         __syncthreads();
       }
-      if (p.ep.amax_out) wave_amax_atomic(ymax, p.ep.amax_out, lane);
+      if (p.ep.amax_out) amax_bits = max(amax_bits, wave_max_bits(ymax));
     } else if (EPI == EPI_STORE) {
       const int ld = GM_STG_LD_256;
 #pragma unroll
@@ -1330,7 +1333,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
         }
         __syncthreads();
       }
-      if (p.ep.amax_out) wave_amax_atomic(hmax, p.ep.amax_out, lane);
+      if (p.ep.amax_out) amax_bits = max(amax_bits, wave_max_bits(hmax));
       if (want_drs) {   // (the rounds end with a barrier: every LDS add is in)
         for (int r = tid; r < rows_valid; r += NTH) atomicAdd(p.ep.drs_out + row0 + r, drs_lds[r]);
         __syncthreads();
@@ -1344,6 +1347,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       else tile_body(std::integral_constant<int, 16 / NW>{});
     }
   }
+  if (p.ep.amax_out && lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.ep.amax_out), amax_bits);
 }
 
 }  // namespace moe
