@@ -59,7 +59,7 @@ def _dglu_grads(G, dy2, w2, pre, counts, m_cap, ep_kw, rs=None, grads=True, layo
 
 @pytest.mark.parametrize("layout", ["PACKED", "NK"])
 def test_param_grads_integer_exact(G, layout):
-    counts = np.array([40, 0, 300, 17])
+    counts = np.array([40, 0, 300, 17, 100, 130])   # 100: a half tile past 64 rows; 130: a full tile past 128
     E, H, I = len(counts), 64, 192
     M = int(counts.sum())
     m_cap = M + 11
