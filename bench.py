@@ -710,11 +710,33 @@ def read_traffic(path):
     return rec.get("fc1_hbm_bytes_per_launch")
 
 
+def _host_info():
+    """CPU model and the BLAS library numpy calls (for the cpu_baseline record)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')}"
+    except Exception:   # numpy without the dict form: leave it unknown
+        pass
+    return model, blas
+
+
 def cpu_baseline(d, dy2_h, rows_per_expert=None):
     """The oracle, as it stands, on the same step: by default every routed row
     of every expert (the whole workload) through FC1+SwiGLU, FC2,
-    dgrad+dSwiGLU and dX in float64 (numpy/BLAS), timed on this host's cores
-    (about 10-20 s of CPU work); rows_per_expert caps each expert's rows."""
+    dgrad+dSwiGLU and dX, timed on this host's cores.  `value` is the float64
+    run (the oracle's arithmetic); the same functions in float32 (BLAS sgemm,
+    closer to the GPU's fp32 accumulation) are timed after it as `fp32`.
+    About 15-30 s of CPU work in all; rows_per_expert caps each expert's rows."""
     from oracle import moe as O
     try:
         cores = len(os.sched_getaffinity(0))
@@ -731,20 +753,27 @@ def cpu_baseline(d, dy2_h, rows_per_expert=None):
     sel = np.concatenate([np.arange(off[e], off[e] + c[e]) for e in range(len(counts))])
     xs, dys = d["x"][sel], dy2_h[sel]
     ep = O.Epilogue()
-    t = time.perf_counter()
-    pre, y = O.fc1_glu(xs, c, d["w1"], ep)
-    O.group_gemm(y, c, d["w2"])
-    dgu = O.dgrad_dglu(dys, c, d["w2"], pre, ep)
-    O.dx(dgu, c, d["w1"])
-    dt = time.perf_counter() - t
+
+    def run(dtype):
+        t = time.perf_counter()
+        pre, y = O.fc1_glu(xs, c, d["w1"], ep, dtype=dtype)
+        O.group_gemm(y, c, d["w2"], dtype=dtype)
+        dgu = O.dgrad_dglu(dys, c, d["w2"], pre, ep, dtype=dtype)
+        O.dx(dgu, c, d["w1"], dtype=dtype)
+        return time.perf_counter() - t
+
     flops = float(c.sum()) * (2 * H * 2 * I + 2 * I * H + 2 * H * I + 2 * 2 * I * H)
+    dt = run(np.float64)
+    dt32 = run(np.float32)
+    model, blas = _host_info()
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(dt, 2), "dtype": "float64",
+            "fp32": {"value": round(flops / dt32 / 1e12, 6), "seconds": round(dt32, 2)},
+            "cpu_model": model, "blas": blas,
             "sample": (f"all {int(c.sum())} routed rows of the 32 experts" if rows_per_expert is None
                        else f"first min(m_e, {cap}) rows of each of the 32 experts "
                             f"({int(c.sum())} of {int(counts.sum())} rows)")
-                      + " through the full step (FC1+SwiGLU, FC2, dgrad+dSwiGLU, dX), float64"}
-
+                      + " through the full step (FC1+SwiGLU, FC2, dgrad+dSwiGLU, dX)"}
 
 if __name__ == "__main__":
     main()

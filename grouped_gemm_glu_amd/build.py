@@ -73,6 +73,44 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_asan(jobs: int = 8, verbose: bool = False) -> str:
+    """A copy of the library whose entry points (api.hip) have their HOST code
+    built with AddressSanitizer; device code and the other units are compiled
+    as usual (objects of an earlier build() are reused).  For the CPU-only
+    argument-validation test; load it with the ASan runtime preloaded.
+    Returns _build/asan/libmoeglu_asan.so."""
+    asan_dir = os.path.join(ROOT, "_build", "asan")
+    os.makedirs(asan_dir, exist_ok=True)
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = []
+    todo = []
+    for unit in SOURCES:
+        src, name, extra = unit
+        if name == "api":
+            continue
+        obj = os.path.join(OBJDIR, name + ".o")
+        objs.append(obj)
+        if not os.path.exists(obj):
+            todo.append(unit)
+    if todo:
+        with ThreadPoolExecutor(max(1, jobs)) as ex:
+            list(ex.map(lambda s: compile_one(s, verbose), todo))
+    api_obj = os.path.join(asan_dir, "api_asan.o")
+    host_asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    cmd = ([hipcc(), "-c", os.path.join(CSRC, "api.hip"), "-o", api_obj] + common_flags()
+           + host_asan + ["-g"])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (host ASan) failed on api.hip:\n{r.stdout}\n{r.stderr}")
+    lib = os.path.join(asan_dir, "libmoeglu_asan.so")
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", lib + ".tmp", api_obj] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (host ASan) failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(lib + ".tmp", lib)
+    return lib
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))

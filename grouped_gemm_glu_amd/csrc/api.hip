@@ -279,7 +279,7 @@ moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T
   if (TK > 0) {
     const int grid = min((TK + 3) / 4, cus * 32);   // 4 pairs (one per wave) per workgroup step
     hipLaunchKernelGGL(group_scatter_kernel, dim3(grid), dim3(256), 0, s, topk_ids_out, TK, k, E, dst,
-                       src, static_cast<const uint16_t*>(x), H, static_cast<uint16_t*>(xg));
+                       offsets, src, static_cast<const uint16_t*>(x), H, static_cast<uint16_t*>(xg));
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

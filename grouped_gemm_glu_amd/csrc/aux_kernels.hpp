@@ -328,11 +328,15 @@ __global__ __launch_bounds__(256) void group_rank_kernel(const int* __restrict__
 // row xg[dst[p]] = x[p / k]: one wave per pair, 16 bytes per lane.
 __global__ __launch_bounds__(256) void group_scatter_kernel(const int* __restrict__ ids, int TK,
                                                             int k, int E, const int* __restrict__ dst,
+                                                            const int* __restrict__ offsets,
                                                             int* __restrict__ src,
                                                             const uint16_t* __restrict__ x, int H,
                                                             uint16_t* __restrict__ xg) {
   const int lane = threadIdx.x & 63;
   const int cpr = H >> 3;
+  // entries of src past the grouped rows (pairs with ids outside [0, E)) may
+  // still hold the per-chunk counts of the earlier kernels: set them to -1
+  for (int r = offsets[E] + blockIdx.x * 256 + threadIdx.x; r < TK; r += gridDim.x * 256) src[r] = -1;
   for (int p = blockIdx.x * 4 + (threadIdx.x >> 6); p < TK; p += gridDim.x * 4) {
     const int e = ids[p];
     if (e < 0 || e >= E) continue;

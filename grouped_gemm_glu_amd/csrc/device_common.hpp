@@ -158,6 +158,16 @@ __device__ __forceinline__ float sigmoidf_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// The Gaussian CDF as 0.5 erfc(-g / sqrt 2) and the tanh form's 0.5 (1 +
+// tanh u) as sigmoid(2u): the same functions as 0.5 (1 + erf) and 0.5 (1 +
+// tanh), but without their cancellation for negative g, so a(g) and a'(g)
+// keep their relative accuracy in the tail (they set MXFP8 block scales of
+// the outputs, which follow the block's largest value, however small).
+__device__ __forceinline__ float gauss_cdf(float g) { return 0.5f * erfcf(g * -0.70710678118654752f); }
+__device__ __forceinline__ float gelu_tanh_u(float g) {
+  return 0.79788456080286536f * (g + 0.044715f * g * g * g);
+}
+
 // a(g) for a compile-time activation (epilogues dispatch once per launch,
 // not per element).
 template <int ACT>
@@ -165,10 +175,9 @@ __device__ __forceinline__ float act_fwd_t(float g, float alpha) {
   if constexpr (ACT == ACT_SWIGLU) {
     return g * sigmoidf_fast(alpha * g);
   } else if constexpr (ACT == ACT_GEGLU) {
-    return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+    return g * gauss_cdf(g);
   } else if constexpr (ACT == ACT_GEGLU_TANH) {
-    const float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
-    return 0.5f * g * (1.0f + tanhf(u));
+    return g * sigmoidf_fast(2.0f * gelu_tanh_u(g));
   } else {
     const float r = fmaxf(g, 0.0f);
     return r * r;
@@ -177,13 +186,10 @@ __device__ __forceinline__ float act_fwd_t(float g, float alpha) {
 
 __device__ __forceinline__ float act_fwd(int act, float g, float alpha) {
   switch (act) {
-    case ACT_SWIGLU: return g * sigmoidf_fast(alpha * g);
-    case ACT_GEGLU: return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
-    case ACT_GEGLU_TANH: {
-      float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
-      return 0.5f * g * (1.0f + tanhf(u));
-    }
-    default: { float r = fmaxf(g, 0.0f); return r * r; }
+    case ACT_SWIGLU: return act_fwd_t<ACT_SWIGLU>(g, alpha);
+    case ACT_GEGLU: return act_fwd_t<ACT_GEGLU>(g, alpha);
+    case ACT_GEGLU_TANH: return act_fwd_t<ACT_GEGLU_TANH>(g, alpha);
+    default: return act_fwd_t<ACT_SRELU>(g, alpha);
   }
 }
 
@@ -195,16 +201,16 @@ __device__ __forceinline__ void act_fwd_bwd_t(float g, float alpha, float& a, fl
     a = g * s;
     da = s * (1.0f + alpha * g * (1.0f - s));
   } else if constexpr (ACT == ACT_GEGLU) {
-    const float cdf = 0.5f * (1.0f + erff(g * 0.70710678118654752f));
+    const float cdf = gauss_cdf(g);
     const float pdf = 0.39894228040143268f * __expf(-0.5f * g * g);
     a = g * cdf;
     da = cdf + g * pdf;
   } else if constexpr (ACT == ACT_GEGLU_TANH) {
-    const float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
-    const float t = tanhf(u);
+    // a = g s, s = sigmoid(2u) = (1 + tanh u) / 2; 1 - tanh^2 u = 4 s (1 - s)
+    const float s = sigmoidf_fast(2.0f * gelu_tanh_u(g));
     const float du = 0.79788456080286536f * (1.0f + 3.0f * 0.044715f * g * g);
-    a = 0.5f * g * (1.0f + t);
-    da = 0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * du;
+    a = g * s;
+    da = s + 2.0f * g * s * (1.0f - s) * du;
   } else {
     const float r = fmaxf(g, 0.0f);
     a = r * r;
@@ -215,33 +221,10 @@ __device__ __forceinline__ void act_fwd_bwd_t(float g, float alpha, float& a, fl
 // a(g) and a'(g) together (the backward epilogue needs both).
 __device__ __forceinline__ void act_fwd_bwd(int act, float g, float alpha, float& a, float& da) {
   switch (act) {
-    case ACT_SWIGLU: {
-      float s = sigmoidf_fast(alpha * g);
-      a = g * s;
-      da = s * (1.0f + alpha * g * (1.0f - s));
-      break;
-    }
-    case ACT_GEGLU: {
-      float cdf = 0.5f * (1.0f + erff(g * 0.70710678118654752f));
-      float pdf = 0.39894228040143268f * __expf(-0.5f * g * g);
-      a = g * cdf;
-      da = cdf + g * pdf;
-      break;
-    }
-    case ACT_GEGLU_TANH: {
-      float u = 0.79788456080286536f * (g + 0.044715f * g * g * g);
-      float t = tanhf(u);
-      float du = 0.79788456080286536f * (1.0f + 3.0f * 0.044715f * g * g);
-      a = 0.5f * g * (1.0f + t);
-      da = 0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * du;
-      break;
-    }
-    default: {
-      float r = fmaxf(g, 0.0f);
-      a = r * r;
-      da = 2.0f * r;
-      break;
-    }
+    case ACT_SWIGLU: act_fwd_bwd_t<ACT_SWIGLU>(g, alpha, a, da); break;
+    case ACT_GEGLU: act_fwd_bwd_t<ACT_GEGLU>(g, alpha, a, da); break;
+    case ACT_GEGLU_TANH: act_fwd_bwd_t<ACT_GEGLU_TANH>(g, alpha, a, da); break;
+    default: act_fwd_bwd_t<ACT_SRELU>(g, alpha, a, da); break;
   }
 }
 

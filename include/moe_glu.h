@@ -161,7 +161,11 @@ typedef struct {
 } moe_operand_t;
 
 /* Reads the device's compute-unit count once; call before graph capture.
- * Every other call initialises lazily on first use. */
+ * Every other call initialises lazily on first use.  The persistent grid of
+ * every GroupGemm is sized from that count ([BLOG] "Eliminando la
+ * sincronización host-device": a fixed launch whose work split is decided on
+ * the device, so the launch itself needs no host-side information that
+ * changes between steps). */
 moe_status_t moe_init(int device);
 
 const char* moe_status_string(moe_status_t s);
@@ -178,7 +182,11 @@ const char* moe_status_string(moe_status_t s);
  * zero.  Requires K % 64 == 0. */
 size_t moe_packed_weight_bytes(int E, int N, int K);
 
-/* Packs per-expert weights into the tile-blocked layout above.
+/* Packs per-expert weights into the tile-blocked layout above: the same
+ * offline weight preparation as the gate/up repack ([BLOG] "Optimizando GLU
+ * vía epílogos GEMM fusionados", Figure 2: the weights are rearranged once, off
+ * the training step, into the order the kernel consumes), here without the
+ * gate/up interleave, for the other GroupGemm operands.
  * src_layout MOE_B_NK: src is [E][N][K]; MOE_B_KN: src is [E][K][N] (transposed
  * while packing).  Uses: FC2's W2 [E][I][H] as MOE_B_KN with N = H, K = I;
  * dgrad's W2 [E][I][H] as MOE_B_NK with N = I, K = H; dX's plain W1 [E][H][2I]
@@ -247,8 +255,9 @@ moe_status_t moe_unpack_gate_up(const void* w1_packed, int E, int H, int I, void
  * expert the pairs keep ascending (t, j) order, so the result is unique and
  * deterministic.  If x (bf16 [T][H]) and xg (bf16 [T*k][H]) are given, xg
  * receives the gathered rows xg[r] = x[src[r]].  Given topk_ids outside
- * [0, E) are not grouped: their dst entries and the rows of src and xg from
- * offsets[E] on are left as they were.  Requires k <= E <= 1024, k <= 16,
+ * [0, E) are not grouped: their dst entries and the rows of xg from
+ * offsets[E] on are left as they were, and src entries from offsets[E] on are
+ * set to -1.  Requires k <= E <= 1024, k <= 16,
  * T*k < 2^31, H % 8 == 0. */
 moe_status_t moe_route_group(const float* logits, const int32_t* topk_ids, int T, int E, int k,
                              int32_t* topk_ids_out, int32_t* counts, int32_t* offsets,
@@ -338,7 +347,9 @@ moe_status_t moe_group_gemm_wgrad(const void* a, const void* b, int P, int Q,
                                   const moe_groups_t* groups, float* c, int accumulate,
                                   int cu_margin, void* stream);
 
-/* Unfused GLU pass (baseline and fallback): y = GLU epilogue of z, where z is
+/* Unfused GLU pass ([BLOG] "¿Dónde se va el cómputo en un bloque MoE?": the
+ * activation as its own memory-bound pass between the GEMMs, the baseline the
+ * fused epilogue replaces): y = GLU epilogue of z, where z is
  * the plain-order bf16 [M_cap][2I] FC1 output WITHOUT bias (bias, if any, is
  * added here).  Same arithmetic as the fused epilogue, as its own kernel. */
 moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
@@ -357,7 +368,10 @@ moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
 moe_status_t moe_dglu_unfused(const void* g, const void* z, const moe_groups_t* groups, int I,
                               const moe_epilogue_t* ep, void* dgu, void* stream);
 
-/* Standalone MXFP8 quantize/transpose (baseline, and offline weight prep) of
+/* Standalone MXFP8 quantize/transpose ([BLOG] "Fusionando cuantización MXFP8 y
+ * NVFP4": the separate pass that reads the bf16 activation output and writes
+ * the MXFP8 copy and its transposed version, which the fused epilogues
+ * replace; also the offline weight prep) of
  * a bf16 [R][C] matrix.  Row-wise blocks run along C.  Column-wise blocks run
  * down 32 rows; with groups (counts over the first rows, M_cap = R) they
  * restart at each group's first row exactly as in the fused epilogues and

@@ -114,16 +114,28 @@ def test_dsv3_fc2_sampled_rows(dsv3_run):
         assert_bf16_close(dsv3_run["out2"][rr], ref, what=f"dsv3 fc2 expert {e}")
 
 
+# Normwise relative error bounds of the backward outputs over the sampled rows
+# (twice what was measured: the element-wise 2e-2 (1 + |ref|) does not bind
+# where the values are ~1e-2).
+DGU_NORMWISE = 7e-5      # measured 3.25e-5
+DX_NORMWISE = 6e-4       # measured 2.71e-4
+
+
 def test_dsv3_dgrad_dglu_sampled_rows(dsv3_run):
     d = dsv3_run["d"]
     counts = d["counts"]
     rows = sample_rows(counts, per_group=1, seed=3)
     experts = expert_of_rows(counts, rows)
+    gs, rs = [], []
     for e in np.unique(experts):
         rr = rows[experts == e]
         pre_r, _ = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
         ref = O.dgrad_dglu(dsv3_run["dy2"][rr], [len(rr)], d["w2"][e:e + 1], pre_r, O.Epilogue())
-        assert_bf16_close(dsv3_run["dgu"][rr], ref, what=f"dsv3 dgu expert {e}", normwise=2e-2)
+        assert_bf16_close(dsv3_run["dgu"][rr], ref, what=f"dsv3 dgu expert {e}")
+        gs.append(dsv3_run["dgu"][rr])
+        rs.append(ref)
+    assert_bf16_close(np.concatenate(gs), np.concatenate(rs), what="dsv3 dgu (sampled rows)",
+                      normwise=DGU_NORMWISE, report=True)
 
 
 def test_dsv3_dx_sampled_rows(dsv3_run):
@@ -131,12 +143,17 @@ def test_dsv3_dx_sampled_rows(dsv3_run):
     counts = d["counts"]
     rows = sample_rows(counts, per_group=1, seed=4)
     experts = expert_of_rows(counts, rows)
+    gs, rs = [], []
     for e in np.unique(experts):
         rr = rows[experts == e]
         pre_r, _ = O.fc1_glu(d["x"][rr], [len(rr)], d["w1"][e:e + 1], O.Epilogue())
         dgu_r = O.dgrad_dglu(dsv3_run["dy2"][rr], [len(rr)], d["w2"][e:e + 1], pre_r, O.Epilogue())
         ref = O.dx(dgu_r, [len(rr)], d["w1"][e:e + 1])
-        assert_bf16_close(dsv3_run["dx"][rr], ref, what=f"dsv3 dx expert {e}", normwise=2e-2)
+        assert_bf16_close(dsv3_run["dx"][rr], ref, what=f"dsv3 dx expert {e}")
+        gs.append(dsv3_run["dx"][rr])
+        rs.append(ref)
+    assert_bf16_close(np.concatenate(gs), np.concatenate(rs), what="dsv3 dx (sampled rows)",
+                      normwise=DX_NORMWISE, report=True)
 
 
 def test_dsv3_extras_leave_outputs_unchanged(dsv3_run):

@@ -22,12 +22,12 @@ import pytest
 import workloads as W
 from oracle import formats as F
 from oracle import moe as O
-from tests.gpu_util import (assert_bf16_close, assert_mx_cols, assert_mx_rows, dev_bits, dev_i32,
-                            empty_bits, empty_bytes, expert_of_rows, host_bits, sample_rows)
+from tests.gpu_util import (MX_ACC_REL, assert_bf16_close, assert_mx_cols, assert_mx_gemm_close,
+                            assert_mx_rows, dev_bits, dev_i32, empty_bits, empty_bytes,
+                            expert_of_rows, host_bits, mx_acc_excess, mx_gemm_terms, sample_rows)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-MAX_FLIP = 0.25
 
 
 @pytest.fixture(scope="module")
@@ -118,8 +118,7 @@ def test_fc1_mx_row_copies_sampled_rows(run):
         gy.append(rr)
         ry.append(y)
     rr, ry = np.concatenate(gy), np.concatenate(ry)
-    assert_mx_rows(run["row_q"][rr], run["row_s"][rr], run["y"][rr], ry, what="row copies",
-                   max_flip=MAX_FLIP)
+    assert_mx_rows(run["row_q"][rr], run["row_s"][rr], run["y"][rr], ry, what="row copies")
 
 
 def test_fc1_mx_col_copies_sampled_blocks(run):
@@ -137,8 +136,7 @@ def test_fc1_mx_col_copies_sampled_blocks(run):
         n = min(32, int(off[e + 1]) - a)
         _, ry = O.fc1_glu(d["x"][a:a + n], [n], d["w1"][e:e + 1], O.Epilogue())
         assert_mx_cols(run["col_q"][:, a:a + n], run["col_s"][:, so[e] + j:so[e] + j + 1],
-                       run["y"][a:a + n], ry, [n], n, what=f"col copies expert {e} block {j}",
-                       max_flip=MAX_FLIP)
+                       run["y"][a:a + n], ry, [n], n, what=f"col copies expert {e} block {j}")
 
 
 def test_x_quantize_sampled_rows_bit_exact(run):
@@ -146,14 +144,6 @@ def test_x_quantize_sampled_rows_bit_exact(run):
     rows = sample_rows(d["counts"], per_group=1, seed=14, max_rows=32)
     q, s = O.mx_quantize_rows(d["x"][rows])
     assert np.array_equal(run["xq"][rows], q) and np.array_equal(run["xs"][rows], s)
-
-
-def _abs_bound(aq, as_, bq, bs):
-    """2^-14 sum_k |a_k b_k| from the dequantised operands (the block-scaled
-    MFMA's accumulation is not strict fp32)."""
-    A = np.abs(O.mx_dequantize_rows(aq, as_))
-    B = np.abs(O.mx_dequantize_rows(bq, bs))
-    return (A @ B.T) * 2.0 ** -14
 
 
 def test_fc1_mx_inputs_sampled_rows_and_columns(run):
@@ -174,7 +164,11 @@ def test_fc1_mx_inputs_sampled_rows_and_columns(run):
         wt = np.ascontiguousarray(d["w1"][e].T[np.concatenate([cols, I + cols])])   # [2c][H]
         q, s = O.mx_quantize_rows(wt)
         rp, ry = O.fc1_glu_mx(aq, as_, [len(rr)], q[None], s[None], O.Epilogue())
-        zb = _abs_bound(aq, as_, q, s)
+        gq, gs = run["xq"][rr], run["xs"][rr]
+        S, D, X = mx_gemm_terms(aq, as_, [len(rr)], q[None], s[None], gpu_aq=gq, gpu_as=gs)
+        cc = np.concatenate([cols, I + cols])
+        mx_acc_excess(run["pre_mx"][rr][:, cc], S, D, X, f"mx-input preact expert {e}")
+        zb = MX_ACC_REL * S + D
         c = len(cols)
         assert_bf16_close(run["pre_mx"][rr][:, np.concatenate([cols, I + cols])], rp,
                           what=f"mx-input preact expert {e}", extra=zb)
@@ -200,5 +194,5 @@ def test_fc2_mx_sampled_rows_and_columns(run):
         yq, ys = O.mx_quantize_rows(ry)
         bq, bs = O.mx_quantize_rows(np.ascontiguousarray(d["w2"][e].T[hs]))      # [h][I]
         ref = O.group_gemm_mx(yq, ys, [len(rr)], bq[None], bs[None])
-        assert_bf16_close(run["out2"][rr][:, hs], ref, what=f"fc2 mx expert {e}",
-                          extra=_abs_bound(yq, ys, bq, bs))
+        assert_mx_gemm_close(run["out2"][rr][:, hs], ref, yq, ys, [len(rr)], bq[None], bs[None],
+                             f"fc2 mx expert {e}", gpu_aq=run["row_q"][rr], gpu_as=run["row_s"][rr])

@@ -74,6 +74,33 @@ def test_group_pairs_with_invalid_ids_bruteforce(T, E, k, seed):
     assert dst.tolist() == bdst
 
 
+@pytest.mark.parametrize("T,E,k,seed", [(7, 4, 2, 0), (33, 8, 3, 1), (1, 3, 1, 2)])
+def test_gather_rows_against_loop_and_dst(T, E, k, seed):
+    """gather_rows (the expected value of every grouped-row check): grouped row
+    r is token src[r], element by element in a Python loop; and read through
+    dst, pair (t, j) lands on row dst[t][j] holding token t's row."""
+    rng = np.random.default_rng(300 + seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    H = 5
+    x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    ids, counts, offsets, dst, src = _route_bruteforce(logits, k)
+    xg = O.gather_rows(x, np.array(src, dtype=np.int32))
+    assert xg.shape == (T * k, H) and xg.dtype == np.uint16
+    for r in range(T * k):
+        for c in range(H):
+            assert int(xg[r, c]) == int(x[src[r], c])
+    for t in range(T):
+        for j in range(k):
+            assert np.array_equal(xg[dst[t][j]], x[t])
+    # a token permutation moves rows with their tokens: gathering x[perm] with
+    # src' = inv(perm)[src] gives the same grouped rows
+    perm = rng.permutation(T)
+    inv = np.argsort(perm)
+    assert np.array_equal(O.gather_rows(x[perm], inv[np.array(src)]), xg)
+    # no routed pair: an empty result with H columns
+    assert O.gather_rows(x, np.zeros(0, dtype=np.int32)).shape == (0, H)
+
+
 def test_route_invariants_gptoss():
     d = W.gptoss(with_weights=False)
     ids, counts, off, dst, src = O.route_topk(d["logits"], d["k"])
@@ -441,6 +468,36 @@ def test_group_gemm_mx_against_loops():
                     xb = F.e4m3_decode(bq[e, n, k]) * 2.0 ** (int(bs[e, n, k // 32]) - 127)
                     s += xa * xb
                 assert out[r, n] == F.f64_to_bf16_bits(np.array([s]))[0]
+
+
+
+def test_wgrad_abs_against_loops():
+    """wgrad_abs (the error scale of every weight-gradient GPU bound) is
+    sum over each group's rows of |a[r][i]| |b[r][j]|, written out as a loop;
+    signs never cancel (it bounds |wgrad| from above) and an empty group
+    gives zeros."""
+    rng = np.random.default_rng(52)
+    counts = np.array([4, 0, 3, 1])
+    M, P, Q = 8, 3, 5
+    a = W.to_bf16_bits(rng.standard_normal((M + 2, P)).astype(np.float32))
+    b = W.to_bf16_bits(rng.standard_normal((M + 2, Q)).astype(np.float32))
+    got = O.wgrad_abs(a, counts, b)
+    assert got.shape == (4, P, Q) and np.all(got[1] == 0.0)
+    A, B = F.bf16_bits_to_f64(a), F.bf16_bits_to_f64(b)
+    off = [0, 4, 4, 7, 8]
+    for e in range(4):
+        for i in range(P):
+            for j in range(Q):
+                s = 0.0
+                for r in range(off[e], off[e + 1]):
+                    s += abs(A[r, i]) * abs(B[r, j])
+                assert got[e, i, j] == pytest.approx(s, rel=1e-15, abs=1e-300)
+    assert np.all(np.abs(O.wgrad(a, counts, b)) <= got * (1 + 1e-12))
+    # all-positive operands: no cancellation, so it equals wgrad itself
+    ap, bp = a & np.uint16(0x7FFF), b & np.uint16(0x7FFF)
+    assert np.allclose(O.wgrad_abs(ap, counts, bp), O.wgrad(ap, counts, bp), rtol=1e-15, atol=0)
+    # flipping the sign of operand rows changes wgrad but not wgrad_abs
+    assert np.array_equal(O.wgrad_abs(a ^ np.uint16(0x8000), counts, b), got)
 
 
 # ------------------------------------------------------------------ weight gradients
