@@ -41,7 +41,8 @@ class EpilogueT(ctypes.Structure):
 
 class MxOutT(ctypes.Structure):
     _fields_ = [("row_q", ctypes.c_void_p), ("row_s", ctypes.c_void_p),
-                ("col_q", ctypes.c_void_p), ("col_s", ctypes.c_void_p), ("e5m2", ctypes.c_int32)]
+                ("col_q", ctypes.c_void_p), ("col_s", ctypes.c_void_p), ("e5m2", ctypes.c_int32),
+                ("col_blocked", ctypes.c_int32)]
 
 
 class GroupsT(ctypes.Structure):
@@ -79,6 +80,8 @@ _SIGS = {
     "moe_group_gemm_quant": ([ctypes.POINTER(OperandT), ctypes.POINTER(OperandT), _I, _I,
                               ctypes.POINTER(GroupsT), _P, ctypes.POINTER(MxOutT), _I, _P], _I),
     "moe_group_gemm_wgrad": ([_P, _P, _I, _I, ctypes.POINTER(GroupsT), _P, _I, _I, _P], _I),
+    "moe_group_gemm_wgrad_mx": ([ctypes.POINTER(OperandT), ctypes.POINTER(OperandT), _I, _I,
+                                 ctypes.POINTER(GroupsT), _P, _I, _I, _P], _I),
     "moe_glu_unfused": ([_P, ctypes.POINTER(GroupsT), _I, ctypes.POINTER(EpilogueT), _P, _P], _I),
     "moe_dglu_unfused": ([_P, _P, ctypes.POINTER(GroupsT), _I, ctypes.POINTER(EpilogueT), _P, _P], _I),
     "moe_mxfp8_quantize": ([_P, _I, _I, ctypes.POINTER(GroupsT), ctypes.POINTER(MxOutT), _P], _I),
@@ -151,10 +154,18 @@ def groups(counts, M_cap: int, offsets_out=None, status_out=None) -> GroupsT:
                          _ptr(status_out)), counts, offsets_out, status_out)
 
 
-def mx_out(row_q=None, row_s=None, col_q=None, col_s=None, e5m2: bool = False) -> MxOutT:
-    """MXFP8 output buffers; ``e5m2`` selects e5m2 element codes (gradients)."""
-    return _keep(MxOutT(_ptr(row_q), _ptr(row_s), _ptr(col_q), _ptr(col_s), 1 if e5m2 else 0),
-                 row_q, row_s, col_q, col_s)
+def mx_out(row_q=None, row_s=None, col_q=None, col_s=None, e5m2: bool = False,
+           col_blocked: bool = False) -> MxOutT:
+    """MXFP8 output buffers; ``e5m2`` selects e5m2 element codes (gradients);
+    ``col_blocked`` the K-tiled layout of the transposed copy."""
+    return _keep(MxOutT(_ptr(row_q), _ptr(row_s), _ptr(col_q), _ptr(col_s), 1 if e5m2 else 0,
+                        1 if col_blocked else 0), row_q, row_s, col_q, col_s)
+
+
+def mx_col_slots(M_cap: int, E: int, blocked: bool = False) -> int:
+    """Scale columns of a transposed MXFP8 copy (row length of col_s); the
+    codes of the blocked layout take 32 bytes per slot."""
+    return 4 * ((M_cap + 127) // 128 + E) if blocked else (M_cap + 31) // 32 + E
 
 
 def operand(data, dtype: int = DT_BF16, layout: int = 0, scales=None) -> OperandT:
@@ -257,6 +268,14 @@ def moe_group_gemm_wgrad(a, b, P, Q, grp: GroupsT, c, accumulate: bool = False,
     _check("moe_group_gemm_wgrad",
            _lib.moe_group_gemm_wgrad(_ptr(a), _ptr(b), P, Q, ctypes.byref(grp), _ptr(c),
                                      1 if accumulate else 0, cu_margin, _stream(stream)))
+
+
+def moe_group_gemm_wgrad_mx(a: OperandT, b: OperandT, P, Q, grp: GroupsT, c,
+                            accumulate: bool = False, cu_margin: int = 0, stream=None):
+    _check("moe_group_gemm_wgrad_mx",
+           _lib.moe_group_gemm_wgrad_mx(ctypes.byref(a), ctypes.byref(b), P, Q, ctypes.byref(grp),
+                                        _ptr(c), 1 if accumulate else 0, cu_margin,
+                                        _stream(stream)))
 
 
 def moe_glu_unfused(z, grp: GroupsT, I, ep: EpilogueT, y, stream=None):

@@ -27,7 +27,8 @@ LIB = os.path.join(PKG, "libmoeglu.so")
 # per activation (MOE_ACT = the moe_act_t value), which also spreads the
 # largest translation units over more parallel jobs.
 SOURCES = ([("api.hip", "api", []), ("gemm_fwd.hip", "gemm_fwd", []), ("gemm_bwd.hip", "gemm_bwd", []),
-            ("gemm_mx.hip", "gemm_mx", []), ("gemm_wgrad.hip", "gemm_wgrad", [])]
+            ("gemm_mx.hip", "gemm_mx", []), ("gemm_wgrad.hip", "gemm_wgrad", []),
+            ("gemm_wgrad_mx.hip", "gemm_wgrad_mx", [])]
            + [(f"gemm_act_{d}.hip", f"gemm_act_{d}_{a}", [f"-DMOE_ACT={a}"])
               for d in ("bwd", "fwd") for a in range(4)])
 ARCH = "gfx950"

@@ -43,6 +43,8 @@ moe_status_t check_mx(const moe_mx_out_t* mx) {
   if ((mx->row_q == nullptr) != (mx->row_s == nullptr)) return MOE_ERR_NULL;
   if ((mx->col_q == nullptr) != (mx->col_s == nullptr)) return MOE_ERR_NULL;
   if (mx->e5m2 != 0 && mx->e5m2 != 1) return MOE_ERR_UNSUPPORTED;
+  if (mx->col_blocked != 0 && mx->col_blocked != 1) return MOE_ERR_UNSUPPORTED;
+  if (mx->col_blocked && mx->col_q && !aligned16(mx->col_q)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -88,7 +90,8 @@ void fill_mx(GemmArgs* a, const moe_mx_out_t* mx, int cols, const moe_groups_t* 
   a->col_s = mx ? mx->col_s : nullptr;
   a->mx_cols = cols;
   a->mx_e5 = mx ? mx->e5m2 : 0;
-  a->col_s_ld = (g->M_cap + 31) / 32 + g->E;
+  a->col_blocked = mx ? mx->col_blocked : 0;
+  a->col_s_ld = a->col_blocked ? 4 * ((g->M_cap + 127) / 128 + g->E) : (g->M_cap + 31) / 32 + g->E;
 }
 
 // Persistent grid: one workgroup per usable CU (the kernel holds a CU's LDS),
@@ -490,6 +493,44 @@ moe_status_t moe_group_gemm_wgrad(const void* a, const void* b, int P, int Q,
   return launch_group_gemm_wgrad(g, grid, (hipStream_t)stream);
 }
 
+moe_status_t moe_group_gemm_wgrad_mx(const moe_operand_t* a, const moe_operand_t* b, int P, int Q,
+                                     const moe_groups_t* groups, float* c, int accumulate,
+                                     int cu_margin, void* stream) {
+  moe_status_t st = check_groups(groups);
+  if (st != MOE_OK) return st;
+  if (!a || !b || !c || !a->data || !b->data || !a->scales || !b->scales) return MOE_ERR_NULL;
+  auto is_mx = [](int dt) { return dt == MOE_DT_MXFP8 || dt == MOE_DT_MXFP8_E5M2; };
+  if (!is_mx(a->dtype) || !is_mx(b->dtype)) return MOE_ERR_UNSUPPORTED;
+  if (P < 64 || P % 64 != 0 || Q < 64 || Q % 64 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(a->data) || !aligned16(b->data) || !aligned4(a->scales) || !aligned4(b->scales) ||
+      !aligned16(c))
+    return MOE_ERR_ALIGN;
+  const int S = 4 * ((groups->M_cap + 127) / 128 + groups->E);   // slots per copied column
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  int cus;
+  if ((st = ensure_init(&cus)) != MOE_OK) return st;
+  fill_groups(&g, groups);
+  g.A = static_cast<const uint16_t*>(a->data);
+  g.B = static_cast<const uint16_t*>(b->data);
+  g.a_scales = a->scales;
+  g.b_scales = b->scales;
+  g.K = 32 * S;                   // bytes per copied column (row of each operand)
+  g.ldb = 32 * S;
+  g.N = Q;
+  g.wg_P = P;
+  g.ntiles_m = (P + GM_BM - 1) / GM_BM;
+  g.ntiles_n = (Q + GM_BN - 1) / GM_BN;
+  g.Cf = c;
+  g.accumulate = accumulate ? 1 : 0;
+  int usable = cus - (cu_margin > 0 ? cu_margin : 0);
+  if (usable < 1) usable = 1;
+  const long long tiles = (long long)groups->E * g.ntiles_m * g.ntiles_n;
+  const int grid = (int)(tiles < usable ? tiles : usable);
+  return launch_group_gemm_wgrad_mx(g, a->dtype == MOE_DT_MXFP8_E5M2, b->dtype == MOE_DT_MXFP8_E5M2,
+                                    grid, (hipStream_t)stream);
+}
+
 moe_status_t moe_glu_unfused(const void* z, const moe_groups_t* groups, int I,
                              const moe_epilogue_t* ep, void* y, void* stream) {
   moe_status_t st = check_groups(groups);
@@ -546,12 +587,13 @@ moe_status_t moe_mxfp8_quantize(const void* v, int R, int C, const moe_groups_t*
                        mx->e5m2);
   }
   if (mx->col_q && R > 0) {
-    int s_ld = (R + 31) / 32 + (groups ? E : 0);
-    long long by = (long long)(R + 31) / 32 + E;
+    const int Eg = groups ? E : 0;
+    int s_ld = mx->col_blocked ? 4 * ((R + 127) / 128 + Eg) : (R + 31) / 32 + Eg;
+    long long by = s_ld;
     int gy = (int)(by < 65535 ? by : 65535);
     hipLaunchKernelGGL(mx_cols_kernel, dim3((C + 255) / 256, gy), dim3(256), 0, s,
                        static_cast<const uint16_t*>(v), R, C, counts, E, mx->col_q, mx->col_s, s_ld,
-                       mx->e5m2);
+                       mx->e5m2, mx->col_blocked);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

@@ -493,25 +493,28 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
 
 // Column-wise: one thread per (column, 32-row block); blocks restart at each
 // group's first row (with counts) or run over all R rows (without).  Grid.y
-// walks blocks; grid.x covers columns in 256-column chunks.
+// walks blocks (scale slots); grid.x covers columns in 256-column chunks.
+// blocked: the K-tiled layout (slots of 32 bytes, each group a whole number
+// of 4-slot K-tiles; slots past a group's rows get zero codes, scale 127).
 __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict__ v, int R, int C,
                                                       const int* __restrict__ counts, int E,
                                                       uint8_t* __restrict__ q,
-                                                      uint8_t* __restrict__ s, int s_ld, int e5) {
+                                                      uint8_t* __restrict__ s, int s_ld, int e5,
+                                                      int blocked) {
   __shared__ GroupScan gs;
   int nblocks;
   if (counts) {
-    build_group_scan<256>(gs, counts, E, R, 1, 0, nullptr, nullptr, false);
+    build_group_scan<256>(gs, counts, E, R, 1, 0, nullptr, nullptr, false, blocked != 0);
     nblocks = gs.mxs_off[E];
   } else {
-    nblocks = (R + 31) >> 5;
+    nblocks = blocked ? 4 * ((R + 127) >> 7) : (R + 31) >> 5;
   }
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= C) return;
   for (int b = blockIdx.y; b < nblocks; b += gridDim.y) {
     int r0, nvalid;
     if (counts) {
-      int lo = 0, hi = E;  // group owning scale column b: last e with mxs_off[e] <= b
+      int lo = 0, hi = E;  // group owning scale slot b: last e with mxs_off[e] <= b
       while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
         if (gs.mxs_off[mid] <= b) lo = mid; else hi = mid;
@@ -523,12 +526,14 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict
       r0 = b * 32;
       nvalid = min(32, R - r0);
     }
+    if (nvalid < 0) nvalid = 0;   // a padding slot of the K-tiled layout
     float x[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) x[i] = (i < nvalid) ? bf16_to_f32(v[(long long)(r0 + i) * C + c]) : 0.0f;
     uint32_t w[8];
-    uint8_t sb = mx_quant32(x, nvalid, w, e5 != 0);
-    store_codes32(q + (long long)c * R + r0, w, nvalid);
+    uint8_t sb = nvalid > 0 ? mx_quant32(x, nvalid, w, e5 != 0) : (uint8_t)127;
+    if (blocked) store_codes32_slot(q + ((long long)c * s_ld + b) * 32, w, nvalid);
+    else store_codes32(q + (long long)c * R + r0, w, nvalid);
     s[(long long)c * s_ld + b] = sb;
   }
 }

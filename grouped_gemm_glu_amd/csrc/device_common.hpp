@@ -119,6 +119,20 @@ __device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32
   return e8m0_byte(E);
 }
 
+// One slot of the K-tiled transposed layout: 32 codes to a 16-byte aligned
+// dst, the codes of rows from nvalid on (past the group's last row) zero.
+__device__ __forceinline__ void store_codes32_slot(uint8_t* dst, const uint32_t* w, int nvalid) {
+  uint32_t m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = nvalid - 4 * i;   // valid bytes of word i
+    m[i] = k >= 4 ? w[i] : (k <= 0 ? 0u : (w[i] & ((1u << (8 * k)) - 1u)));
+  }
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  d[0] = make_uint4(m[0], m[1], m[2], m[3]);
+  d[1] = make_uint4(m[4], m[5], m[6], m[7]);
+}
+
 // 32 codes (w, little-endian) to dst, which has any alignment.  A full block
 // at a non-4-byte-aligned address (a transposed block starting at a group's
 // first row) goes out as h = 4 - (dst % 4) head bytes, 7 aligned dwords
@@ -249,7 +263,7 @@ struct GroupScan {
   int row_off[kMaxExperts + 1];   // o_e of the clamped counts
   int tile_off[kMaxExperts + 1];  // prefix of full-height m-tiles per expert
   int half_off[kMaxExperts + 1];  // prefix of half-height m-tiles (0 or 1 per expert)
-  int mxs_off[kMaxExperts + 1];   // prefix of ceil(m_e/32): MX column-scale offsets
+  int mxs_off[kMaxExperts + 1];   // MX column-scale slot of each group's first block
   long long wave_tmp[16];
   long long total_raw;
 };
@@ -274,13 +288,14 @@ __device__ __forceinline__ T block_incl_scan(T v, long long* wave_tmp) {
 // Fills gs from counts[0..E) for m-tiles of BM rows.  With half_rows > 0 an
 // expert's last m-tile counts as a half-height tile (half_off) when it holds
 // 1 .. half_rows rows, else as a full one (tile_off); half_rows = 0 makes every
-// m-tile full.  NT threads, each owning up to kMaxExperts/NT consecutive
+// m-tile full.  mxs_off: the first column-scale slot of each group, ceil(m/32)
+// slots per group, or with mx_blocked 4 ceil(m/128) (the K-tiled layout).  NT threads, each owning up to kMaxExperts/NT consecutive
 // experts.  The writer workgroup also stores the clamped offsets and the
 // status bits.  gs is valid after the final barrier.
 template <int NT>
 __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, int E, int M_cap,
                                  int BM, int half_rows, int* offsets_out, int* status_out,
-                                 bool writer) {
+                                 bool writer, bool mx_blocked = false) {
   const int t = threadIdx.x;
   constexpr int PER = (kMaxExperts + NT - 1) / NT;
   int c[PER];
@@ -300,6 +315,7 @@ __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, 
   int mloc[PER];
   auto n_half = [&](int m) { const int r = m % BM; return (half_rows > 0 && r > 0 && r <= half_rows) ? 1 : 0; };
   auto n_full = [&](int m) { return (m + BM - 1) / BM - n_half(m); };
+  auto n_mx = [&](int m) { return mx_blocked ? 4 * ((m + 127) >> 7) : (m + kMxBlock - 1) / kMxBlock; };
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     int e = t * PER + i;
@@ -311,7 +327,7 @@ __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, 
     run += c[i];
     mt_sum += n_full(m);
     hf_sum += n_half(m);
-    mx_sum += (m + kMxBlock - 1) / kMxBlock;
+    mx_sum += n_mx(m);
   }
   if (t == NT - 1) gs.total_raw = run;
   int mt_incl = block_incl_scan<NT, int>(mt_sum, gs.wave_tmp);
@@ -328,7 +344,7 @@ __device__ void build_group_scan(GroupScan& gs, const int* __restrict__ counts, 
     }
     mt_run += n_full(mloc[i]);
     hf_run += n_half(mloc[i]);
-    mx_run += (mloc[i] + kMxBlock - 1) / kMxBlock;
+    mx_run += n_mx(mloc[i]);
   }
   if (t == NT - 1) {
     gs.tile_off[E] = mt_run;

@@ -85,8 +85,10 @@ enum { EPI_GLU = 0, EPI_STORE = 1, EPI_DGLU = 2, EPI_GLU_MX = 3, EPI_WGRAD = 4, 
 enum { BL_NK = 0, BL_KN = 1, BL_PACKED = 2 };
 // operand element type: bf16, or MXFP8 (OCP e4m3 codes with one E8M0 scale
 // per 32 consecutive K values, consumed by the block-scaled MFMA); AT_MX_A5:
-// the same with e5m2 codes for A (a gradient) and e4m3 for B
-enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2 };
+// the same with e5m2 codes for A (a gradient) and e4m3 for B; AT_MX_B5 and
+// AT_MX_AB5: e5m2 codes for B, or for both (weight gradients, where both
+// operands are transposed MXFP8 copies of activations or gradients)
+enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2, AT_MX_B5 = 3, AT_MX_AB5 = 4 };
 
 // Waves per workgroup.  4: a 2 x 2 grid of waves, one per SIMD, each owning
 // a 128 x 128 sub-tile.  8: a 4 x 2 grid of 64 x 128 sub-tiles, two waves per
@@ -120,7 +122,8 @@ struct GemmArgs {
   uint8_t* col_s;
   int mx_cols;              // columns of the quantised output (row length of row_q)
   int mx_e5;                // 1: the quantised copies hold e5m2 codes, 0: e4m3fn
-  int col_s_ld;             // ceil(M_cap/32) + E
+  int col_blocked;          // 1: transposed copy in the K-tiled layout (slots of 32 rows)
+  int col_s_ld;             // slots per column: ceil(M_cap/32) + E, or 4 (ceil(M_cap/128) + E)
   int ntiles_n;
   // MXFP8 operands: A scales [M_cap][K/32]; B scales in the tile-blocked
   // order [E][ceil(N/256)][K/128][256][4] (4 consecutive K blocks per row)
@@ -234,14 +237,26 @@ __device__ __forceinline__ void mx_from_stage_map(const Stg& stg, int rows_valid
   if (p.col_q) {
     // items of two adjacent columns x 32 rows: one 4-byte LDS read per row;
     // the row blocks of a column pair are consecutive items, so neighbouring
-    // lanes store neighbouring 32-byte pieces of a column
+    // lanes store neighbouring 32-byte pieces of a column.  K-tiled layout:
+    // a group's last tile also fills its slots up to the next multiple of 4
+    // (128 rows) with zero codes and scale byte 127.
     const int nrb = (rows_valid + 31) >> 5;
+    const int npad = p.col_blocked ? 4 * ((rows_valid + 127) >> 7) : nrb;
     const int nc2 = ncols >> 1;
     const int nrbt = stg.rows() >> 5;
+    const long long slot_bytes = 32LL * p.col_s_ld;   // K-tiled: one column's codes
     for (int it = t; it < nc2 * nrbt; it += NT) {
       const int rb = it % nrbt, c2 = it / nrbt;
       const long long gc = gcol(2 * c2);
-      if (rb >= nrb || gc < 0) continue;
+      if (rb >= npad || gc < 0) continue;
+      if (rb >= nrb) {   // K-tiled padding slot
+        const uint32_t z[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        store_codes32_slot(p.col_q + gc * slot_bytes + (scol0 + rb) * 32LL, z, 0);
+        store_codes32_slot(p.col_q + (gc + 1) * slot_bytes + (scol0 + rb) * 32LL, z, 0);
+        p.col_s[gc * p.col_s_ld + scol0 + rb] = 127;
+        p.col_s[(gc + 1) * p.col_s_ld + scol0 + rb] = 127;
+        continue;
+      }
       int nvalid = rows_valid - rb * 32;
       if (nvalid > 32) nvalid = 32;
       float v0[32], v1[32];
@@ -253,10 +268,13 @@ __device__ __forceinline__ void mx_from_stage_map(const Stg& stg, int rows_valid
       }
       uint32_t w[8];
       uint8_t sb = mx_quant32(v0, nvalid, w, p.mx_e5 != 0);
-      store_codes32(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
+      if (p.col_blocked) store_codes32_slot(p.col_q + gc * slot_bytes + (scol0 + rb) * 32LL, w, nvalid);
+      else store_codes32(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[gc * p.col_s_ld + scol0 + rb] = sb;
       sb = mx_quant32(v1, nvalid, w, p.mx_e5 != 0);
-      store_codes32(p.col_q + (gc + 1) * p.M_cap + grow0 + rb * 32, w, nvalid);
+      if (p.col_blocked)
+        store_codes32_slot(p.col_q + (gc + 1) * slot_bytes + (scol0 + rb) * 32LL, w, nvalid);
+      else store_codes32(p.col_q + (gc + 1) * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[(gc + 1) * p.col_s_ld + scol0 + rb] = sb;
     }
   }
@@ -364,22 +382,32 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8 stages also carry the tile's
   // E8M0 scales: 256 rows x 4 bytes for A and for B after the two tiles.
   constexpr bool MXT = AT != AT_BF16;
-  // block-scaled MFMA format codes (0 = e4m3, 1 = e5m2) of the weight (the
-  // first source) and of the activations (the second source)
-  constexpr int FMT_A = AT == AT_MX_A5 ? 1 : 0;
+  // block-scaled MFMA format codes (0 = e4m3, 1 = e5m2) of B (the first
+  // source) and of A (the second source)
+  constexpr int FMT_A = (AT == AT_MX_A5 || AT == AT_MX_AB5) ? 1 : 0;
+  constexpr int FMT_B = (AT == AT_MX_B5 || AT == AT_MX_AB5) ? 1 : 0;
   constexpr int ESZ = MXT ? 1 : 2;            // operand element bytes
   constexpr int KSTEPS = MXT ? 2 : 4;         // k-steps per K-tile
   static_assert(!MXT || (BLAY == BL_PACKED && (EPI == EPI_STORE || EPI == EPI_GLU ||
-                                                EPI == EPI_GLU_MX)),
-                "MXFP8 inputs: packed B; plain store or GLU epilogue");
+                                                EPI == EPI_GLU_MX)) ||
+                    (BLAY == BL_NK && EPI == EPI_WGRAD),
+                "MXFP8 inputs: packed B with a plain store or GLU epilogue, or a weight gradient");
   static_assert(2 * GM_TILE_BYTES + 2048 <= GM_STAGE_ALLOC, "scale slots");
-  // Weight gradients reduce over a group's rows: both operands are stored
-  // [rows][columns] with the reduction dimension as the row index.  They go
-  // to LDS as they are (LDS-DMA, wg_off layout) and the MFMA fragments come
-  // out of the LDS transpose read.  Other N-contiguous B operands go through
-  // a register transpose.
+  // Weight gradients reduce over a group's rows.  bf16 (WGT): both operands
+  // are stored [rows][columns] with the reduction dimension as the row index;
+  // they go to LDS as they are (LDS-DMA, wg_off layout) and the MFMA
+  // fragments come out of the LDS transpose read.  MXFP8 (WGM): both
+  // operands are transposed copies in the K-tiled layout, [columns][slots of
+  // 32 rows], so each is K-contiguous with its own block scales and takes
+  // the ordinary MXFP8 path; group e's reduction is its 4 ceil(m_e/128) slots
+  // from slot 4 sum_{j<e} ceil(m_j/128), whole 128-code K-tiles zero-padded
+  // past the group's rows.  Other N-contiguous B operands go through a
+  // register transpose.
   constexpr bool WG = EPI == EPI_WGRAD;
-  static_assert(!WG || (BLAY == BL_KN && !MXT), "weight gradient: N-contiguous bf16 operands");
+  constexpr bool WGM = WG && MXT;
+  constexpr bool WGT = WG && !MXT;
+  static_assert(!WG || (BLAY == BL_KN && !MXT) || (BLAY == BL_NK && MXT),
+                "weight gradient: N-contiguous bf16 operands or K-tiled MXFP8 copies");
   constexpr bool KNR = BLAY == BL_KN && !WG;
   constexpr int NW = gm_waves(EPI, BLAY, AT);   // waves per workgroup (4 or 8)
   constexpr int NTH = 64 * NW;           // threads
@@ -397,8 +425,10 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
 
-  build_group_scan<NTH>(gs, p.counts, p.E, p.M_cap, GM_BM, WG ? 0 : GM_BM / 2, p.offsets_out,
-                          p.status_out, blockIdx.x == 0);
+  // (MXFP8 weight gradient: 128-row m-tiles, so tile_off[e] is the group's
+  // first K-tile of the column copies)
+  build_group_scan<NTH>(gs, p.counts, p.E, p.M_cap, WGM ? 128 : GM_BM, WG ? 0 : GM_BM / 2,
+                          p.offsets_out, p.status_out, blockIdx.x == 0, p.col_blocked != 0);
   if (WG) {
     // Every expert owns the same number of output tiles but its tiles cost
     // m_e: hand them out largest group first (ties: lower id), the order kept
@@ -484,10 +514,12 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     const int m_e = gs.row_off[e + 1] - g_row0;
     // grouped GEMM: the tile's first grouped row; weight gradient: the
     // group's first row (the reduction runs over all m_e rows)
-    const int row0 = WG ? g_row0 : g_row0 + mt * GM_BM;
+    // (MXFP8 weight gradient: A's rows are the output rows mt*256 ..)
+    const int row0 = WGT ? g_row0 : (WGM ? mt * GM_BM : g_row0 + mt * GM_BM);
     const int rows_valid = WG ? min(GM_BM, p.wg_P - mt * GM_BM) : min(GM_BM, m_e - mt * GM_BM);
     const int n0 = nt * GM_BN;
-    const int nk_t = WG ? (m_e + 63) / 64 : nk;      // K-tiles of this tile
+    const int nk_t = WGT ? (m_e + 63) / 64 : (WGM ? (m_e + 127) / 128 : nk);   // K-tiles of this tile
+    const int kt0 = WGM ? gs.tile_off[e] : 0;        // first K-tile (MXFP8 weight gradient)
 
     // The tile body for MI 32-row MFMA blocks per wave, NW / 2 wave rows:
     // the 256-row tile (4 waves: MI = 4, waves 128 x 128; 8 waves: MI = 2,
@@ -511,16 +543,16 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // rows of a group's last m-tile read zeros instead of the next group's
     // rows, which costs no memory traffic, and MFMAs on zero operands draw
     // less power on this power-limited chip.
-    const uint32_t a_stride = WG ? (uint32_t)p.wg_P * 2u : (uint32_t)p.K * ESZ;
+    const uint32_t a_stride = WGT ? (uint32_t)p.wg_P * 2u : (uint32_t)p.K * ESZ;
     // weight gradient: only the group's rows (the next group's rows read zero)
-    const long long a_bytes = (long long)(WG ? m_e : rows_valid) * a_stride;
+    const long long a_bytes = (long long)(WGT ? m_e : rows_valid) * a_stride;
     const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A);
     const rsrc_t rsA = make_rsrc(Ab + (long long)row0 * a_stride, a_bytes);
-    const uint8_t* Bb = WG ? reinterpret_cast<const uint8_t*>(p.B) + (long long)row0 * p.ldb * 2
-                           : reinterpret_cast<const uint8_t*>(p.B) + (long long)e * p.b_estride * ESZ;
+    const uint8_t* Bb = WGT ? reinterpret_cast<const uint8_t*>(p.B) + (long long)row0 * p.ldb * 2
+                            : reinterpret_cast<const uint8_t*>(p.B) + (long long)e * p.b_estride * ESZ;
     const uint32_t b_stride = (uint32_t)p.ldb * ESZ;
     rsrc_t rsB;
-    if (WG)
+    if (WGT)
       rsB = make_rsrc(Bb, (long long)m_e * b_stride);
     else if (BLAY == BL_NK)
       rsB = make_rsrc(Bb + (long long)n0 * b_stride, (long long)(p.N - n0) * b_stride);
@@ -530,12 +562,14 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       rsB = make_rsrc(Bb, p.b_estride * ESZ);
 
     // MXFP8 scales of the tile: A rows row0.. (K/32 bytes each), B's blocked
-    // 1 KB per K-tile
+    // 1 KB per K-tile (weight gradient: B rows n0.., K/32 bytes each)
     const uint32_t sa_stride = (uint32_t)p.K / 32u;
+    const uint32_t sb_stride = (uint32_t)p.ldb / 32u;
     rsrc_t rsSA, rsSB;
     if (MXT) {
       rsSA = make_rsrc(p.a_scales + (long long)row0 * sa_stride, (long long)rows_valid * sa_stride);
-      rsSB = make_rsrc(p.b_scales + ((long long)e * NT + nt) * nk * 1024, (long long)nk * 1024);
+      rsSB = WGM ? make_rsrc(p.b_scales + (long long)n0 * sb_stride, (long long)(p.N - n0) * sb_stride)
+                 : make_rsrc(p.b_scales + ((long long)e * NT + nt) * nk * 1024, (long long)nk * 1024);
     }
 
     // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (8 rows);
@@ -600,7 +634,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     };
     auto issue_direct = [&](int kt, uint8_t* sa) {
       const bool in = kt < nk_t;
-      if constexpr (WG) {
+      if constexpr (WGT) {
         const long long r0 = (long long)kt * 64;
         const rsrc_t rak = in ? make_rsrc(Ab + ((long long)row0 + r0) * a_stride,
                                           ((long long)m_e - r0) * a_stride)
@@ -610,23 +644,22 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
         issue_wg(rbk, sa + GM_TILE_BYTES, b_stride, (uint32_t)n0 * 2u);
         return;
       }
-      if (!WG)
-        issue_tile(std::integral_constant<int, TBM>{}, in ? rsA : rsZ, sa, a_stride,
-                   (uint32_t)kt * 128u);
+      const uint32_t kk = (uint32_t)(kt0 + kt);   // K-tile within the rows
+      issue_tile(std::integral_constant<int, TBM>{}, in ? rsA : rsZ, sa, a_stride, kk * 128u);
       if (BLAY == BL_NK)
         issue_tile(std::integral_constant<int, GM_BN>{}, in ? rsB : rsZ, sa + GM_TILE_BYTES,
-                   b_stride, (uint32_t)kt * 128u);
+                   b_stride, kk * 128u);
       if (BLAY == BL_PACKED)
         issue_block(in ? rsB : rsZ, sa + GM_TILE_BYTES, (uint32_t)kt * GM_TILE_BYTES);
       if (MXT) {   // 4 scale bytes per row: one dword per lane, 64 rows per wave
         const uint32_t r = (uint32_t)(wave * 64 + lane_t);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             in ? rsSA : rsZ, (__attribute__((address_space(3))) void*)(sa + 2 * GM_TILE_BYTES + wave * 256),
-            4, r * sa_stride, (uint32_t)kt * 4u, 0, 0);
+            4, r * sa_stride, kk * 4u, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             in ? rsSB : rsZ,
             (__attribute__((address_space(3))) void*)(sa + 2 * GM_TILE_BYTES + 1024 + wave * 256), 4,
-            r * 4u, (uint32_t)kt * 1024u, 0, 0);
+            WGM ? r * sb_stride : r * 4u, WGM ? kk * 4u : kk * 1024u, 0, 0);
       }
     };
     u32x4 rb[8];
@@ -676,7 +709,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       const uint8_t* sb = sa + GM_TILE_BYTES;
       const int h = lane_t >> 5;
       const int ra = wm * HR + (lane_t & 31), rbw = wn * 128 + (lane_t & 31);
-      if constexpr (WG) {
+      if constexpr (WGT) {
         // lane l names row ks*16 + 8 (l/32) + 4 t + (l%16)/4 at column
         // c0 + 16 ((l/16) % 2) + 4 (l % 4) and so receives column c0 + l % 32
         // at rows ks*16 + 8 (l/32) + 4 t .. + 3: two reads (t = 0, 1) give
@@ -748,10 +781,10 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
             const int sB = (int)(scb[sset][j] >> sh), sA = (int)(sca[sset][i] >> sh);
             if (ks == 0)
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  bfx[buf][j], afx[buf][i], acc[i][j], 0, FMT_A, 0, sB, 0, sA);
+                  bfx[buf][j], afx[buf][i], acc[i][j], FMT_B, FMT_A, 0, sB, 0, sA);
             else
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  bfx[buf][j], afx[buf][i], acc[i][j], 0, FMT_A, 2, sB, 2, sA);
+                  bfx[buf][j], afx[buf][i], acc[i][j], FMT_B, FMT_A, 2, sB, 2, sA);
           }
         }
     };
@@ -776,7 +809,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // issued as a burst right after the barrier, the four waves' DMA
     // instructions queue at the address unit and hold up the MFMAs issued
     // behind them.
-    constexpr int NVM = WG ? 16 : (TBM + GM_BN) / (8 * NW);
+    constexpr int NVM = WGT ? 16 : (TBM + GM_BN) / (8 * NW);
     auto mfma_step_dma = [&](int buf, int sset, int ks) {
       mfmas(buf, sset, ks);
       static_for<NMF>([&](auto gc) {

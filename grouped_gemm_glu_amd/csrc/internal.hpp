@@ -45,5 +45,8 @@ MOE_DECLARE_ACT_LAUNCHERS(3)
 #undef MOE_DECLARE_ACT_LAUNCHERS
 // K-grouped weight gradient (fp32 output)
 moe_status_t launch_group_gemm_wgrad(const GemmArgs& args, int grid, hipStream_t stream);
+// the same on K-tiled MXFP8 column copies; a_e5 / b_e5: e5m2 codes
+moe_status_t launch_group_gemm_wgrad_mx(const GemmArgs& args, bool a_e5, bool b_e5, int grid,
+                                        hipStream_t stream);
 
 }  // namespace moe

@@ -114,16 +114,27 @@ typedef struct {
  *                                          row; group e's scales start at column
  *                                          sum_{j<e} ceil(m_j/32)
  * Any pointer may be NULL (that copy is skipped); row_q/row_s and col_q/col_s
- * go in pairs.  No alignment requirement.
+ * go in pairs.  No alignment requirement (col_blocked = 1: 16 bytes).
  * e5m2 = 1 selects OCP e5m2 elements instead (the gradient format of an
  * MXFP8 recipe: largest value 57344 = 1.75 * 2^15, the scale rule with 57344
- * in place of 448); 0 = e4m3fn.  (host struct) */
+ * in place of 448); 0 = e4m3fn.
+ * col_blocked = 1 writes the transposed copy in the K-tiled layout that the
+ * MXFP8 weight-gradient GroupGemm (moe_group_gemm_wgrad_mx) reads, the copy
+ * the pages keep "for back prop": a row of col_s has S = 4 (ceil(R/128) + E)
+ * slots and the matching row of col_q 32 S bytes, slot s holding one 32-row
+ * block (its scale byte at col_s[c][s], its 32 codes at col_q[c][32 s ..]);
+ * group e's blocks take slots so_e, so_e + 1, ... with so_e = 4 sum_{j<e}
+ * ceil(m_j/128), so every group starts on a 128-code boundary, and the slots
+ * up to so_e + 4 ceil(m_e/128) that no row reaches (and the codes of a partial
+ * block past the group's last row) hold zero codes with scale byte 127.
+ * col_blocked = 0 is the dense layout above.  (host struct) */
 typedef struct {
   uint8_t* row_q;
   uint8_t* row_s;
   uint8_t* col_q;
   uint8_t* col_s;
   int32_t e5m2;
+  int32_t col_blocked;
 } moe_mx_out_t;
 
 /* Expert groups.  The counts are the ONLY copy of the group sizes and stay in
@@ -142,7 +153,8 @@ typedef struct {
 typedef enum {
   MOE_DT_BF16 = 0,
   MOE_DT_MXFP8 = 1,         /* e4m3fn bytes + E8M0 scales, 32-blocks along K */
-  MOE_DT_MXFP8_E5M2 = 2     /* e5m2 bytes + E8M0 scales (a gradient, e.g. dgu for dX); A only */
+  MOE_DT_MXFP8_E5M2 = 2     /* e5m2 bytes + E8M0 scales (a gradient, e.g. dgu for dX); the A operand
+                               of moe_group_gemm_quant, either operand of moe_group_gemm_wgrad_mx */
 } moe_dtype_t;
 
 typedef enum {
@@ -346,6 +358,26 @@ moe_status_t moe_group_gemm_quant(const moe_operand_t* a, const moe_operand_t* b
 moe_status_t moe_group_gemm_wgrad(const void* a, const void* b, int P, int Q,
                                   const moe_groups_t* groups, float* c, int accumulate,
                                   int cu_margin, void* stream);
+
+/* MXFP8 weight gradients ([BLOG] "Fusionando cuantización MXFP8 y NVFP4": the
+ * epilogues also write a transposed MXFP8 copy "for back prop"; these are
+ * the products that read it): the same K-grouped GroupGemm as
+ * moe_group_gemm_wgrad, C_e = A_e^T B_e in fp32 [E][P][Q], on the
+ * block-scaled MFMA, each operand a transposed MXFP8 copy in the K-tiled
+ * layout of moe_mx_out_t (col_blocked = 1) over the same groups:
+ *   a->data  [P][32 S] codes, a->scales [P][S] E8M0 (the col_q/col_s of an
+ *            [M_cap][P] tensor), S = 4 (ceil(M_cap/128) + E);
+ *   b->data  [Q][32 S], b->scales [Q][S] likewise;
+ *   dtype    MOE_DT_MXFP8 (e4m3 codes) or MOE_DT_MXFP8_E5M2, per operand;
+ *            layout ignored.
+ * The result is the exact product of the dequantised copies up to fp32
+ * accumulation: dW1 from the copies of xg and dgu, dW2 from those of y and
+ * dy2.  accumulate = 0 overwrites c (an empty group writes zeros); 1 adds.
+ * Requires P % 64 == 0, Q % 64 == 0; codes and c 16-byte aligned, scales
+ * 4-byte aligned. */
+moe_status_t moe_group_gemm_wgrad_mx(const moe_operand_t* a, const moe_operand_t* b, int P, int Q,
+                                     const moe_groups_t* groups, float* c, int accumulate,
+                                     int cu_margin, void* stream);
 
 /* Unfused GLU pass ([BLOG] "¿Dónde se va el cómputo en un bloque MoE?": the
  * activation as its own memory-bound pass between the GEMMs, the baseline the

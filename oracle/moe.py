@@ -560,23 +560,38 @@ def mx_quantize_rows(v_bits, fmt: str = "e4m3"):
     return q, s
 
 
-def mx_scale_col_offsets(counts) -> np.ndarray:
-    """Scale-column offset of each group: so_e = sum_{j<e} ceil(m_j / 32)."""
+def mx_scale_col_offsets(counts, blocked: bool = False) -> np.ndarray:
+    """Scale-column (slot) offset of each group: so_e = sum_{j<e} ceil(m_j / 32),
+    or in the K-tiled layout 4 sum_{j<e} ceil(m_j / 128)."""
     c = np.asarray(counts, dtype=np.int64)
-    blocks = (c + MX_BLOCK - 1) // MX_BLOCK
+    blocks = 4 * ((c + 127) // 128) if blocked else (c + MX_BLOCK - 1) // MX_BLOCK
     so = np.zeros(len(c) + 1, dtype=np.int64)
     so[1:] = np.cumsum(blocks)
     return so
 
 
-def mx_quantize_cols(v_bits, counts, m_cap: Optional[int] = None, fmt: str = "e4m3"):
+def mx_col_slots(m_cap: int, E: int, blocked: bool = False) -> int:
+    """Scale columns per row of a transposed copy: ceil(M_cap/32) + E, or
+    4 (ceil(M_cap/128) + E) in the K-tiled layout."""
+    return 4 * ((m_cap + 127) // 128 + E) if blocked else (m_cap + MX_BLOCK - 1) // MX_BLOCK + E
+
+
+def mx_quantize_cols(v_bits, counts, m_cap: Optional[int] = None, fmt: str = "e4m3",
+                     blocked: bool = False):
     """Column-wise (transposed) MXFP8 copy ([BLOG] "Fusionando cuantización
     MXFP8…": MXFP8 output plus a transposed version for back prop).
 
     Blocks are 32 consecutive rows of one column that restart at each group's
     first row; a group's last block may be partial and takes its amax over its
-    valid rows only.  Returns (col_q [C][M_cap] uint8, col_s [C][ceil(M_cap/32)+E]
-    uint8); positions no group writes stay 0 here (the GPU leaves them untouched).
+    valid rows only.  Returns (col_q, col_s).  Dense layout: col_q [C][M_cap]
+    (block codes at the block's rows), col_s [C][ceil(M_cap/32)+E]; positions no
+    group writes stay 0 here (the GPU leaves them untouched).  K-tiled layout
+    (``blocked``; the operand layout of the MXFP8 weight gradient): col_s
+    [C][S], S = 4 (ceil(M_cap/128) + E), col_q [C][32 S] with slot s = one
+    block (codes at bytes 32 s .. 32 s + 31); group e's blocks take slots
+    so_e + b, so_e = 4 sum_{j<e} ceil(m_j/128); the codes of rows past the
+    group in its last block are 0, and its slots up to so_e + 4 ceil(m_e/128)
+    that hold no row have zero codes and scale byte 127.
     """
     v = bf16_bits_to_f64(v_bits)
     R, C = v.shape
@@ -585,9 +600,9 @@ def mx_quantize_cols(v_bits, counts, m_cap: Optional[int] = None, fmt: str = "e4
     off = exclusive_offsets(counts)
     if m_cap is None:
         m_cap = R
-    so = mx_scale_col_offsets(counts)
-    ncols = (m_cap + MX_BLOCK - 1) // MX_BLOCK + E
-    col_q = np.zeros((C, m_cap), dtype=np.uint8)
+    so = mx_scale_col_offsets(counts, blocked)
+    ncols = mx_col_slots(m_cap, E, blocked)
+    col_q = np.zeros((C, 32 * ncols if blocked else m_cap), dtype=np.uint8)
     col_s = np.zeros((C, ncols), dtype=np.uint8)
     for e in range(E):
         a, b = int(off[e]), int(off[e + 1])
@@ -595,9 +610,59 @@ def mx_quantize_cols(v_bits, counts, m_cap: Optional[int] = None, fmt: str = "e4
             r1 = min(r0 + MX_BLOCK, b)
             for c in range(C):
                 codes, byte = mx_quantize_block(v[r0:r1, c], fmt)
-                col_q[c, r0:r1] = codes
+                if blocked:
+                    slot = int(so[e]) + blk
+                    col_q[c, 32 * slot:32 * slot + (r1 - r0)] = codes
+                else:
+                    col_q[c, r0:r1] = codes
                 col_s[c, so[e] + blk] = byte
+        if blocked:
+            for blk in range((b - a + MX_BLOCK - 1) // MX_BLOCK, int(so[e + 1] - so[e])):
+                col_s[:, so[e] + blk] = 127
     return col_q, col_s
+
+
+def mx_dequantize_cols(col_q, col_s, counts, m_cap: int, fmt: str = "e4m3",
+                       blocked: bool = False) -> np.ndarray:
+    """Values of a transposed MXFP8 copy (``mx_quantize_cols`` layouts), as
+    float64 [M][C] over the routed rows: row r of group e, column c is
+    decode(code) * 2^(scale - 127) of the block holding it."""
+    from .formats import e8m0_value, fp8_decode
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    so = mx_scale_col_offsets(counts, blocked)
+    C = col_q.shape[0]
+    M = int(off[-1])
+    out = np.zeros((M, C))
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        for blk, r0 in enumerate(range(a, b, MX_BLOCK)):
+            r1 = min(r0 + MX_BLOCK, b)
+            slot = int(so[e]) + blk
+            codes = (col_q[:, 32 * slot:32 * slot + (r1 - r0)] if blocked else col_q[:, r0:r1])
+            out[r0:r1] = (fp8_decode(codes, fmt) * e8m0_value(col_s[:, slot])[:, None]).T
+    return out
+
+
+def wgrad_mx(aq, as_, bq, bs, counts, m_cap: int, a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+             blocked: bool = True) -> np.ndarray:
+    """MXFP8 weight gradient: the K-grouped GroupGemm of ``wgrad`` on
+    transposed MXFP8 copies ("Boosting MoE Training Throughput with Advanced
+    Fusion Kernels", section "Fusionando cuantización MXFP8 y NVFP4": the
+    transposed copy exists for back prop), as the exact
+    dequantise-then-multiply definition: C_e = deq(A)_e^T deq(B)_e in float64
+    over the group's rows.  aq/as_ the copy of an [M_cap][P] tensor (codes,
+    scales), bq/bs of an [M_cap][Q] one.  Returns float64 [E][P][Q]."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = exclusive_offsets(counts)
+    A = mx_dequantize_cols(aq, as_, counts, m_cap, a_fmt, blocked)
+    B = mx_dequantize_cols(bq, bs, counts, m_cap, b_fmt, blocked)
+    out = np.zeros((len(counts), A.shape[1], B.shape[1]))
+    for e in range(len(counts)):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            out[e] = A[a:b].T @ B[a:b]
+    return out
 
 
 def mx_dequantize_rows(q, s, fmt: str = "e4m3"):

@@ -83,10 +83,11 @@ def assert_bf16_close(gpu_bits, ref_bits, rtol=2e-2, what="", normwise=None, ext
 
 # Element-wise allowance, as a multiple of sum_k |a_k b_k|, for the block-scaled
 # MFMA's accumulation, which is not strict fp32: twice the largest deviation
-# measured over every MXFP8-operand test beyond the output's own bf16 rounding
-# (2^-13.72 sum|ab|, FC1 with MXFP8 inputs, K = 256; mx_acc_excess prints it
-# per test).  A misplaced scale or K block errs by the order of sum|ab| itself.
-MX_ACC_REL = 1.5e-4
+# measured over every MXFP8-operand test beyond the output's own rounding
+# (2^-13.18 sum|ab|: the MXFP8 weight gradient over a 1000-row group; FC1 with
+# MXFP8 inputs reached 2^-13.72 at K = 256; each test prints its own).  A
+# misplaced scale or K block errs by the order of sum|ab| itself.
+MX_ACC_REL = 2.2e-4
 
 
 def mx_gemm_terms(aq, as_, counts, bq, bs, a_fmt="e4m3", gpu_aq=None, gpu_as=None):
@@ -300,12 +301,15 @@ def assert_mx_rows(gpu_q, gpu_s, gpu_vals, ref_vals, what="mx rows", fmt="e4m3")
     return st
 
 
-def assert_mx_cols(gpu_q, gpu_s, gpu_vals, ref_vals, counts, m_cap, what="mx cols", fmt="e4m3"):
+def assert_mx_cols(gpu_q, gpu_s, gpu_vals, ref_vals, counts, m_cap, what="mx cols", fmt="e4m3",
+                   blocked=False):
     """Transposed MXFP8 copy (32-row blocks restarting at each group) against
-    the oracle's quantisation of the oracle's values, as in assert_mx_rows."""
+    the oracle's quantisation of the oracle's values, as in assert_mx_rows.
+    ``blocked``: the K-tiled layout, whose zero codes past a group's rows and
+    padding slots (zero codes, scale byte 127) must match exactly."""
     from oracle import moe as O
-    rq, rs = O.mx_quantize_cols(ref_vals, counts, m_cap=m_cap, fmt=fmt)
-    so = O.mx_scale_col_offsets(counts)
+    rq, rs = O.mx_quantize_cols(ref_vals, counts, m_cap=m_cap, fmt=fmt, blocked=blocked)
+    so = O.mx_scale_col_offsets(counts, blocked)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     C = ref_vals.shape[1]
     tot = np.zeros(3, dtype=np.int64)
@@ -321,8 +325,17 @@ def assert_mx_cols(gpu_q, gpu_s, gpu_vals, ref_vals, counts, m_cap, what="mx col
             t = np.concatenate([v, np.zeros((pad, C), v.dtype)]) if pad else v
             return t.T.reshape(C, nb, 32)
 
-        gq = np.concatenate([gpu_q[:, a:b], np.zeros((C, pad), np.uint8)], axis=1).reshape(C, nb, 32)
-        rqe = np.concatenate([rq[:, a:b], np.zeros((C, pad), np.uint8)], axis=1).reshape(C, nb, 32)
+        if blocked:
+            s0 = int(so[e])
+            gq = gpu_q[:, 32 * s0:32 * (s0 + nb)].reshape(C, nb, 32)
+            rqe = rq[:, 32 * s0:32 * (s0 + nb)].reshape(C, nb, 32)
+            assert np.all(gq[:, -1, 32 - pad:] == 0) if pad else True, f"{what} group {e}: codes past the rows"
+            s1 = int(so[e + 1])
+            assert np.array_equal(gpu_s[:, s0 + nb:s1], rs[:, s0 + nb:s1]), f"{what} group {e}: padding scales"
+            assert np.all(gpu_q[:, 32 * (s0 + nb):32 * s1] == 0), f"{what} group {e}: padding codes"
+        else:
+            gq = np.concatenate([gpu_q[:, a:b], np.zeros((C, pad), np.uint8)], axis=1).reshape(C, nb, 32)
+            rqe = np.concatenate([rq[:, a:b], np.zeros((C, pad), np.uint8)], axis=1).reshape(C, nb, 32)
         tot += _mx_block_check(gq, gpu_s[:, so[e]:so[e] + nb], blocks(gpu_vals[a:b]),
                                rqe, rs[:, so[e]:so[e] + nb], blocks(ref_vals[a:b]), f"{what} group {e}",
                                fmt)

@@ -135,3 +135,19 @@ def test_normwise_bound_is_enforced():
     gvals = F.bf16_bits_to_f64(r) * (1 + 1e-2)
     with pytest.raises(AssertionError, match="normwise"):
         assert_bf16_close(F.f64_to_bf16_bits(gvals), r, normwise=4e-3)
+
+
+def test_blocked_column_copies_check_and_padding():
+    counts = [40, 0, 23]
+    v = _rows(9, R=63, C=4)
+    q, s = O.mx_quantize_cols(v, counts, m_cap=70, blocked=True)
+    n, exact, ex = assert_mx_cols(q, s, v, v, counts, 70, "cols blocked", blocked=True)
+    assert (n, exact, ex) == (4 * (2 + 1), 12, 0)
+    q2 = q.copy()
+    q2[0, 32 * 3 + 5] = 1                   # group 0's padding slot 3
+    with pytest.raises(AssertionError, match="padding codes"):
+        assert_mx_cols(q2, s, v, v, counts, 70, "planted padding", blocked=True)
+    q3 = q.copy()
+    q3[1, 32 * 1 + 8 + 3] = 2               # group 0 block 1 holds rows 32..39: byte 11 is past them
+    with pytest.raises(AssertionError, match="past the rows"):
+        assert_mx_cols(q3, s, v, v, counts, 70, "planted tail", blocked=True)

@@ -829,3 +829,95 @@ def test_non_gated_forward_and_backward(act):
             assert abs(dz[r, j] - fd) <= 2.0 ** -8 * abs(fd) + 1e-6, (r, j, dz[r, j], fd)
             checked += 1
     assert checked >= 20
+
+
+# ------------------------------------------------------------------ K-tiled copies, MXFP8 wgrad
+def test_mx_cols_blocked_layout_matches_dense_blocks():
+    """The K-tiled transposed copy holds the dense copy's blocks, each group
+    from slot 4 sum_{j<e} ceil(m_j/128), one 32-byte slot per block, the codes
+    of rows past a group zero, and its unused slots up to the next multiple of
+    4 with zero codes and scale byte 127."""
+    rng = np.random.default_rng(61)
+    counts = [40, 0, 129, 5, 128]
+    m_cap = 310
+    v = W.to_bf16_bits((rng.standard_normal((m_cap, 6)) * 3).astype(np.float32))
+    qd, sd = O.mx_quantize_cols(v, counts, m_cap=m_cap)
+    qb, sb = O.mx_quantize_cols(v, counts, m_cap=m_cap, blocked=True)
+    S = O.mx_col_slots(m_cap, len(counts), blocked=True)
+    assert S == 4 * ((m_cap + 127) // 128 + len(counts)) and qb.shape == (6, 32 * S) and sb.shape == (6, S)
+    so_d, so_b = O.mx_scale_col_offsets(counts), O.mx_scale_col_offsets(counts, blocked=True)
+    assert so_b.tolist() == [0, 4, 4, 12, 16, 20]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    for e, m in enumerate(counts):
+        nb = (m + 31) // 32
+        for b in range(nb):
+            n = min(32, m - 32 * b)
+            sl = so_b[e] + b
+            assert np.array_equal(sb[:, sl], sd[:, so_d[e] + b])
+            assert np.array_equal(qb[:, 32 * sl:32 * sl + n], qd[:, off[e] + 32 * b:off[e] + 32 * b + n])
+            assert np.all(qb[:, 32 * sl + n:32 * sl + 32] == 0)
+        for b in range(nb, so_b[e + 1] - so_b[e]):
+            sl = so_b[e] + b
+            assert np.all(sb[:, sl] == 127) and np.all(qb[:, 32 * sl:32 * sl + 32] == 0)
+
+
+@pytest.mark.parametrize("blocked", [False, True])
+def test_mx_dequantize_cols_round_trip_bound(blocked):
+    rng = np.random.default_rng(62)
+    counts = [70, 33, 0, 1]
+    M = sum(counts)
+    v = W.to_bf16_bits((rng.standard_normal((M, 5)) * 2.0 ** rng.integers(-8, 8, (M, 1))).astype(np.float32))
+    q, s = O.mx_quantize_cols(v, counts, m_cap=M, blocked=blocked)
+    d = O.mx_dequantize_cols(q, s, counts, M, blocked=blocked)
+    x = F.bf16_bits_to_f64(v)
+    so = O.mx_scale_col_offsets(counts, blocked)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    for e in range(len(counts)):
+        for r in range(off[e], off[e + 1]):
+            X = F.e8m0_value(s[:, so[e] + (r - off[e]) // 32])
+            assert np.all(np.abs(d[r] - x[r]) <= 0.5 * F.e4m3_ulp(np.abs(x[r]) / X) * X)
+
+
+def test_wgrad_mx_exact_on_exactly_quantisable_inputs():
+    """Small integers (|v| <= 7) are exact in e4m3 and e5m2 whatever the block
+    scale the rule picks, so the MXFP8 weight gradient on their copies equals
+    wgrad of the bf16 values exactly, for both layouts and both formats."""
+    rng = np.random.default_rng(63)
+    counts = [130, 0, 31, 64, 1]
+    M, P, Q = sum(counts), 6, 5
+    a = W.to_bf16_bits(rng.integers(-7, 8, (M, P)).astype(np.float32))
+    b = W.to_bf16_bits(rng.integers(-7, 8, (M, Q)).astype(np.float32))
+    ref = O.wgrad(a, counts, b)
+    for blocked in (False, True):
+        for fa, fb in (("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")):
+            aq, as_ = O.mx_quantize_cols(a, counts, m_cap=M, fmt=fa, blocked=blocked)
+            bq, bs = O.mx_quantize_cols(b, counts, m_cap=M, fmt=fb, blocked=blocked)
+            got = O.wgrad_mx(aq, as_, bq, bs, counts, M, fa, fb, blocked=blocked)
+            assert np.array_equal(got, ref), (blocked, fa, fb)
+
+
+def test_wgrad_mx_against_loop_over_codes():
+    """Gaussian values: each product term decoded from its own code and scale
+    byte in a Python loop (slot arithmetic written out for the K-tiled
+    layout)."""
+    rng = np.random.default_rng(64)
+    counts = [37, 0, 70]
+    M, P, Q = sum(counts), 3, 4
+    a = W.to_bf16_bits(rng.standard_normal((M, P)).astype(np.float32))
+    b = W.to_bf16_bits((rng.standard_normal((M, Q)) * 1e-3).astype(np.float32))
+    aq, as_ = O.mx_quantize_cols(a, counts, m_cap=M, blocked=True)
+    bq, bs = O.mx_quantize_cols(b, counts, m_cap=M, fmt="e5m2", blocked=True)
+    got = O.wgrad_mx(aq, as_, bq, bs, counts, M, "e4m3", "e5m2")
+    starts = [0, 37, 37]
+    slot0 = [0, 4, 4]
+    for e in range(3):
+        for p in range(P):
+            for q in range(Q):
+                s = 0.0
+                for k in range(counts[e]):
+                    sl = slot0[e] + k // 32
+                    xa = F.e4m3_decode(aq[p, 32 * sl + k % 32]) * 2.0 ** (int(as_[p, sl]) - 127)
+                    xb = F.e5m2_decode(bq[q, 32 * sl + k % 32]) * 2.0 ** (int(bs[q, sl]) - 127)
+                    s += xa * xb
+                assert got[e, p, q] == pytest.approx(s, rel=1e-12, abs=1e-300)
+    assert np.all(got[1] == 0)
