@@ -578,13 +578,29 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     const uint32_t kn_voff =
         (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
 
+    // bf16 on 8 waves (FC1 and the plain GroupGemm): the main loop runs on
+    // v_mfma_f32_16x16x32_bf16 (its accumulators are moved into the 32 x 32
+    // layout below for the epilogues); everything else on
+    // v_mfma_f32_32x32x16_bf16 or the block-scaled 32 x 32 x 64 form (the
+    // dGLU epilogue's preact registers leave no room for the 16 x 16 form's
+    // extra fragments).
+    constexpr bool M16 = NW == 8 && !MXT && !WG && EPI != EPI_DGLU;
+    constexpr int MB = 2 * MI;                  // 16-row blocks per wave
     f32x16 acc[MI][4];
+    f32x4 acc16[M16 ? MB : 1][8];
+    if constexpr (M16) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j) acc16[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    }
 
     // direct global -> LDS of one ROWS x 64 operand tile (swizzled layout).
     // Instruction j of wave w fills rows 8 (NJ w + j) .. + 7 (NJ = ROWS / 8 NW);
@@ -840,6 +856,89 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // LDS access names its array directly.  With an odd tile count the last
     // K-tile (in lds0) runs after the loop, with no DMA (the loop's last
     // prefetch into lds1 reads zeros and is drained before the epilogue).
+    if constexpr (M16) {
+    // 16x16x32 main loop: a K-tile is 2 k-steps of 32; A fragments double
+    // buffered, B fragments single and reloaded right after their last use
+    bf16x8 aF[2][MB], bB[8];
+    const int ch_l = lane_t >> 4;
+    const int ra16 = wm * HR + (lane_t & 15), rb16 = wn * 128 + (lane_t & 15);
+    auto rdA = [&](const uint8_t* sa, int ks, int i) {
+      return *reinterpret_cast<const bf16x8*>(sa + swz_off(ra16 + 16 * i, 4 * ks + ch_l));
+    };
+    auto rdB = [&](const uint8_t* sa, int ks, int j) {
+      return *reinterpret_cast<const bf16x8*>(sa + GM_TILE_BYTES + swz_off(rb16 + 16 * j, 4 * ks + ch_l));
+    };
+    constexpr int NJA = TBM / (8 * NW);           // == MB
+    constexpr int NJB = 32 / NW;                  // 4
+    static_assert(NJA == MB, "A DMA pieces");
+    auto dmaA = [&](int kt, uint8_t* st, int j) {
+      const bool in = kt < nk_t;
+      const uint32_t vrow = (uint32_t)(wave * 8 * NJA + rl_t) * a_stride;
+      const int c = pc_t ^ (rl_t ^ ((wave * NJA + j) & 3));
+      lds_dma16(in ? rsA : rsZ, st + (wave * NJA + j) * 1024,
+                vrow + (uint32_t)(j * 8) * a_stride + (uint32_t)(c << 4), (uint32_t)kt * 128u);
+    };
+    auto dmaB = [&](int kt, uint8_t* st, int j) {
+      const bool in = kt < nk_t;
+      const int blk = wave * NJB + j;
+      lds_dma16(in ? rsB : rsZ, st + GM_TILE_BYTES + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16),
+                (uint32_t)kt * GM_TILE_BYTES);
+    };
+    // one k-step, j (B block) outer: B fragment j is dead after its MB MFMAs
+    // and is reloaded for the next k-step right away, so every reload has
+    // most of the k-step to land; the next A fragments (MB of them, double
+    // buffered) are read during the first MB blocks; the next stage's DMA
+    // (when DMA) goes out one instruction per block.
+    auto kstep = [&](auto curc, auto dmac, const uint8_t* nsa, int nks, int dkt, uint8_t* dst) {
+      constexpr int cur = decltype(curc)::value;
+      constexpr bool DMA = decltype(dmac)::value;
+      static_for<8>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j < MB) aF[cur ^ 1][j] = rdA(nsa, nks, j);
+        if constexpr (DMA) {
+          if constexpr (j < NJA) dmaA(dkt, dst, j);
+          else if constexpr (j - NJA < NJB) dmaB(dkt, dst, j - NJA);
+        }
+        static_for<MB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bB[j], aF[cur][i], acc16[i][j], 0, 0, 0);
+        });
+        bB[j] = rdB(nsa, nks, j);
+        if constexpr (j < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // A read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (DMA && j < NJA + NJB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MB - 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // B reload
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using NoD = std::false_type;
+    using D = std::true_type;
+    issue_direct(0, lds0);
+    stage_barrier();
+    issue_direct(1, lds1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aF[0][i] = rdA(lds0, 0, i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bB[j] = rdB(lds0, 0, j);
+    const int nk_even16 = nk_t & ~1;
+    for (int kt = 0; kt < nk_even16; kt += 2) {
+      kstep(I0{}, NoD{}, lds0, 1, 0, nullptr);
+      stage_barrier();
+      kstep(I1{}, D{}, lds1, 0, kt + 2, lds0);
+      kstep(I0{}, NoD{}, lds1, 1, 0, nullptr);
+      stage_barrier();
+      kstep(I1{}, D{}, lds0, 0, kt + 3, lds1);
+    }
+    if (nk_t & 1) {
+      kstep(I0{}, NoD{}, lds0, 1, 0, nullptr);
+      kstep(I1{}, NoD{}, lds0, 0, 0, nullptr);
+    }
+    } else {
     issue_direct(0, lds0);
     if (KNR) {
       kn_load(0);
@@ -871,9 +970,35 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       first_steps(lds0, 0);
       mfma_step(1, 0, KSTEPS - 1);
     }
+    }   // not M16
     // the loop leaves one DMA (a K-tile past the end: zeros) and one set of
     // fragment reads in flight; the epilogue reuses both stage arrays
     stage_barrier();
+    if constexpr (M16) {
+      // 16 x 16 block (2i + a, 2j + b) gives lane l rows 16a + l % 16 and
+      // columns 16b + 4 (l / 16) + 0..3; the 32 x 32 block (i, j) wants lane L
+      // to hold row L % 32 and columns 8q + 4 (L / 32) + 0..3.  In 16-lane rows
+      // R: q = 2b takes [X0.R0, X1.R0, X0.R1, X1.R1] and q = 2b + 1 takes
+      // [X0.R2, X1.R2, X0.R3, X1.R3] of the pair X_a = block (2i + a, 2j + b):
+      // one v_permlane16_swap (odd rows of the first operand with even rows
+      // of the second) and one v_permlane32_swap (upper half of the first with
+      // lower half of the second) per register pair.
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc16[2 * i][2 * j + b][r]),
+                                                                __float_as_uint(acc16[2 * i + 1][2 * j + b][r]),
+                                                                false, false);
+              const auto s32 = __builtin_amdgcn_permlane32_swap(s16[0], s16[1], false, false);
+              acc[i][j][8 * b + r] = __uint_as_float(s32[0]);
+              acc[i][j][8 * b + 4 + r] = __uint_as_float(s32[1]);
+            }
+    }
 
     // ================================================================ epilogues
     // The MFMAs compute D = W X^T per 32 x 32 block, so accumulator element r
