@@ -554,6 +554,31 @@ def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I
 
     fc1_mxin_ms = time_kernel(fc1_mxin)
     del xq, xs, w1q, w1s
+    # MXFP8 weight gradient dW1 = Xg^T dgu from K-tiled transposed copies
+    # (e4m3 for Xg, e5m2 for the gradient; the FC1 pre-activation of this run
+    # stands in for dgu, which has its shape), fp32 out; the two column
+    # quantisations that write the copies are timed with it
+    S = G.mx_col_slots(M, E, blocked=True)
+    xcq = torch.empty((H, 32 * S), dtype=torch.uint8, device=dev)
+    xcs = torch.empty((H, S), dtype=torch.uint8, device=dev)
+    gcq = torch.empty((2 * I, 32 * S), dtype=torch.uint8, device=dev)
+    gcs = torch.empty((2 * I, S), dtype=torch.uint8, device=dev)
+    dw1 = torch.empty((E, H, 2 * I), dtype=torch.float32, device=dev)
+    op_xc = G.operand(xcq, dtype=G.DT_MXFP8, scales=xcs)
+    op_gc = G.operand(gcq, dtype=G.DT_MXFP8_E5M2, scales=gcs)
+
+    def quant_cols():
+        G.moe_mxfp8_quantize(x, M, H, grp, G.mx_out(col_q=xcq, col_s=xcs, col_blocked=True))
+        G.moe_mxfp8_quantize(pre, M, 2 * I, grp, G.mx_out(col_q=gcq, col_s=gcs, e5m2=True,
+                                                          col_blocked=True))
+
+    def wgrad_mx():
+        G.moe_group_gemm_wgrad_mx(op_xc, op_gc, H, 2 * I, grp, dw1)
+
+    quant_cols()
+    qcols_ms = time_kernel(quant_cols)
+    wgrad_mx_ms = time_kernel(wgrad_mx)
+    del xcq, xcs, gcq, gcs, dw1
     fc2_flops = 2.0 * M * I * H
     fc1_flops = 2.0 * M * H * 2 * I
     del x, w1t, z, w2q, w2s
@@ -566,6 +591,11 @@ def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I
             "fc1_mxfp8_inputs_ms": round(fc1_mxin_ms, 4),
             "fc1_mxfp8_inputs_tflops": round(fc1_flops / fc1_mxin_ms / 1e9, 1),
             "fc1_mxfp8_inputs_frac_fp8_peak": round(fc1_flops / fc1_mxin_ms / 1e9 / 5000.0, 4),
+            "dw1_mxfp8_ms": round(wgrad_mx_ms, 4),
+            "dw1_mxfp8_tflops": round(fc1_flops / wgrad_mx_ms / 1e9, 1),
+            "dw1_mxfp8_frac_fp8_peak": round(fc1_flops / wgrad_mx_ms / 1e9 / 5000.0, 4),
+            "dw1_mxfp8_hbm_bound_ms": round(E * H * 2 * I * 4 / PEAK_HBM_GBS / 1e6, 4),
+            "k_tiled_copies_x_and_dgu_ms": round(qcols_ms, 4),
             "activations": "student-t(3) x 0.5, bf16"}
 
 
