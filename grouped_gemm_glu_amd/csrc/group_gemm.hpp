@@ -93,11 +93,13 @@ enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2, AT_MX_B5 = 3, AT_MX_AB5 = 4 };
 // Waves per workgroup.  4: a 2 x 2 grid of waves, one per SIMD, each owning
 // a 128 x 128 sub-tile.  8: a 4 x 2 grid of 64 x 128 sub-tiles, two waves per
 // SIMD, so that one wave's MFMAs run while the other waits on its loads or at
-// the stage barrier (the bf16 kernels on packed weights: 3-4% faster on
-// the DeepSeek-V3-like share, same results bit for bit).
+// the stage barrier (the kernels on packed weights with bf16 or MXFP8 e4m3 /
+// e5m2-A operands: 3-5% faster on the DeepSeek-V3-like share, same results
+// bit for bit).
 constexpr int gm_waves(int epi, int blay, int at) {
-  return (at == AT_BF16 && blay == BL_PACKED &&
-          (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU))
+  return (blay == BL_PACKED &&
+          ((at == AT_BF16 && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU)) ||
+           ((at == AT_MX || at == AT_MX_A5) && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE))))
              ? 8
              : 4;
 }
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   constexpr bool KNR = BLAY == BL_KN && !WG;
   constexpr int NW = gm_waves(EPI, BLAY, AT);   // waves per workgroup (4 or 8)
   constexpr int NTH = 64 * NW;           // threads
-  static_assert(NW == 4 || (!WG && !MXT && !KNR), "8 waves: bf16 operands, packed B");
+  static_assert(NW == 4 || (!WG && !KNR), "8 waves: packed B");
   // Two distinct stage arrays: the compiler can then see that the LDS-DMA
   // writes of the next stage never alias the fragment reads of the current
   // one, and does not wait for the prefetch before computing.
@@ -431,11 +433,12 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // tile; whether it is also scheduled apart, among the half tiles that take
   // the first ids, is per kernel.  The dGLU kernel (N = I: few tile rounds
   // per CU) keeps that, since a workgroup's share is then at most one half
-  // tile plus full ones.  FC1, FC2 and dX on 8 waves (many rounds) schedule
-  // it in its expert's 4 x 8 block instead, where it shares the B panels of
-  // the expert's other m-tiles in L2: measured 2-3% faster on the
-  // DeepSeek-V3-like share, neutral on the GPT-OSS-like FC1.
-  constexpr bool HALF_FIRST = !WG && !(NW == 8 && !MXT && EPI != EPI_DGLU);
+  // tile plus full ones.  The other 8-wave kernels (FC1, FC2 and dX, bf16
+  // or MXFP8; many rounds) schedule it in its expert's 4 x 8 block instead,
+  // where it shares the B panels of the expert's other m-tiles in L2:
+  // measured 2-9% faster on the DeepSeek-V3-like share, neutral on the
+  // GPT-OSS-like FC1.
+  constexpr bool HALF_FIRST = !WG && !(NW == 8 && EPI != EPI_DGLU);
   build_group_scan<NTH>(gs, p.counts, p.E, p.M_cap, WGM ? 128 : GM_BM, HALF_FIRST ? GM_BM / 2 : 0,
                           p.offsets_out, p.status_out, blockIdx.x == 0, p.col_blocked != 0);
   if (WG) {
@@ -594,6 +597,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // dGLU epilogue's preact registers leave no room for the 16 x 16 form's
     // extra fragments).
     constexpr bool M16 = NW == 8 && !MXT && !WG && EPI != EPI_DGLU;
+    constexpr bool MX8 = NW == 8 && MXT && !WG;
     constexpr int MB = 2 * MI;                  // 16-row blocks per wave
     f32x16 acc[MI][4];
     f32x4 acc16[M16 ? MB : 1][8];
@@ -676,7 +680,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
                    b_stride, kk * 128u);
       if (BLAY == BL_PACKED)
         issue_block(in ? rsB : rsZ, sa + GM_TILE_BYTES, (uint32_t)kt * GM_TILE_BYTES);
-      if (MXT) {   // 4 scale bytes per row: one dword per lane, 64 rows per wave
+      if (MXT && NW == 4) {   // 4 scale bytes per row: one dword per lane, 64 rows per wave
         const uint32_t r = (uint32_t)(wave * 64 + lane_t);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             in ? rsSA : rsZ, (__attribute__((address_space(3))) void*)(sa + 2 * GM_TILE_BYTES + wave * 256),
@@ -685,6 +689,14 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
             in ? rsSB : rsZ,
             (__attribute__((address_space(3))) void*)(sa + 2 * GM_TILE_BYTES + 1024 + wave * 256), 4,
             WGM ? r * sb_stride : r * 4u, WGM ? kk * 4u : kk * 1024u, 0, 0);
+      }
+      if (MXT && NW == 8) {   // waves 0-3: A's scales, waves 4-7: B's (64 rows per wave)
+        const bool ah = wave < 4;
+        const uint32_t r = (uint32_t)((wave & 3) * 64 + lane_t);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            in ? (ah ? rsSA : rsSB) : rsZ,
+            (__attribute__((address_space(3))) void*)(sa + 2 * GM_TILE_BYTES + (ah ? 0 : 1024) + (wave & 3) * 256),
+            4, r * (ah ? sa_stride : 4u), kk * (ah ? 4u : 1024u), 0, 0);
       }
     };
     u32x4 rb[8];
@@ -947,6 +959,132 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       kstep(I0{}, NoD{}, lds0, 1, 0, nullptr);
       kstep(I1{}, NoD{}, lds0, 0, 0, nullptr);
     }
+    } else if constexpr (MX8) {
+    // MXFP8 operands on 8 waves: the same order on the block-scaled
+    // v_mfma_scale_f32_32x32x64_f8f6f4.  A K-tile is 2 k-steps of 64 codes;
+    // per k-step, B block j (outer) feeds its MI MFMAs and is re-read for the
+    // next k-step at once (B single-buffered, A double-buffered), and a new
+    // K-tile's scale dwords are read with its first fragments (two scale
+    // sets, one per stage array).  Lane half h takes bytes 16h .. 16h + 15 of
+    // each of the k-step's two 32-code blocks (chunks 4 ks + h, 4 ks + 2 + h);
+    // the upper half's scale dword is shifted down one byte so that both
+    // halves select byte 2 ks (block 2 ks + h).
+    i32x8 aX[2][MI], bX[4];
+    uint32_t sAx[2][MI], sBx[2][4];
+    const int hx = lane_t >> 5;
+    const int rax = wm * HR + (lane_t & 31), rbx = wn * 128 + (lane_t & 31);
+    const uint32_t shx = 8u * (uint32_t)(lane >> 5);
+    auto rd32x = [&](const uint8_t* t, int r, int ks) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(t + swz_off(r, 4 * ks + hx));
+      const uint4 hi = *reinterpret_cast<const uint4*>(t + swz_off(r, 4 * ks + 2 + hx));
+      i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      return v;
+    };
+    auto rdSAx = [&](const uint8_t* sa, int i) {
+      return reinterpret_cast<const uint32_t*>(sa + 2 * GM_TILE_BYTES)[rax + 32 * i];
+    };
+    auto rdSBx = [&](const uint8_t* sa, int j) {
+      return reinterpret_cast<const uint32_t*>(sa + 2 * GM_TILE_BYTES + 1024)[rbx + 32 * j];
+    };
+    constexpr int NJA = TBM / (8 * NW);           // A DMA pieces per K-tile (2 or 4)
+    auto dmaA = [&](int kt, uint8_t* st, int j) {
+      const bool in = kt < nk_t;
+      const uint32_t vrow = (uint32_t)(wave * 8 * NJA + rl_t) * a_stride;
+      const int c = pc_t ^ (rl_t ^ ((wave * NJA + j) & 3));
+      lds_dma16(in ? rsA : rsZ, st + (wave * NJA + j) * 1024,
+                vrow + (uint32_t)(j * 8) * a_stride + (uint32_t)(c << 4), (uint32_t)kt * 128u);
+    };
+    auto dmaB = [&](int kt, uint8_t* st, int j) {
+      const bool in = kt < nk_t;
+      const int blk = wave * 4 + j;
+      lds_dma16(in ? rsB : rsZ, st + GM_TILE_BYTES + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16),
+                (uint32_t)kt * GM_TILE_BYTES);
+    };
+    // (one instruction whose operands are selected per wave half: a branch
+    // here would let the compiler sink the k-step's MFMAs past it)
+    const bool sA_half = wave < 4;
+    const rsrc_t rsS = sA_half ? rsSA : rsSB;
+    const uint32_t s_voff = (uint32_t)((wave & 3) * 64 + lane_t) * (sA_half ? sa_stride : 4u);
+    const uint32_t s_kmul = sA_half ? 4u : 1024u;
+    const int s_lds = 2 * GM_TILE_BYTES + (sA_half ? 0 : 1024) + (wave & 3) * 256;
+    auto dmaS = [&](int kt, uint8_t* st) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          kt < nk_t ? rsS : rsZ, (__attribute__((address_space(3))) void*)(st + s_lds), 4, s_voff,
+          (uint32_t)kt * s_kmul, 0, 0);
+    };
+    // one k-step on A buffer CUR, scale set SET, k-step KS of its K-tile;
+    // the next k-step's fragments come from (nsa, NKS), with its K-tile's
+    // scales into set NSET when NEWT; DMA: K-tile dkt into dst, pieces
+    // spread over the blocks (A pieces, B pieces, then the scale dword)
+    auto kstepx = [&](auto curc, auto setc, auto ksc, auto dmac, auto nksc, auto nsetc, auto newtc,
+                      const uint8_t* nsa, int dkt, uint8_t* dst) {
+      constexpr int cur = decltype(curc)::value, set = decltype(setc)::value;
+      constexpr int ks = decltype(ksc)::value, nks = decltype(nksc)::value;
+      constexpr int nset = decltype(nsetc)::value;
+      constexpr bool DMA = decltype(dmac)::value, NEWT = decltype(newtc)::value;
+      static_for<4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j < MI) {
+          aX[cur ^ 1][j] = rd32x(nsa, rax + 32 * j, nks);
+          if constexpr (NEWT) sAx[nset][j] = rdSAx(nsa, j);
+        }
+        if constexpr (DMA) {
+          // 2 or 4 A pieces, 4 B pieces and one scale dword over 4 blocks
+          if constexpr (NJA == 4) { dmaA(dkt, dst, j); dmaB(dkt, dst, j); }
+          else {
+            if constexpr (j < 2) dmaA(dkt, dst, j);
+            dmaB(dkt, dst, j);
+          }
+          if constexpr (j == 3) dmaS(dkt, dst);
+        }
+        static_for<MI>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const int sb = (int)(sBx[set][j] >> shx), sa_ = (int)(sAx[set][i] >> shx);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bX[j], aX[cur][i], acc[i][j], FMT_B, FMT_A, 2 * ks, sb, 2 * ks, sa_);
+        });
+        bX[j] = rd32x(nsa + GM_TILE_BYTES, rbx + 32 * j, nks);
+        if constexpr (NEWT) sBx[nset][j] = rdSBx(nsa, j);
+        if constexpr (j < MI) __builtin_amdgcn_sched_group_barrier(0x100, NEWT ? 3 : 2, 0);   // A reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (DMA) __builtin_amdgcn_sched_group_barrier(0x020, (NJA == 4 || j < 2 ? 2 : 1) + (j == 3 ? 1 : 0), 0);
+        if constexpr (MI > 1) __builtin_amdgcn_sched_group_barrier(0x008, MI - 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NEWT ? 3 : 2, 0);                        // B reload
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using NoDx = std::false_type;
+    using Dx = std::true_type;
+    issue_direct(0, lds0);
+    stage_barrier();
+    issue_direct(1, lds1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      aX[0][i] = rd32x(lds0, rax + 32 * i, 0);
+      sAx[0][i] = rdSAx(lds0, i);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bX[j] = rd32x(lds0 + GM_TILE_BYTES, rbx + 32 * j, 0);
+      sBx[0][j] = rdSBx(lds0, j);
+    }
+    const int nk_evenx = nk_t & ~1;
+    for (int kt = 0; kt < nk_evenx; kt += 2) {
+      kstepx(C0{}, C0{}, C0{}, NoDx{}, C1{}, C0{}, std::false_type{}, lds0, 0, nullptr);
+      stage_barrier();
+      kstepx(C1{}, C0{}, C1{}, Dx{}, C0{}, C1{}, std::true_type{}, lds1, kt + 2, lds0);
+      kstepx(C0{}, C1{}, C0{}, NoDx{}, C1{}, C1{}, std::false_type{}, lds1, 0, nullptr);
+      stage_barrier();
+      kstepx(C1{}, C1{}, C1{}, Dx{}, C0{}, C0{}, std::true_type{}, lds0, kt + 3, lds1);
+    }
+    if (nk_t & 1) {
+      kstepx(C0{}, C0{}, C0{}, NoDx{}, C1{}, C0{}, std::false_type{}, lds0, 0, nullptr);
+      kstepx(C1{}, C0{}, C1{}, NoDx{}, C0{}, C1{}, std::false_type{}, lds0, 0, nullptr);
+    }
     } else {
     issue_direct(0, lds0);
     if (KNR) {
@@ -979,7 +1117,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       first_steps(lds0, 0);
       mfma_step(1, 0, KSTEPS - 1);
     }
-    }   // not M16
+    }   // neither M16 nor MX8
     // the loop leaves one DMA (a K-tile past the end: zeros) and one set of
     // fragment reads in flight; the epilogue reuses both stage arrays
     stage_barrier();
