@@ -207,6 +207,38 @@ def test_dsv3_dbias_is_column_sums_of_dgu(dsv3_run):
         assert np.all(np.abs(dsv3_run["db"][e] - blk.sum(axis=0)) <= bound), f"expert {e}"
 
 
+def test_dsv3_dbias_sampled_columns_oracle(dsv3_run):
+    """d(bias) at full size against the oracle on sampled (expert, column)
+    pairs: for the largest, a middle and the smallest non-empty expert and 4
+    columns each, the oracle computes that expert's pre-activation and dgu at
+    those columns for ALL its rows (each dgu column depends only on its own
+    G column and pre-activation pair) and sums them as bias_grad does.  The
+    GPU sums its own bf16 dgu values, each within one bf16 ulp of the
+    oracle's (2^-7 of |ref|), in fp32: bound 2^-7 sum|ref| + m_e 2^-24 sum|ref|."""
+    d = dsv3_run["d"]
+    counts, I = d["counts"], d["I"]
+    order = [int(e) for e in np.argsort(counts) if counts[e] > 0]
+    experts = sorted({order[-1], order[len(order) // 2], order[0]})
+    off = np.concatenate([[0], np.cumsum(counts)])
+    g = np.random.default_rng(7)
+    ep = O.Epilogue()
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        cols = np.unique(np.concatenate([[0, I - 1], g.integers(0, I, 2)]))
+        w1_sub = d["w1"][e][:, np.concatenate([cols, I + cols])][None]        # [1][H][2S]
+        w2_sub = d["w2"][e][cols][None]                                       # [1][S][H]
+        pre_s, _ = O.fc1_glu(d["x"][r0:r1], [r1 - r0], w1_sub, ep)
+        dgu_s = O.dgrad_dglu(dsv3_run["dy2"][r0:r1], [r1 - r0], w2_sub, pre_s, ep)
+        want = O.bias_grad(dgu_s, [r1 - r0])[0]                               # [2S]
+        absum = np.abs(F.bf16_bits_to_f64(dgu_s)).sum(axis=0)
+        got = np.concatenate([dsv3_run["db"][e][cols], dsv3_run["db"][e][I + cols]])
+        bound = (2.0 ** -7 + (r1 - r0) * 2.0 ** -24) * absum + 1e-30
+        err = np.abs(got - want)
+        assert np.all(err <= bound), (e, cols, err, bound)
+        print(f"[dbias] expert {e} ({r1 - r0} rows), columns {cols.tolist()}: "
+              f"max |err| / sum|ref| = {float(np.max(err / np.maximum(absum, 1e-30))):.3g}")
+
+
 def test_dsv3_drow_scale_sampled_rows(dsv3_run):
     """d(row_scale) on sampled rows against the oracle's (its own G and its own
     pre-activation), within fp32 accumulation plus the bf16 rounding flips of
