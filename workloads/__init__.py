@@ -189,7 +189,7 @@ def gptoss_logits() -> np.ndarray:
     return logits + bias[None, :]
 
 
-def gptoss(with_weights: bool = True) -> dict:
+def gptoss(with_weights: bool = True, with_w2: bool = False) -> dict:
     c = GPTOSS
     seed, T, E, H, I = c["seed"], c["T"], c["E"], c["H"], c["I"]
     d = dict(name="gptoss", T=T, E=E, k=c["k"], H=H, I=I, alpha=c["alpha"], limit=c["limit"],
@@ -197,6 +197,8 @@ def gptoss(with_weights: bool = True) -> dict:
     if with_weights:
         d["w1"] = per_expert_normal_bf16(seed, "w1", E, (H, 2 * I), 0.02)
         d["b1"] = normal_bf16(seed, "b1", 0, (E, 2 * I), 0.01)
+    if with_w2:   # the optional FC2: W2 [E][I][H] bf16 ~N(0, 0.02)
+        d["w2"] = per_expert_normal_bf16(seed, "w2", E, (I, H), 0.02)
     return d
 
 
