@@ -256,6 +256,12 @@ def main():
         dcq = torch.empty((2 * I, M), dtype=torch.uint8, device=dev)
         dcs = torch.empty((2 * I, (M + 31) // 32 + E), dtype=torch.uint8, device=dev)
         mx_dgu = G.mx_out(row_q=dq, row_s=ds, col_q=dcq, col_s=dcs)
+        # the same copies with the transposed one in the K-tiled layout that the
+        # MXFP8 weight gradient reads
+        S = G.mx_col_slots(M, E, blocked=True)
+        dkq = torch.empty((2 * I, 32 * S), dtype=torch.uint8, device=dev)
+        dks = torch.empty((2 * I, S), dtype=torch.uint8, device=dev)
+        mx_dgu_k = G.mx_out(row_q=dq, row_s=ds, col_q=dkq, col_s=dks, col_blocked=True)
 
         def b1_bwd():
             G.moe_group_gemm_quant(op_dy2, op_w2d, I, H, grp, gmat)
@@ -268,15 +274,26 @@ def main():
         def fused_bwd_mx():
             G.moe_group_gemm_dglu_bwd(dy2, op_w2d, H, I, grp, pre, ep, dgu, mx_dgu)
 
+        def b1_bwd_mx_k():
+            b1_bwd()
+            G.moe_mxfp8_quantize(dgu, M, 2 * I, grp, mx_dgu_k)
+
+        def fused_bwd_mx_k():
+            G.moe_group_gemm_dglu_bwd(dy2, op_w2d, H, I, grp, pre, ep, dgu, mx_dgu_k)
+
         pb = paired_ms(torch, {"fused": dglu, "b1": b1_bwd, "fused_mx": fused_bwd_mx,
-                               "b1_mx": b1_bwd_mx})
+                               "b1_mx": b1_bwd_mx, "fused_mx_k": fused_bwd_mx_k,
+                               "b1_mx_k": b1_bwd_mx_k})
         b1["dgrad_dglu_fused_ms"] = round(pb["fused"], 4)
         b1["dgrad_dglu_unfused_ms"] = round(pb["b1"], 4)
         b1["dgrad_dglu_fused_speedup"] = round(pb["b1"] / pb["fused"], 3)
         b1["dgrad_dglu_mx_fused_ms"] = round(pb["fused_mx"], 4)
         b1["dgrad_dglu_mx_unfused_ms"] = round(pb["b1_mx"], 4)
         b1["dgrad_dglu_mx_fused_speedup"] = round(pb["b1_mx"] / pb["fused_mx"], 3)
-        del gmat, dq, ds, dcq, dcs
+        b1["dgrad_dglu_mx_ktiled_fused_ms"] = round(pb["fused_mx_k"], 4)
+        b1["dgrad_dglu_mx_ktiled_unfused_ms"] = round(pb["b1_mx_k"], 4)
+        b1["dgrad_dglu_mx_ktiled_fused_speedup"] = round(pb["b1_mx_k"] / pb["fused_mx_k"], 3)
+        del gmat, dq, ds, dcq, dcs, dkq, dks
 
     fc1_tflops = fc1_flops / (fc1_ms * 1e-3) / 1e12
     value = step_flops / (ms_per_step * 1e-3) / 1e12
@@ -536,8 +553,18 @@ def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I
         G.moe_glu_unfused(z, grp, I, ep, y)
         G.moe_mxfp8_quantize(y, M, I, grp, mx)
 
-    pm = paired_ms(torch, {"fused": fc1_mx, "b1": b1})
+    # the transposed copy in the K-tiled layout the MXFP8 weight gradient reads
+    Sk = G.mx_col_slots(M, E, blocked=True)
+    col_qk = torch.empty((I, 32 * Sk), dtype=torch.uint8, device=dev)
+    col_sk = torch.empty((I, Sk), dtype=torch.uint8, device=dev)
+    mx_k = G.mx_out(row_q=row_q, row_s=row_s, col_q=col_qk, col_s=col_sk, col_blocked=True)
+
+    def fc1_mx_k():
+        G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, None, pre, mx_k)
+
+    pm = paired_ms(torch, {"fused": fc1_mx, "b1": b1, "fused_k": fc1_mx_k})
     fc1_ms, b1_ms = pm["fused"], pm["b1"]
+    del col_qk, col_sk
     # the MXFP8 recipe's FC1 itself on the block-scaled MFMA: rows of x
     # quantised on the GPU, gate/up-repacked MXFP8 W1
     xq = torch.empty((M, H), dtype=torch.uint8, device=dev)
@@ -583,6 +610,7 @@ def bench_mxfp8(G, torch, time_kernel, w1, w1p, w2, counts, counts_h, E, M, H, I
     fc1_flops = 2.0 * M * H * 2 * I
     del x, w1t, z, w2q, w2s
     return {"fc1_swiglu_mx_ms": round(fc1_ms, 4),
+            "fc1_swiglu_mx_ktiled_cols_ms": round(pm["fused_k"], 4),
             "fc1_tflops": round(fc1_flops / fc1_ms / 1e9, 1),
             "fc1_b1_unfused_ms": round(b1_ms, 4), "fc1_fused_speedup": round(b1_ms / fc1_ms, 3),
             "fc2_mxfp8_ms": round(fc2_ms, 4), "fc2_tflops": round(fc2_flops / fc2_ms / 1e9, 1),

@@ -589,11 +589,19 @@ moe_status_t moe_mxfp8_quantize(const void* v, int R, int C, const moe_groups_t*
   if (mx->col_q && R > 0) {
     const int Eg = groups ? E : 0;
     int s_ld = mx->col_blocked ? 4 * ((R + 127) / 128 + Eg) : (R + 31) / 32 + Eg;
-    long long by = s_ld;
-    int gy = (int)(by < 65535 ? by : 65535);
-    hipLaunchKernelGGL(mx_cols_kernel, dim3((C + 255) / 256, gy), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(v), R, C, counts, E, mx->col_q, mx->col_s, s_ld,
-                       mx->e5m2, mx->col_blocked);
+    if (mx->col_blocked) {   // LDS-staged, 256 rows x 64 columns per item
+      const long long items = (long long)((R + 255) / 256 + Eg) * ((C + 63) / 64);
+      const int grid = (int)(items < (long long)cus * 6 ? items : (long long)cus * 6);
+      hipLaunchKernelGGL(mx_cols_ktiled_kernel, dim3(grid), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(v), R, C, counts, E, mx->col_q, mx->col_s, s_ld,
+                         mx->e5m2);
+    } else {
+      long long by = s_ld;
+      int gy = (int)(by < 65535 ? by : 65535);
+      hipLaunchKernelGGL(mx_cols_kernel, dim3((C + 255) / 256, gy), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(v), R, C, counts, E, mx->col_q, mx->col_s, s_ld,
+                         mx->e5m2, mx->col_blocked);
+    }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

@@ -538,6 +538,115 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const uint16_t* __restrict
   }
 }
 
+// The K-tiled transposed copy (blocked layout) with the tile staged in LDS:
+// one work item is 256 rows (8 slots, two K-tiles) of one group x 64 columns.
+// The item's rows are read as 128-byte row segments into LDS, each 16-byte
+// chunk rotated by its row's 32-row block (chunk (c + r/32) % 8) so that the
+// column reads of the quantisation step spread over the banks; lane (jp, k) of
+// a wave then quantises slot k of the column pair jp (one 4-byte read per row)
+// and writes their 32-code runs, 8 consecutive slots of a column (256
+// contiguous bytes) per 8 lanes.  Slots
+// of the group past its rows get zero codes and scale byte 127.  Persistent
+// grid over (row chunk, column chunk), column chunk fastest.
+__global__ __launch_bounds__(256) void mx_cols_ktiled_kernel(const uint16_t* __restrict__ v, int R, int C,
+                                                             const int* __restrict__ counts, int E,
+                                                             uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ s, int S, int e5) {
+  __shared__ GroupScan gs;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int Eg = 1;
+  if (counts) {
+    build_group_scan<256>(gs, counts, E, R, 256, 0, nullptr, nullptr, false, true);
+    Eg = E;
+  } else {   // one group of R rows
+    if (t == 0) {
+      gs.row_off[0] = 0; gs.row_off[1] = R;
+      gs.tile_off[0] = 0; gs.tile_off[1] = (R + 255) >> 8;
+      gs.mxs_off[0] = 0; gs.mxs_off[1] = 4 * ((R + 127) >> 7);
+    }
+    __syncthreads();
+  }
+  const int ncb = (C + 63) >> 6;
+  const long long items = (long long)gs.tile_off[Eg] * ncb;
+  // item geometry: group, chunk within it, rows, slots, columns
+  struct Item { int e, tc, r0, nrows, nsl, c0, ncols; };
+  auto item_of = [&](long long it) {
+    Item d;
+    const int ch = (int)(it / ncb), cb = (int)(it - (long long)ch * ncb);
+    int lo = 0, hi = Eg;   // the group of row chunk ch: last e with tile_off[e] <= ch
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (gs.tile_off[mid] <= ch) lo = mid; else hi = mid;
+    }
+    d.e = lo;
+    d.tc = ch - gs.tile_off[lo];
+    const int m_e = gs.row_off[lo + 1] - gs.row_off[lo];
+    d.r0 = gs.row_off[lo] + 256 * d.tc;
+    d.nrows = min(256, m_e - 256 * d.tc);
+    d.nsl = min(8, 4 * ((m_e + 127) >> 7) - 8 * d.tc);
+    d.c0 = cb * 64;
+    d.ncols = min(64, C - d.c0);
+    return d;
+  };
+  // this thread's 8 chunks of 8 columns (rows p*32 + t/8, chunk t%8); the
+  // next item's loads go out before the current item is quantised
+  uint4 buf[8];
+  auto load_item = [&](const Item& d) {
+#pragma unroll
+    for (int pss = 0; pss < 8; ++pss) {
+      const int rr = pss * 32 + (t >> 3), cc = t & 7;
+      buf[pss] = make_uint4(0u, 0u, 0u, 0u);
+      if (rr < d.nrows && cc * 8 < d.ncols)
+        buf[pss] = *reinterpret_cast<const uint4*>(v + (long long)(d.r0 + rr) * C + d.c0 + cc * 8);
+    }
+  };
+  long long it = blockIdx.x;
+  Item cur;
+  if (it < items) {
+    cur = item_of(it);
+    load_item(cur);
+  }
+  for (; it < items; it += gridDim.x) {
+    const int e = cur.e, tc = cur.tc, nrows = cur.nrows, nsl = cur.nsl, c0 = cur.c0, ncols = cur.ncols;
+    __syncthreads();   // the previous item's reads of the tile are done
+#pragma unroll
+    for (int pss = 0; pss < 8; ++pss) {
+      const int rr = pss * 32 + (t >> 3), cc = t & 7;
+      *reinterpret_cast<uint4*>(tile + rr * 64 + ((cc + (rr >> 5)) & 7) * 8) = buf[pss];
+    }
+    __syncthreads();
+    if (it + gridDim.x < items) {
+      cur = item_of(it + gridDim.x);
+      load_item(cur);
+    }
+    // lane (column pair jp, slot k): one 4-byte LDS read per row gives both
+    // columns' values
+    {
+      const int j = wave * 16 + 2 * (lane >> 3), k = lane & 7;
+      if (j < ncols && k < nsl) {
+        const int nv = max(0, min(32, nrows - 32 * k));
+        const uint32_t* col = reinterpret_cast<const uint32_t*>(tile + (((j >> 3) + k) & 7) * 8 + (j & 7));
+        float x0[32], x1[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t pr = col[(32 * k + i) * 32];
+          x0[i] = __uint_as_float(pr << 16);
+          x1[i] = __uint_as_float(pr & 0xFFFF0000u);
+        }
+        uint32_t w0[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u}, w1[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        const uint8_t sb0 = nv > 0 ? mx_quant32(x0, nv, w0, e5 != 0) : (uint8_t)127;
+        const uint8_t sb1 = nv > 0 ? mx_quant32(x1, nv, w1, e5 != 0) : (uint8_t)127;
+        const long long slot = (long long)(c0 + j) * S + gs.mxs_off[e] + 8 * tc + k;
+        store_codes32_slot(q + slot * 32, w0, nv);
+        store_codes32_slot(q + (slot + S) * 32, w1, nv);
+        s[slot] = sb0;
+        s[slot + S] = sb1;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- MXFP8 weight pack
 // Offline quantisation of a bf16 weight to MXFP8 along K, written in the
 // tile-blocked order the block-scaled GEMM streams: per expert, blocks of 256
