@@ -183,6 +183,17 @@ __device__ __forceinline__ void lds_dma16(const rsrc_t& rs, uint8_t* lds_wave_ba
       rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff, 0, 0);
 }
 
+// 16 bytes to global memory with the non-temporal hint: kernel outputs are
+// not read again by the kernel, and streaming them keeps the L2 for the
+// operand panels that the tiles running together share.  Used where a store
+// instruction writes whole 128-byte lines (staged rows); FC1's 32-byte row
+// pieces of y stay ordinary stores, which the L2 merges (with the hint they
+// measured 3% slower on the GPT-OSS-like FC1).
+__device__ __forceinline__ void store16_nt(void* dst, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));
+}
+
 // A zero the compiler cannot see through.  Epilogue addressing is derived
 // from it so that none of it is hoisted out of the tile loop, where it would
 // stay live across the main loop and push loop values into scratch.
@@ -368,8 +379,8 @@ __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
   for (int it = t; it < stg.rows() * cpr; it += NT) {
     int r = it / cpr, ch = it - r * cpr;
     if (r < rows_valid && ch * 8 < ncols_valid) {
-      uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
-      *reinterpret_cast<uint4*>(dst + r * dst_ld + ch * 8) = v;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
+      store16_nt(dst + r * dst_ld + ch * 8, v);
     }
   }
 }
@@ -1331,7 +1342,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
           const int r = it >> 5, ch = it & 31, cc = (ch & 15) * 8;
           if (r < rows_valid && cc < cvalid_n) {
             const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + ch * 8);
-            *reinterpret_cast<uint4*>(prow0 + r * ld2 + (ch < 16 ? 0 : p.I) + cc) = v;
+            store16_nt(prow0 + r * ld2 + (ch < 16 ? 0 : p.I) + cc, v);
           }
         }
         __syncthreads();
@@ -1620,7 +1631,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
             const int c = chunk_col(k) + pc * 8;
             if (r < rows_valid && c < p.I) {
               const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + k * 64 + pc * 8);
-              *reinterpret_cast<uint4*>(p.C + (long long)(row0 + r) * ld2 + (k < 2 ? 0 : p.I) + c) = v;
+              store16_nt(p.C + (long long)(row0 + r) * ld2 + (k < 2 ? 0 : p.I) + c, v);
             }
           }
         }
