@@ -1183,7 +1183,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       // own 16.5 KB of the stage arrays (rows of 128 fp32 + 16 bytes of
       // padding) so that each store writes 2 rows x 512 contiguous bytes:
       // whole cache lines instead of 32 rows x 32 bytes, a quarter of the L2
-      // write requests.  Rows past wg_P are outside the descriptor and
+      // write requests; with the non-temporal hint (aux bit 1 on gfx950), as
+      // the output is not read again here.  Rows past wg_P are outside the descriptor and
       // dropped; columns past N are skipped; accumulate adds the current
       // contents first.
       if (!(p.accumulate && m_e == 0)) {
@@ -1215,7 +1216,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
                     __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsC, off, 0, 0));
                 v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
               }
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsC, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsC, off, 0, 2);   // nt
             }
           }
         }
