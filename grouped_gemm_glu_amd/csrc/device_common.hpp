@@ -121,6 +121,9 @@ __device__ __forceinline__ uint8_t mx_quant32(const float* v, int nvalid, uint32
 
 // One slot of the K-tiled transposed layout: 32 codes to a 16-byte aligned
 // dst, the codes of rows from nvalid on (past the group's last row) zero.
+// NT: with the non-temporal hint (for callers whose neighbouring lanes write
+// the neighbouring slots, so that the lines are written whole).
+template <bool NT = false>
 __device__ __forceinline__ void store_codes32_slot(uint8_t* dst, const uint32_t* w, int nvalid) {
   uint32_t m[8];
 #pragma unroll
@@ -128,9 +131,26 @@ __device__ __forceinline__ void store_codes32_slot(uint8_t* dst, const uint32_t*
     const int k = nvalid - 4 * i;   // valid bytes of word i
     m[i] = k >= 4 ? w[i] : (k <= 0 ? 0u : (w[i] & ((1u << (8 * k)) - 1u)));
   }
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  d[0] = make_uint4(m[0], m[1], m[2], m[3]);
-  d[1] = make_uint4(m[4], m[5], m[6], m[7]);
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  v4u* d = reinterpret_cast<v4u*>(dst);
+  const v4u lo = {m[0], m[1], m[2], m[3]}, hi = {m[4], m[5], m[6], m[7]};
+  if constexpr (NT) {
+    __builtin_nontemporal_store(lo, d);
+    __builtin_nontemporal_store(hi, d + 1);
+  } else {
+    d[0] = lo;
+    d[1] = hi;
+  }
+}
+
+// 32 codes to a 16-byte aligned dst with the non-temporal hint (row-wise
+// copies, where 8 neighbouring lanes write one 256-byte run).
+__device__ __forceinline__ void store_codes32_aligned_nt(uint8_t* dst, const uint32_t* w) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  v4u* d = reinterpret_cast<v4u*>(dst);
+  const v4u lo = {w[0], w[1], w[2], w[3]}, hi = {w[4], w[5], w[6], w[7]};
+  __builtin_nontemporal_store(lo, d);
+  __builtin_nontemporal_store(hi, d + 1);
 }
 
 // 32 codes (w, little-endian) to dst, which has any alignment.  A full block

@@ -223,6 +223,7 @@ __device__ __forceinline__ void mx_from_stage_map(const Stg& stg, int rows_valid
                                                   const GemmArgs& p, int scol0, GCol gcol) {
   const int t = threadIdx.x + opaque_zero();
   if (p.row_q) {
+    const bool rq_aligned = (reinterpret_cast<uintptr_t>(p.row_q) & 15) == 0;
     const int nb = ncols >> 5;
     for (int it = t; it < stg.rows() * nb; it += NT) {
       int r = it / nb, cb = it - r * nb;
@@ -243,7 +244,10 @@ __device__ __forceinline__ void mx_from_stage_map(const Stg& stg, int rows_valid
       uint32_t w[8];
       uint8_t sb = mx_quant32(v, 32, w, p.mx_e5 != 0);
       long long grow = grow0 + r;
-      store_codes32(p.row_q + grow * p.mx_cols + gc, w, 32);
+      // (rows are a multiple of 64 bytes and gc of 32: 16-byte aligned
+      // whenever row_q is)
+      if (rq_aligned) store_codes32_aligned_nt(p.row_q + grow * p.mx_cols + gc, w);
+      else store_codes32(p.row_q + grow * p.mx_cols + gc, w, 32);
       p.row_s[grow * (p.mx_cols >> 5) + (gc >> 5)] = sb;
     }
   }
@@ -264,8 +268,8 @@ __device__ __forceinline__ void mx_from_stage_map(const Stg& stg, int rows_valid
       if (rb >= npad || gc < 0) continue;
       if (rb >= nrb) {   // K-tiled padding slot
         const uint32_t z[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        store_codes32_slot(p.col_q + gc * slot_bytes + (scol0 + rb) * 32LL, z, 0);
-        store_codes32_slot(p.col_q + (gc + 1) * slot_bytes + (scol0 + rb) * 32LL, z, 0);
+        store_codes32_slot<true>(p.col_q + gc * slot_bytes + (scol0 + rb) * 32LL, z, 0);
+        store_codes32_slot<true>(p.col_q + (gc + 1) * slot_bytes + (scol0 + rb) * 32LL, z, 0);
         p.col_s[gc * p.col_s_ld + scol0 + rb] = 127;
         p.col_s[(gc + 1) * p.col_s_ld + scol0 + rb] = 127;
         continue;
@@ -281,12 +285,12 @@ __device__ __forceinline__ void mx_from_stage_map(const Stg& stg, int rows_valid
       }
       uint32_t w[8];
       uint8_t sb = mx_quant32(v0, nvalid, w, p.mx_e5 != 0);
-      if (p.col_blocked) store_codes32_slot(p.col_q + gc * slot_bytes + (scol0 + rb) * 32LL, w, nvalid);
+      if (p.col_blocked) store_codes32_slot<true>(p.col_q + gc * slot_bytes + (scol0 + rb) * 32LL, w, nvalid);
       else store_codes32(p.col_q + gc * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[gc * p.col_s_ld + scol0 + rb] = sb;
       sb = mx_quant32(v1, nvalid, w, p.mx_e5 != 0);
       if (p.col_blocked)
-        store_codes32_slot(p.col_q + (gc + 1) * slot_bytes + (scol0 + rb) * 32LL, w, nvalid);
+        store_codes32_slot<true>(p.col_q + (gc + 1) * slot_bytes + (scol0 + rb) * 32LL, w, nvalid);
       else store_codes32(p.col_q + (gc + 1) * p.M_cap + grow0 + rb * 32, w, nvalid);
       p.col_s[(gc + 1) * p.col_s_ld + scol0 + rb] = sb;
     }
