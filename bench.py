@@ -304,6 +304,8 @@ def main():
         log("secondary: B2 traditional path")
         extra["b2_traditional_fc1"] = bench_b2(G, torch, time_kernel, x, counts, counts_h, w1, E,
                                                M, H, I, ep, y, kern_ms["fc1_glu"])
+        log("secondary: vendor GEMM libraries on the same FC1")
+        extra["vendor_fc1"] = bench_vendor(torch, x, w1, counts_h, E, M, H, I, kern_ms["fc1_glu"])
         log("secondary: CU margin with a concurrent copy")
         extra["cu_margin_overlap"] = bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre)
         log("secondary: amax outputs and parameter gradients")
@@ -433,6 +435,49 @@ def bench_b2(G, torch, time_kernel, x, counts, counts_h, w1, E, M, H, I, ep, y, 
     del w1t, z
     return {"ms": round(ms, 4), "fused_speedup": round(ms / fused_ms, 3),
             "what": "host readback of counts + 32 per-expert GEMM launches on 4 streams + GLU pass"}
+
+
+def bench_vendor(torch, x, w1, counts_h, E, M, H, I, fused_ms):
+    """Context for the FC1 kernel: the ROCm GEMM libraries behind torch on the
+    same FC1 GEMM (bf16 in, fp32 accumulation, bf16 pre-activation out, no
+    activation), with both operands K-contiguous: one hipBLASLt GEMM per
+    expert (the counts taken as known on the host: no readback charged),
+    torch._grouped_mm over the group offsets, and one dense GEMM of the same FLOPs (all rows against a
+    single expert's weights, whose panels the last-level cache holds) as the
+    ceiling that the library reaches on this chip for this shape."""
+    dev = x.device
+    xb = x.view(torch.bfloat16)
+    wkn = w1.view(torch.bfloat16).view(E, H, 2 * I)            # [E][K][N]
+    wnk = wkn.transpose(1, 2).contiguous()                      # [E][N][K]
+    out = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    off = np.concatenate([[0], np.cumsum(counts_h)]).astype(np.int64)
+    flops = 2.0 * M * H * 2 * I
+
+    def per_expert():
+        for e in range(E):
+            if counts_h[e]:
+                torch.mm(xb[off[e]:off[e + 1]], wnk[e].t(), out=out[off[e]:off[e + 1]])
+
+    def dense():
+        torch.mm(xb, wnk[0].t(), out=out)
+
+    res = {}
+    for name, fn in (("per_expert_hipblaslt", per_expert), ("dense_same_flops", dense)):
+        ms = min(_ev_ms(torch, fn, 10) for _ in range(3))
+        res[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                     "fused_fc1_speedup": round(ms / fused_ms, 3)}
+    try:
+        offs = torch.from_numpy(off[1:].astype(np.int32)).to(dev)
+        torch._grouped_mm(xb, wkn, offs=offs)
+        ms = min(_ev_ms(torch, lambda: torch._grouped_mm(xb, wkn, offs=offs), 10) for _ in range(3))
+        res["torch_grouped_mm"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                                   "fused_fc1_speedup": round(ms / fused_ms, 3)}
+    except Exception as exc:   # not every torch build has it on ROCm
+        res["torch_grouped_mm"] = {"error": repr(exc)[:200]}
+    res["what"] = ("FC1 GEMM only (no SwiGLU), bf16, library kernels chosen by torch; "
+                   "fused_fc1_speedup = library ms / this library's FC1 + SwiGLU ms")
+    del wnk, out
+    return res
 
 
 def bench_overlap(G, torch, x, grp, w1p, H, I, ep, y, pre, margin=32, copy_mib=2048):
