@@ -863,6 +863,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // behind them.
     constexpr int NVM = WGT ? 16 : (TBM + GM_BN) / (8 * NW);
     auto mfma_step_dma = [&](int buf, int sset, int ks) {
+      if constexpr (NW == 8) __builtin_amdgcn_s_setprio(1);   // as in the 16x16 loop (dGLU: -0.7%)
       mfmas(buf, sset, ks);
       static_for<NMF>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
@@ -871,6 +872,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // MFMA
       });
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NW == 8) __builtin_amdgcn_s_setprio(0);
     };
     // k-steps 0 .. KSTEPS-2 of the K-tile in stage sa (fragments of k-step 0
     // requested); the last k-step runs after the stage barrier
@@ -924,10 +926,17 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // and is reloaded for the next k-step right away, so every reload has
     // most of the k-step to land; the next A fragments (MB of them, double
     // buffered) are read during the first MB blocks; the next stage's DMA
-    // (when DMA) goes out one instruction per block.
+    // (when DMA) goes out one instruction per block.  The k-step that issues
+    // the DMA (the first after a stage barrier) runs at raised wave priority:
+    // of the two waves sharing a SIMD, the one that is behind keeps issuing
+    // while the other, done first, has dropped back, so the pair reaches the
+    // next barrier closer together (interleaved, same results: FC1 -0.8%,
+    // FC2 -0.8%, dX -1.5%; the MXFP8 loop measured no gain and keeps one
+    // priority).
     auto kstep = [&](auto curc, auto dmac, const uint8_t* nsa, int nks, int dkt, uint8_t* dst) {
       constexpr int cur = decltype(curc)::value;
       constexpr bool DMA = decltype(dmac)::value;
+      if constexpr (DMA) __builtin_amdgcn_s_setprio(1);
       static_for<8>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -948,6 +957,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // B reload
       });
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DMA) __builtin_amdgcn_s_setprio(0);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
