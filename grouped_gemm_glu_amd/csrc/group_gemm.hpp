@@ -454,6 +454,14 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // measured 2-9% faster on the DeepSeek-V3-like share, neutral on the
   // GPT-OSS-like FC1.
   constexpr bool HALF_FIRST = !WG && !(NW == 8 && EPI != EPI_DGLU);
+  // The 8-wave dGLU kernel (N = I = 2048 on the DeepSeek-V3-like share: 2.2
+  // full-tile units per CU) splits each short m-tile once more, into two
+  // 128 x 128 quarter tiles (column halves of the n-tile): with F full tiles
+  // and 2H quarter tiles on P workgroups every workgroup gets F / P full tiles
+  // and at most one quarter, where a half tile left the workgroups that drew
+  // one idle-free and the rest idle for its duration.
+  constexpr bool QTILE = NW == 8 && EPI == EPI_DGLU;
+  static_assert(!QTILE || (HALF_FIRST && BLAY == BL_PACKED), "quarter tiles: packed B, short tiles first");
   build_group_scan<NTH>(gs, p.counts, p.E, p.M_cap, WGM ? 128 : GM_BM, HALF_FIRST ? GM_BM / 2 : 0,
                           p.offsets_out, p.status_out, blockIdx.x == 0, p.col_blocked != 0);
   if (WG) {
@@ -475,7 +483,10 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // the full ones, so that every workgroup's share is balanced: with F full
   // and H half tiles on P workgroups, H <= P gives each workgroup at most
   // ceil((H + F) / P) tiles of which the first may be a half one.
-  const int n_half = WG ? 0 : gs.half_off[p.E] * p.ntiles_n;
+  // ids per short m-tile: one per n-tile, or with quarter tiles one per
+  // 128-column half of I
+  const int NHT = QTILE ? (p.N + 127) / 128 : p.ntiles_n;
+  const int n_half = WG ? 0 : gs.half_off[p.E] * NHT;
   const int total_tiles =
       WG ? p.E * p.ntiles_m * p.ntiles_n : n_half + gs.tile_off[p.E] * p.ntiles_n;
 
@@ -500,14 +511,17 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // the run of consecutive ids an XCD takes per round shares few A panels
     // and few B panels.
     int e, mt, nt;
+    int nq = 0;   // quarter tiles: the n-tile's column half
     if (!WG && tile < n_half) {
-      int lo = 0, hi = p.E;  // invariant: half_off[lo]*NT <= tile < half_off[hi]*NT
+      int lo = 0, hi = p.E;  // invariant: half_off[lo]*NHT <= tile < half_off[hi]*NHT
       while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
-        if (gs.half_off[mid] * NT <= tile) lo = mid; else hi = mid;
+        if (gs.half_off[mid] * NHT <= tile) lo = mid; else hi = mid;
       }
       e = lo;
-      nt = tile - gs.half_off[e] * NT;
+      const int lq = tile - gs.half_off[e] * NHT;
+      nt = QTILE ? lq >> 1 : lq;
+      nq = QTILE ? lq & 1 : 0;
       mt = gs.tile_off[e + 1] - gs.tile_off[e];   // after the expert's full m-tiles
     } else {
       int local, MT;
@@ -544,7 +558,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // (MXFP8 weight gradient: A's rows are the output rows mt*256 ..)
     const int row0 = WGT ? g_row0 : (WGM ? mt * GM_BM : g_row0 + mt * GM_BM);
     const int rows_valid = WG ? min(GM_BM, p.wg_P - mt * GM_BM) : min(GM_BM, m_e - mt * GM_BM);
-    const int n0 = nt * GM_BN;
+    const int n0 = nt * GM_BN + nq * (GM_BN / 2);
     const int nk_t = WGT ? (m_e + 63) / 64 : (WGM ? (m_e + 127) / 128 : nk);   // K-tiles of this tile
     const int kt0 = WGM ? gs.tile_off[e] : 0;        // first K-tile (MXFP8 weight gradient)
 
@@ -553,8 +567,11 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // waves 64 x 128); a group's last m-tile with at most 128 valid rows runs
     // with half the MI as a 128-row tile, half the MFMA work of the padded
     // 256-row tile.  Weight-gradient tiles are always full.
-    auto tile_body = [&](auto mic) {
+    auto tile_body = [&](auto mic, auto nbwc) {
     constexpr int MI = decltype(mic)::value;
+    constexpr int NBW = decltype(nbwc)::value;  // 32-column MFMA blocks per wave (4; quarter tiles 2)
+    constexpr int WBN = 32 * NBW;               // columns per wave
+    constexpr int TBN = 2 * WBN;                // tile columns
     constexpr int HR = 32 * MI;                 // rows per wave row
     constexpr int TBM = (NW / 2) * HR;          // tile rows
     constexpr int SHR = TBM / 2;                // staged rows per LDS stage array
@@ -613,6 +630,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // extra fragments).
     constexpr bool M16 = NW == 8 && !MXT && !WG && EPI != EPI_DGLU;
     constexpr bool MX8 = NW == 8 && MXT && !WG;
+    static_assert(NBW == 4 || (EPI == EPI_DGLU && !M16 && !MX8), "narrow tiles: the dGLU kernel's 32 x 32 loop only");
     constexpr int MB = 2 * MI;                  // 16-row blocks per wave
     f32x16 acc[MI][4];
     f32x4 acc16[M16 ? MB : 1][8];
@@ -651,11 +669,15 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     const rsrc_t rsZ = make_rsrc(Ab, 0);
     // a packed 32 KB block is already in LDS order: each wave instruction
     // streams 1 KB contiguously
+    // (a quarter tile takes rows nq * 128 .. + 127 of the block: the second
+    // 16 KB, whose rows keep their swizzle, which depends on row bits 0..4)
     auto issue_block = [&](const rsrc_t& rs, uint8_t* lds_tile, uint32_t koff) {
+      constexpr int NBK = TBN / (8 * NW);      // 1 KB pieces per wave
 #pragma unroll
-      for (int j = 0; j < 32 / NW; ++j) {
-        const int blk = wave * (32 / NW) + j;
-        lds_dma16(rs, lds_tile + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16), koff);
+      for (int j = 0; j < NBK; ++j) {
+        const int blk = wave * NBK + j;
+        lds_dma16(rs, lds_tile + blk * 1024,
+                  (uint32_t)(nq * (GM_TILE_BYTES / 2) + blk * 1024 + lane_t * 16), koff);
       }
     };
     // weight gradient: K-tile kt (rows kt*64 .. + 63 of the group) of an
@@ -760,7 +782,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     auto frag_load = [&](const uint8_t* sa, int ks, int buf, int sset) {
       const uint8_t* sb = sa + GM_TILE_BYTES;
       const int h = lane_t >> 5;
-      const int ra = wm * HR + (lane_t & 31), rbw = wn * 128 + (lane_t & 31);
+      const int ra = wm * HR + (lane_t & 31), rbw = wn * WBN + (lane_t & 31);
       if constexpr (WGT) {
         // lane l names row ks*16 + 8 (l/32) + 4 t + (l%16)/4 at column
         // c0 + 16 ((l/16) % 2) + 4 (l % 4) and so receives column c0 + l % 32
@@ -791,7 +813,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
           bfr[buf][j] = *reinterpret_cast<const bf16x8*>(sb + swz_off(rbw + j * 32, ch));
         };
         rd_a(0);
-        rd_b(0); rd_b(1); rd_b(2); rd_b(3);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) rd_b(j);
 #pragma unroll
         for (int i = 1; i < MI; ++i) rd_a(i);
       } else {
@@ -824,7 +847,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NBW; ++j) {
           if constexpr (!MXT) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i],
                                                                 acc[i][j], 0, 0, 0);
@@ -841,8 +864,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
         }
     };
     // LDS reads issued by the frag_load just before a k-step
-    constexpr int DS_STEP = (MXT || WG) ? 2 * (MI + 4) : MI + 4;
-    constexpr int NMF = 4 * MI;                 // MFMAs per k-step
+    constexpr int DS_STEP = (MXT || WG) ? 2 * (MI + 4) : MI + NBW;
+    constexpr int NMF = NBW * MI;               // MFMAs per k-step
     // NMF MFMAs; the LDS reads issued just before are spread over them from
     // the first MFMA on (two per MFMA where there are more reads than
     // MFMAs), so each has many MFMAs of cover before its use
@@ -861,7 +884,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // issued as a burst right after the barrier, the four waves' DMA
     // instructions queue at the address unit and hold up the MFMAs issued
     // behind them.
-    constexpr int NVM = WGT ? 16 : (TBM + GM_BN) / (8 * NW);
+    constexpr int NVM = WGT ? 16 : (TBM + TBN) / (8 * NW);
     auto mfma_step_dma = [&](int buf, int sset, int ks) {
       if constexpr (NW == 8) __builtin_amdgcn_s_setprio(1);   // as in the 16x16 loop (dGLU: -0.7%)
       mfmas(buf, sset, ks);
@@ -1530,14 +1553,14 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       auto do_block = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
         // (a select, not a branch: the block stays one scheduling region)
-        const bool drs_j = want_drs && n0 + wn * 128 + 32 * j < p.I;   // whole block (I % 64 == 0)
+        const bool drs_j = want_drs && n0 + wn * WBN + 32 * j < p.I;   // whole block (I % 64 == 0)
         u32x4 lg[MI][2], lu[MI][2];
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const uint32_t rowb = (uint32_t)(wm * HR + 32 * i + lm) * (uint32_t)ld2 * 2u;
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const uint32_t col = (uint32_t)(n0 + wn * 128 + 32 * j + 16 * pp + 8 * lh);
+            const uint32_t col = (uint32_t)(n0 + wn * WBN + 32 * j + 16 * pp + 8 * lh);
             lg[i][pp] = __builtin_amdgcn_raw_buffer_load_b128(rsPre, rowb + col * 2u, 0, 0);
             lu[i][pp] = __builtin_amdgcn_raw_buffer_load_b128(
                 rsPre, rowb + (col + (uint32_t)p.I) * 2u, 0, 0);
@@ -1605,13 +1628,13 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       };
       float hmax = 0.0f;   // rotated amax of this thread's share of the tile
 #pragma unroll
-      for (int round = 0; round < 2; ++round) {
+      for (int round = 0; round < NBW / 2; ++round) {   // (quarter tiles: one round)
         if (round == 0) stage_round(std::integral_constant<int, 0>{});
-        else stage_round(std::integral_constant<int, 1>{});
+        else if constexpr (NBW == 4) stage_round(std::integral_constant<int, 1>{});
         __syncthreads();
         // staged chunk k (64 columns): dg (k < 2) or du, of wave half wn = k & 1;
-        // its first global column of I is n0 + 128 (k & 1) + 64 round
-        auto chunk_col = [&](int k) { return n0 + 128 * (k & 1) + 64 * round; };
+        // its first global column of I is n0 + WBN (k & 1) + 64 round
+        auto chunk_col = [&](int k) { return n0 + WBN * (k & 1) + 64 * round; };
         if (p.ep.amax_out) {
           const uint32_t ok = (chunk_col(0) < p.I ? 5u : 0u) | (chunk_col(1) < p.I ? 10u : 0u);
           hmax = fmaxf(hmax, rht16_amax_stage<NTH>(stg, rows_valid, ok, p.ep.rht_signs));
@@ -1672,10 +1695,15 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     }
     };  // tile_body
     if constexpr (WG) {
-      tile_body(std::integral_constant<int, 4>{});
+      tile_body(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
     } else {
-      if (rows_valid <= 128) tile_body(std::integral_constant<int, 8 / NW>{});
-      else tile_body(std::integral_constant<int, 16 / NW>{});
+      using NB4 = std::integral_constant<int, 4>;
+      if (rows_valid <= 128) {
+        if constexpr (QTILE) tile_body(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+        else tile_body(std::integral_constant<int, 8 / NW>{}, NB4{});
+      } else {
+        tile_body(std::integral_constant<int, 16 / NW>{}, NB4{});
+      }
     }
   }
   if (p.ep.amax_out && lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.ep.amax_out), amax_bits);
