@@ -454,13 +454,13 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // measured 2-9% faster on the DeepSeek-V3-like share, neutral on the
   // GPT-OSS-like FC1.
   constexpr bool HALF_FIRST = !WG && !(NW == 8 && EPI != EPI_DGLU);
-  // The 8-wave dGLU kernel (N = I = 2048 on the DeepSeek-V3-like share: 2.2
-  // full-tile units per CU) splits each short m-tile once more, into two
-  // 128 x 128 quarter tiles (column halves of the n-tile): with F full tiles
-  // and 2H quarter tiles on P workgroups every workgroup gets F / P full tiles
-  // and at most one quarter, where a half tile left the workgroups that drew
-  // one idle-free and the rest idle for its duration.
-  constexpr bool QTILE = NW == 8 && EPI == EPI_DGLU;
+  // The dGLU kernels on packed W2 (N = I = 2048 on the DeepSeek-V3-like
+  // share: 2.2 full-tile units per CU) split each short m-tile once more,
+  // into two 128 x 128 quarter tiles (column halves of the n-tile): with F
+  // full tiles and 2H quarter tiles on P workgroups every workgroup gets F / P
+  // full tiles and at most one quarter, where a half tile left the workgroups
+  // that drew one idle-free and the rest idle for its duration.
+  constexpr bool QTILE = (EPI == EPI_DGLU || EPI == EPI_DGLU_G) && BLAY == BL_PACKED;
   static_assert(!QTILE || (HALF_FIRST && BLAY == BL_PACKED), "quarter tiles: packed B, short tiles first");
   build_group_scan<NTH>(gs, p.counts, p.E, p.M_cap, WGM ? 128 : GM_BM, HALF_FIRST ? GM_BM / 2 : 0,
                           p.offsets_out, p.status_out, blockIdx.x == 0, p.col_blocked != 0);
@@ -630,7 +630,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // extra fragments).
     constexpr bool M16 = NW == 8 && !MXT && !WG && EPI != EPI_DGLU;
     constexpr bool MX8 = NW == 8 && MXT && !WG;
-    static_assert(NBW == 4 || (EPI == EPI_DGLU && !M16 && !MX8), "narrow tiles: the dGLU kernel's 32 x 32 loop only");
+    static_assert(NBW == 4 || ((EPI == EPI_DGLU || EPI == EPI_DGLU_G) && !M16 && !MX8),
+                  "narrow tiles: the dGLU kernels' 32 x 32 loop only");
     constexpr int MB = 2 * MI;                  // 16-row blocks per wave
     f32x16 acc[MI][4];
     f32x4 acc16[M16 ? MB : 1][8];
@@ -1699,7 +1700,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     } else {
       using NB4 = std::integral_constant<int, 4>;
       if (rows_valid <= 128) {
-        if constexpr (QTILE) tile_body(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+        if constexpr (QTILE) tile_body(std::integral_constant<int, 8 / NW>{}, std::integral_constant<int, 2>{});
         else tile_body(std::integral_constant<int, 8 / NW>{}, NB4{});
       } else {
         tile_body(std::integral_constant<int, 16 / NW>{}, NB4{});
