@@ -118,3 +118,38 @@ def test_cu_margin_leaves_results_unchanged(G, margin):
     ref = _fc1_gpu(G, d["x"], counts, d["w1"], I, {}, preact=True)
     got = _fc1_gpu(G, d["x"], counts, d["w1"], I, {}, preact=True, cu_margin=margin)
     assert np.array_equal(got["y"], ref["y"]) and np.array_equal(got["preact"], ref["preact"])
+
+
+@pytest.mark.parametrize("E,I", [(1024, 64), (48, 320)])
+def test_dglu_many_short_groups(G, E, I):
+    """dgrad + dSwiGLU with many groups whose last m-tile holds at most 128
+    rows (run as 128 x 128 quarter tiles, one per 128 columns of I: with
+    I = 64 one quarter per group, with I = 320 three, the last one a column
+    half past I), against the oracle; then with fewer workgroups (a grid that
+    is not a multiple of the 8 XCDs), which must give the same bits."""
+    rng = np.random.default_rng(E + I)
+    counts = np.zeros(E, dtype=np.int64)
+    hot = rng.choice(E, size=min(E, 40), replace=False)
+    counts[hot] = rng.integers(1, 420, size=len(hot))
+    counts[E - 1] = 128                             # exactly a short tile's rows
+    H = 128
+    M = int(counts.sum())
+    m_cap = M + 5
+    dy2 = W.to_bf16_bits((rng.standard_normal((m_cap, H)) * 0.1).astype(np.float32))
+    w2 = W.to_bf16_bits((rng.standard_normal((E, I, H)) * 0.05).astype(np.float32))
+    pre = W.to_bf16_bits((rng.standard_normal((m_cap, 2 * I)) * 2).astype(np.float32))
+    w2p = empty_bits((G.moe_packed_weight_bytes(E, I, H) // 2,))
+    G.moe_pack_weight(dev_bits(w2), E, I, H, G.B_NK, w2p)
+    op = G.operand(w2p, layout=G.B_PACKED)
+    grp = G.groups(dev_i32(counts), m_cap)
+    outs = []
+    for margin in (0, 100):
+        dgu = empty_bits((m_cap, 2 * I))
+        G.moe_group_gemm_dglu_bwd(dev_bits(dy2), op, H, I, grp, dev_bits(pre),
+                                  G.epilogue("swiglu", alpha=1.702), dgu, cu_margin=margin)
+        _sync()
+        outs.append(host_bits(dgu))
+    ref = O.dgrad_dglu(dy2[:M], counts, w2, pre[:M], O.Epilogue(act="swiglu", alpha=1.702))
+    assert_bf16_close(outs[0][:M], ref, what=f"dgu E{E} I{I}", normwise=2e-2)
+    assert np.all(outs[0][M:] == BF16_NAN_SENTINEL)
+    assert np.array_equal(outs[0], outs[1])
