@@ -562,11 +562,13 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     const int nk_t = WGT ? (m_e + 63) / 64 : (WGM ? (m_e + 127) / 128 : nk);   // K-tiles of this tile
     const int kt0 = WGM ? gs.tile_off[e] : 0;        // first K-tile (MXFP8 weight gradient)
 
-    // The tile body for MI 32-row MFMA blocks per wave, NW / 2 wave rows:
-    // the 256-row tile (4 waves: MI = 4, waves 128 x 128; 8 waves: MI = 2,
-    // waves 64 x 128); a group's last m-tile with at most 128 valid rows runs
-    // with half the MI as a 128-row tile, half the MFMA work of the padded
-    // 256-row tile.  Weight-gradient tiles are always full.
+    // The tile body for MI 32-row MFMA blocks per wave, NW / 2 wave rows, and
+    // NBW 32-column blocks per wave, 2 wave columns: the 256 x 256 tile (4
+    // waves: MI = 4, waves 128 x 128; 8 waves: MI = 2, waves 64 x 128); a
+    // group's last m-tile with at most 128 valid rows runs with half the MI as
+    // a 128-row tile, half the MFMA work of the padded 256-row tile (the dGLU
+    // kernels on packed W2: two 128 x 128 quarter tiles, NBW = 2).
+    // Weight-gradient tiles are always full.
     auto tile_body = [&](auto mic, auto nbwc) {
     constexpr int MI = decltype(mic)::value;
     constexpr int NBW = decltype(nbwc)::value;  // 32-column MFMA blocks per wave (4; quarter tiles 2)
