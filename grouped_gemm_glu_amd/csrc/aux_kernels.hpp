@@ -20,7 +20,7 @@ __device__ __forceinline__ int plain_col_of_packed(int pr, int I) {
 
 // 16-byte chunk key of the tile-blocked layout (include/moe_glu.h): the same
 // XOR the GEMM uses for its LDS operand tiles.
-__device__ __forceinline__ int pack_key(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+__device__ __forceinline__ int pack_key(int r) { return (r & 7) ^ (((r >> 2) & 2) | ((r >> 4) & 1)); }
 
 enum { PACK_NK = 0, PACK_KN = 1, PACK_GATEUP = 2, UNPACK_GATEUP = 3 };
 

@@ -189,9 +189,9 @@ const char* moe_status_string(moe_status_t s);
  * (nb * K/64 + kb) * 16384 of the expert, and experts are ceil(N/256) * 256 * K
  * elements apart.  Inside a block, the 16-byte chunk c (0..7, k = 64 kb + 8c
  * .. +7) of row r (n = 256 nb + r) sits at byte r * 128 + 16 * (c XOR s(r)),
- * s(r) = (r mod 8) XOR ((r / 8) mod 4): the order in which the kernels stage
- * it in LDS, so each block streams from memory contiguously.  Rows n >= N are
- * zero.  Requires K % 64 == 0. */
+ * s(r) = (r mod 8) XOR (2 ((r / 8) mod 2) + (r / 16) mod 2): the order in
+ * which the kernels stage it in LDS, so each block streams from memory
+ * contiguously.  Rows n >= N are zero.  Requires K % 64 == 0. */
 size_t moe_packed_weight_bytes(int E, int N, int K);
 
 /* Packs per-expert weights into the tile-blocked layout above: the same

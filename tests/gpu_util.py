@@ -176,7 +176,7 @@ def packed_layout(w_nk: np.ndarray) -> np.ndarray:
     """The tile-blocked weight format documented in include/moe_glu.h, written
     out in numpy from its definition: per expert [N][K] -> blocks of 256 rows x
     64 columns, block (nb, kb) at (nb * K/64 + kb) * 16384, chunk c of row r at
-    16 * (c ^ s(r)) bytes into the row, s(r) = (r % 8) ^ ((r // 8) % 4); rows
+    16 * (c ^ s(r)) bytes into the row, s(r) = (r % 8) ^ (2 ((r // 8) % 2) + (r // 16) % 2); rows
     past N are zero.  Returns uint16 [E * ceil(N/256)*256 * K]."""
     E, N, K = w_nk.shape
     NB, KB = (N + 255) // 256, K // 64
@@ -185,7 +185,7 @@ def packed_layout(w_nk: np.ndarray) -> np.ndarray:
     out = np.zeros((E, NB, KB, 256, 8, 8), dtype=np.uint16)
     blocks = pad.reshape(E, NB, 256, KB, 8, 8).transpose(0, 1, 3, 2, 4, 5)  # e nb kb r c q
     r = np.arange(256)
-    key = (r % 8) ^ ((r // 8) % 4)
+    key = (r % 8) ^ (2 * ((r // 8) % 2) + (r // 16) % 2)
     for c in range(8):
         out[:, :, :, r, c ^ key, :] = blocks[:, :, :, r, c, :]
     return out.reshape(-1)
@@ -213,7 +213,7 @@ def packed_mx_layout(q_nk: np.ndarray, s_nk: np.ndarray):
     blocks = qp.reshape(E, NB, 256, KB, 8, 16).transpose(0, 1, 3, 2, 4, 5)   # e nb kb r c b
     out = np.zeros((E, NB, KB, 256, 8, 16), dtype=np.uint8)
     r = np.arange(256)
-    key = (r % 8) ^ ((r // 8) % 4)
+    key = (r % 8) ^ (2 * ((r // 8) % 2) + (r // 16) % 2)
     for c in range(8):
         out[:, :, :, r, c ^ key, :] = blocks[:, :, :, r, c, :]
     sc = sp.reshape(E, NB, 256, KB, 4).transpose(0, 1, 3, 2, 4)                # e nb kb r b
