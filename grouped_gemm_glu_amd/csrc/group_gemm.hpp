@@ -9,18 +9,20 @@
 // a group is partial and handled by clamped loads and masked stores ([MEGA]
 // §5.3).
 //
-// Tile 256 x 256 x 64.  The bf16 kernels on packed weights run 8 waves (two
-// per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles, 2 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 each; the others 4 waves in a 2 x 2 grid of
-// 128 x 128 sub-tiles (4 x 4 blocks).  Operands
-// are staged in LDS as [rows][64] bf16, 128 bytes per row, with the 16-byte
-// chunk index XOR-swizzled by ((r ^ (r >> 3)) & 7) so that the fragment reads
-// (8 consecutive rows, one chunk) and the transposed weight writes (rows 8
-// apart) are both free of bank conflicts.  Two LDS stages filled by direct
-// global -> LDS loads (buffer_load ... lds): the DMA of K-tile t + 2 is issued
-// right after the barrier that frees its stage, one instruction per MFMA of
-// the last k-step of K-tile t, whose fragments are already in registers, so
-// the barrier does not drain the MFMA pipe.
+// Tile 256 x 256 x 64.  The step's kernels on packed weights (gm_waves) run
+// 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles: FC1, FC2 and
+// dX as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16, dgrad + dGLU as 2 x 4
+// blocks of v_mfma_f32_32x32x16_bf16, MXFP8 operands as 2 x 4 blocks of the
+// block-scaled 32 x 32 x 64; every other kernel (weight gradients, plain B
+// layouts, the parameter-gradient dGLU, ...) 4 waves in a 2 x 2 grid of
+// 128 x 128 sub-tiles.  Operands are
+// staged in LDS as [rows][128 bytes] (64 bf16 or 128 fp8 values), with the
+// 16-byte chunk index XOR-swizzled by row bits 0..4 (swz_key) so that the
+// fragment reads of both MFMA shapes are free of bank conflicts.  Two LDS
+// stages filled by direct global -> LDS loads (buffer_load ... lds): the DMA
+// of K-tile t + 2 is issued right after the barrier that frees its stage,
+// spread over the MFMAs of the last k-step of K-tile t, whose fragments are
+// already in registers, so the barrier does not drain the MFMA pipe.
 //
 // Epilogues (fused; the accumulators never go to HBM in fp32):
 //   EPI_GLU   FC1: bias, clamp, activation * up, row scale -> bf16 y; optional
@@ -403,8 +405,8 @@ __device__ __forceinline__ void store_stage(const Stg& stg, int rows_valid,
 template <int EPI, int BLAY, int AT = AT_BF16, int ACT = ACT_SWIGLU>
 __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_kernel(GemmArgs p) {
   // Operand rows are staged as 128-byte K slices whatever the type: 64 bf16
-  // (4 k-steps of v_mfma_f32_32x32x16_bf16) or 128 e4m3 (2 k-steps of
-  // v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8 stages also carry the tile's
+  // (4 k-steps of v_mfma_f32_32x32x16_bf16 or 2 of v_mfma_f32_16x16x32_bf16)
+  // or 128 e4m3 (2 k-steps of v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8 stages also carry the tile's
   // E8M0 scales: 256 rows x 4 bytes for A and for B after the two tiles.
   constexpr bool MXT = AT != AT_BF16;
   // block-scaled MFMA format codes (0 = e4m3, 1 = e5m2) of B (the first
@@ -892,7 +894,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     };
     // The same with the next stage's DMA (NVM VMEM instructions per wave, 2
     // more with MXFP8 scales) spread over the MFMAs, one or two per MFMA:
-    // issued as a burst right after the barrier, the four waves' DMA
+    // issued as a burst right after the barrier, the waves' DMA
     // instructions queue at the address unit and hold up the MFMAs issued
     // behind them.
     constexpr int NVM = WGT ? 16 : (TBM + TBN) / (8 * NW);
