@@ -634,13 +634,15 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     const uint32_t kn_voff =
         (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
 
-    // bf16 on 8 waves (FC1 and the plain GroupGemm): the main loop runs on
-    // v_mfma_f32_16x16x32_bf16 (its accumulators are moved into the 32 x 32
-    // layout below for the epilogues); everything else on
-    // v_mfma_f32_32x32x16_bf16 or the block-scaled 32 x 32 x 64 form (the
-    // dGLU epilogue's preact registers leave no room for the 16 x 16 form's
-    // extra fragments).
-    constexpr bool M16 = NW == 8 && !MXT && !WG && EPI != EPI_DGLU;
+    // bf16 on 8 waves (FC1, the plain GroupGemm, and dgrad + dGLU on full
+    // and half tiles): the main loop runs on v_mfma_f32_16x16x32_bf16 (its
+    // accumulators are moved into the 32 x 32 layout below for the
+    // epilogues; the results are bit-identical to the 32 x 32 loop's).  The
+    // dGLU quarter tiles (64 columns per wave) and everything else run on
+    // v_mfma_f32_32x32x16_bf16 or the block-scaled 32 x 32 x 64 form.  With
+    // conflict-free 16 x 16 reads the dGLU kernel gains 0.4-0.7% (it measured
+    // even while those reads had two-way bank conflicts).
+    constexpr bool M16 = NW == 8 && !MXT && !WG && (EPI != EPI_DGLU || NBW == 4);
     constexpr bool MX8 = NW == 8 && MXT && !WG;
     static_assert(NBW == 4 || ((EPI == EPI_DGLU || EPI == EPI_DGLU_G) && !M16 && !MX8),
                   "narrow tiles: the dGLU kernels' 32 x 32 loop only");
