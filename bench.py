@@ -241,9 +241,19 @@ def main():
             G.moe_group_gemm_quant(op_x, op_w1t, 2 * I, H, grp, z)
             G.moe_glu_unfused(z, grp, I, ep, y)
 
-        pm = paired_ms(torch, {"fused": fc1, "b1": b1_chain})
+        def b1_gemm_only():
+            G.moe_group_gemm_quant(op_x, op_w1t, 2 * I, H, grp, z)
+
+        def fc1_no_preact():   # inference, or a backward that recomputes z
+            G.moe_group_gemm_glu_fwd(x, grp, w1p, H, I, ep, y, None)
+
+        pm = paired_ms(torch, {"fused": fc1, "b1": b1_chain, "fused_y_only": fc1_no_preact,
+                               "b1_gemm": b1_gemm_only})
         b1 = {"fc1_fused_ms": round(pm["fused"], 4), "fc1_unfused_ms": round(pm["b1"], 4),
               "fused_speedup": round(pm["b1"] / pm["fused"], 3),
+              "fc1_fused_y_only_ms": round(pm["fused_y_only"], 4),
+              "fused_y_only_speedup": round(pm["b1"] / pm["fused_y_only"], 3),
+              "b1_gemm_ms": round(pm["b1_gemm"], 4),
               "timing": "interleaved, best of 3 rounds of 10"}
         del w1t_plain, z
         # the backward counterpart: dgrad GroupGemm writing dL/dy in bf16, then
