@@ -10,9 +10,10 @@
 // §5.3).
 //
 // Tile 256 x 256 x 64.  The step's kernels on packed weights (gm_waves) run
-// 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles: FC1, FC2 and
-// dX as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16, dgrad + dGLU as 2 x 4
-// blocks of v_mfma_f32_32x32x16_bf16, MXFP8 operands as 2 x 4 blocks of the
+// 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles: FC1, FC2, dX
+// and dgrad + dGLU as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16 (the dGLU's
+// 128 x 128 quarter tiles: 32 x 64 per wave, 1 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16), MXFP8 operands as 2 x 4 blocks of the
 // block-scaled 32 x 32 x 64; every other kernel (weight gradients, plain B
 // layouts, the parameter-gradient dGLU, ...) 4 waves in a 2 x 2 grid of
 // 128 x 128 sub-tiles.  Operands are
@@ -406,8 +407,9 @@ template <int EPI, int BLAY, int AT = AT_BF16, int ACT = ACT_SWIGLU>
 __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_kernel(GemmArgs p) {
   // Operand rows are staged as 128-byte K slices whatever the type: 64 bf16
   // (4 k-steps of v_mfma_f32_32x32x16_bf16 or 2 of v_mfma_f32_16x16x32_bf16)
-  // or 128 e4m3 (2 k-steps of v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8 stages also carry the tile's
-  // E8M0 scales: 256 rows x 4 bytes for A and for B after the two tiles.
+  // or 128 e4m3 (2 k-steps of v_mfma_scale_f32_32x32x64_f8f6f4).  MXFP8
+  // stages also carry the tile's E8M0 scales: 256 rows x 4 bytes for A and
+  // for B after the two tiles.
   constexpr bool MXT = AT != AT_BF16;
   // block-scaled MFMA format codes (0 = e4m3, 1 = e5m2) of B (the first
   // source) and of A (the second source)
