@@ -508,8 +508,6 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   const int slot = (P % 8 == 0) ? ((blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3)) : blockIdx.x;
   const int nk = p.K * ESZ / 128;             // K-tiles of 128 bytes per row
   const int NT = p.ntiles_n;
-  // LDS-DMA lane coordinates: a wave instruction fills 8 rows x 128 B
-  const int rl = lane >> 3, pc = lane & 7;
 
   // the amax epilogues' running wave maximum (bits of a non-negative float):
   // raised into amax_out with one atomic per wave after the last tile, not
@@ -1644,8 +1642,9 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
         __builtin_amdgcn_sched_barrier(0);
       };
       float hmax = 0.0f;   // rotated amax of this thread's share of the tile
-#pragma unroll
-      for (int round = 0; round < NBW / 2; ++round) {   // (quarter tiles: one round)
+      constexpr int NROUND = NBW / 2;   // (quarter tiles: one round)
+#pragma unroll NROUND
+      for (int round = 0; round < NROUND; ++round) {
         if (round == 0) stage_round(std::integral_constant<int, 0>{});
         else if constexpr (NBW == 4) stage_round(std::integral_constant<int, 1>{});
         __syncthreads();
