@@ -98,10 +98,12 @@ enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2, AT_MX_B5 = 3, AT_MX_AB5 = 4 };
 // SIMD, so that one wave's MFMAs run while the other waits on its loads or at
 // the stage barrier (the kernels on packed weights with bf16 or MXFP8 e4m3 /
 // e5m2-A operands: 3-5% faster on the DeepSeek-V3-like share, same results
-// bit for bit).
+// bit for bit; the dGLU kernel with d(bias) / d(row_scale) 6.5% faster once
+// its epilogue stopped spilling).
 constexpr int gm_waves(int epi, int blay, int at) {
   return (blay == BL_PACKED &&
-          ((at == AT_BF16 && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU)) ||
+          ((at == AT_BF16 &&
+            (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU || epi == EPI_DGLU_G)) ||
            ((at == AT_MX || at == AT_MX_A5) && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE))))
              ? 8
              : 4;
@@ -459,13 +461,14 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // A group's last m-tile with at most 128 rows always runs as a 128-row
   // tile; whether it is also scheduled apart, among the half tiles that take
   // the first ids, is per kernel.  The dGLU kernel (N = I: few tile rounds
-  // per CU) keeps that, since a workgroup's share is then at most one half
-  // tile plus full ones.  The other 8-wave kernels (FC1, FC2 and dX, bf16
+  // per CU; with or without the parameter gradients) keeps that, since a
+  // workgroup's share is then at most one half tile plus full ones.  The
+  // other 8-wave kernels (FC1, FC2 and dX, bf16
   // or MXFP8; many rounds) schedule it in its expert's 4 x 8 block instead,
   // where it shares the B panels of the expert's other m-tiles in L2:
   // measured 2-9% faster on the DeepSeek-V3-like share, neutral on the
   // GPT-OSS-like FC1.
-  constexpr bool HALF_FIRST = !WG && !(NW == 8 && EPI != EPI_DGLU);
+  constexpr bool HALF_FIRST = !WG && !(NW == 8 && EPI != EPI_DGLU && EPI != EPI_DGLU_G);
   // The dGLU kernels on packed W2 (N = I = 2048 on the DeepSeek-V3-like
   // share: 2.2 full-tile units per CU) split each short m-tile once more,
   // into two 128 x 128 quarter tiles (column halves of the n-tile): with F
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // v_mfma_f32_32x32x16_bf16 or the block-scaled 32 x 32 x 64 form.  With
     // conflict-free 16 x 16 reads the dGLU kernel gains 0.4-0.7% (it measured
     // even while those reads had two-way bank conflicts).
-    constexpr bool M16 = NW == 8 && !MXT && !WG && (EPI != EPI_DGLU || NBW == 4);
+    constexpr bool M16 = NW == 8 && !MXT && !WG && ((EPI != EPI_DGLU && EPI != EPI_DGLU_G) || NBW == 4);
     constexpr bool MX8 = NW == 8 && MXT && !WG;
     static_assert(NBW == 4 || ((EPI == EPI_DGLU || EPI == EPI_DGLU_G) && !M16 && !MX8),
                   "narrow tiles: the dGLU kernels' 32 x 32 loop only");
@@ -1656,14 +1659,20 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
           hmax = fmaxf(hmax, rht16_amax_stage<NTH>(stg, rows_valid, ok, p.ep.rht_signs));
         }
         if (PG && p.ep.dbias_out) {
-          // d(bias): thread t sums staged column t (chunk t / 64) over the
-          // tile's valid rows (bf16 values as written), one atomic per column
-          const int t = tid + z0, k = t >> 6, c = chunk_col(k) + (t & 63);
+          // d(bias): thread t of a 256-thread group sums staged column t
+          // (chunk t / 64) over the tile's valid rows (bf16 values as
+          // written), one atomic per column and group; with 8 waves the two
+          // groups take one staged row half each
+          constexpr int NGRP = NTH / 256;
+          static_assert(NGRP == 1 || NGRP == 2, "d(bias) column sums: 4 or 8 waves");
+          const int t = (tid + z0) & 255, grp_half = (tid + z0) >> 8;
+          const int k = t >> 6, c = chunk_col(k) + (t & 63);
           if (c < p.I) {
             // 8 rows per step, 4 partial sums: the loads run ahead of the adds
             float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
+              if (NGRP == 2 && hh != grp_half) continue;
               const uint16_t* col = (hh ? stg.h1 : stg.h0) + k * 64 + (t & 63);
               const int nr = min(SHR, rows_valid - hh * SHR);
               int r = 0;
