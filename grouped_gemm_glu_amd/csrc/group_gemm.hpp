@@ -11,12 +11,12 @@
 //
 // Tile 256 x 256 x 64.  The step's kernels on packed weights (gm_waves) run
 // 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles: FC1, FC2, dX
-// and dgrad + dGLU as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16 (the dGLU's
-// 128 x 128 quarter tiles: 32 x 64 per wave, 1 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16), MXFP8 operands as 2 x 4 blocks of the
-// block-scaled 32 x 32 x 64; every other kernel (weight gradients, plain B
-// layouts, the parameter-gradient dGLU, ...) 4 waves in a 2 x 2 grid of
-// 128 x 128 sub-tiles.  Operands are
+// and dgrad + dGLU (with or without the parameter gradients) as 4 x 8 blocks
+// of v_mfma_f32_16x16x32_bf16 (the dGLU's 128 x 128 quarter tiles: 32 x 64
+// per wave, 1 x 2 blocks of v_mfma_f32_32x32x16_bf16), MXFP8 operands as
+// 2 x 4 blocks of the block-scaled 32 x 32 x 64; every other kernel (weight
+// gradients, plain B layouts, the non-gated activations) 4 waves in a 2 x 2
+// grid of 128 x 128 sub-tiles.  Operands are
 // staged in LDS as [rows][128 bytes] (64 bf16 or 128 fp8 values), with the
 // 16-byte chunk index XOR-swizzled by row bits 0..4 (swz_key) so that the
 // fragment reads of both MFMA shapes are free of bank conflicts.  Two LDS
@@ -637,8 +637,9 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     const uint32_t kn_voff =
         (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
 
-    // bf16 on 8 waves (FC1, the plain GroupGemm, and dgrad + dGLU on full
-    // and half tiles): the main loop runs on v_mfma_f32_16x16x32_bf16 (its
+    // bf16 on 8 waves (FC1, the plain GroupGemm, and dgrad + dGLU with or
+    // without the parameter gradients on full and half tiles): the main
+    // loop runs on v_mfma_f32_16x16x32_bf16 (its
     // accumulators are moved into the 32 x 32 layout below for the
     // epilogues; the results are bit-identical to the 32 x 32 loop's).  The
     // dGLU quarter tiles (64 columns per wave) and everything else run on
