@@ -11,12 +11,12 @@
 //
 // Tile 256 x 256 x 64.  The step's kernels on packed weights (gm_waves) run
 // 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles: FC1, FC2, dX
-// and dgrad + dGLU (with or without the parameter gradients) as 4 x 8 blocks
-// of v_mfma_f32_16x16x32_bf16 (the dGLU's 128 x 128 quarter tiles: 32 x 64
-// per wave, 1 x 2 blocks of v_mfma_f32_32x32x16_bf16), MXFP8 operands as
-// 2 x 4 blocks of the block-scaled 32 x 32 x 64; every other kernel (weight
-// gradients, plain B layouts, the non-gated activations) 4 waves in a 2 x 2
-// grid of 128 x 128 sub-tiles.  Operands are
+// and dgrad + dGLU (with or without the parameter gradients), and the
+// non-gated forms, as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16 (the dGLU's
+// 128 x 128 quarter tiles: 32 x 64 per wave, 1 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16), MXFP8 operands as 2 x 4 blocks of the
+// block-scaled 32 x 32 x 64; the other kernels (weight gradients, plain B
+// layouts) 4 waves in a 2 x 2 grid of 128 x 128 sub-tiles.  Operands are
 // staged in LDS as [rows][128 bytes] (64 bf16 or 128 fp8 values), with the
 // 16-byte chunk index XOR-swizzled by row bits 0..4 (swz_key) so that the
 // fragment reads of both MFMA shapes are free of bank conflicts.  Two LDS
@@ -99,11 +99,12 @@ enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2, AT_MX_B5 = 3, AT_MX_AB5 = 4 };
 // the stage barrier (the kernels on packed weights with bf16 or MXFP8 e4m3 /
 // e5m2-A operands: 3-5% faster on the DeepSeek-V3-like share, same results
 // bit for bit; the dGLU kernel with d(bias) / d(row_scale) 6.5% faster once
-// its epilogue stopped spilling).
+// its epilogue stopped spilling, the non-gated FC1 14% and its backward 3%).
 constexpr int gm_waves(int epi, int blay, int at) {
   return (blay == BL_PACKED &&
           ((at == AT_BF16 &&
-            (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU || epi == EPI_DGLU_G)) ||
+            (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU || epi == EPI_DGLU_G ||
+             epi == EPI_ACT || epi == EPI_DACT)) ||
            ((at == AT_MX || at == AT_MX_A5) && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE))))
              ? 8
              : 4;
