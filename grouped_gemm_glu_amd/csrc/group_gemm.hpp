@@ -9,14 +9,15 @@
 // a group is partial and handled by clamped loads and masked stores ([MEGA]
 // §5.3).
 //
-// Tile 256 x 256 x 64.  The step's kernels on packed weights (gm_waves) run
-// 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles: FC1, FC2, dX
-// and dgrad + dGLU (with or without the parameter gradients), and the
-// non-gated forms, as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16 (the dGLU's
-// 128 x 128 quarter tiles: 32 x 64 per wave, 1 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16), MXFP8 operands as 2 x 4 blocks of the
-// block-scaled 32 x 32 x 64; the other kernels (weight gradients, plain B
-// layouts) 4 waves in a 2 x 2 grid of 128 x 128 sub-tiles.  Operands are
+// Tile 256 x 256 x 64.  The step's kernels on packed or K-contiguous plain
+// weights (gm_waves) run 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128
+// sub-tiles: FC1, FC2, dX and dgrad + dGLU (with or without the parameter
+// gradients), and the non-gated forms, as 4 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16 (the dGLU's 128 x 128 quarter tiles: 32 x 64 per
+// wave, 1 x 2 blocks of v_mfma_f32_32x32x16_bf16), MXFP8 operands as 2 x 4
+// blocks of the block-scaled 32 x 32 x 64; the other kernels (weight
+// gradients, N-contiguous plain B) 4 waves in a 2 x 2 grid of 128 x 128
+// sub-tiles.  Operands are
 // staged in LDS as [rows][128 bytes] (64 bf16 or 128 fp8 values), with the
 // 16-byte chunk index XOR-swizzled by row bits 0..4 (swz_key) so that the
 // fragment reads of both MFMA shapes are free of bank conflicts.  Two LDS
@@ -99,13 +100,17 @@ enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2, AT_MX_B5 = 3, AT_MX_AB5 = 4 };
 // the stage barrier (the kernels on packed weights with bf16 or MXFP8 e4m3 /
 // e5m2-A operands: 3-5% faster on the DeepSeek-V3-like share, same results
 // bit for bit; the dGLU kernel with d(bias) / d(row_scale) 6.5% faster once
-// its epilogue stopped spilling, the non-gated FC1 14% and its backward 3%).
+// its epilogue stopped spilling, the non-gated FC1 14% and its backward 3%;
+// on K-contiguous plain weights, whose B DMA is row-strided like A's, dX 10%
+// and dgrad's GEMM 3%).
 constexpr int gm_waves(int epi, int blay, int at) {
   return (blay == BL_PACKED &&
           ((at == AT_BF16 &&
             (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU || epi == EPI_DGLU_G ||
              epi == EPI_ACT || epi == EPI_DACT)) ||
-           ((at == AT_MX || at == AT_MX_A5) && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE))))
+           ((at == AT_MX || at == AT_MX_A5) && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE)))) ||
+                 (blay == BL_NK && at == AT_BF16 &&
+                  (epi == EPI_STORE || epi == EPI_DGLU || epi == EPI_DGLU_G || epi == EPI_DACT))
              ? 8
              : 4;
 }
@@ -962,8 +967,15 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     auto dmaB = [&](int kt, uint8_t* st, int j) {
       const bool in = kt < nk_t;
       const int blk = wave * NJB + j;
-      lds_dma16(in ? rsB : rsZ, st + GM_TILE_BYTES + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16),
-                (uint32_t)kt * GM_TILE_BYTES);
+      if constexpr (BLAY == BL_NK) {   // K-contiguous plain B: row-strided, as A
+        const uint32_t vrow = (uint32_t)(wave * 8 * NJB + rl_t) * b_stride;
+        const int c = pc_t ^ (rl_t ^ swz_hi(blk & 3));
+        lds_dma16(in ? rsB : rsZ, st + GM_TILE_BYTES + blk * 1024,
+                  vrow + (uint32_t)(j * 8) * b_stride + (uint32_t)(c << 4), (uint32_t)kt * 128u);
+      } else {                         // packed: each 1 KB piece contiguous
+        lds_dma16(in ? rsB : rsZ, st + GM_TILE_BYTES + blk * 1024, (uint32_t)(blk * 1024 + lane_t * 16),
+                  (uint32_t)kt * GM_TILE_BYTES);
+      }
     };
     // one k-step, j (B block) outer: B fragment j is dead after its MB MFMAs
     // and is reloaded for the next k-step right away, so every reload has
