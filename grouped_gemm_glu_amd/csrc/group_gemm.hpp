@@ -475,14 +475,15 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   // measured 2-9% faster on the DeepSeek-V3-like share, neutral on the
   // GPT-OSS-like FC1.
   constexpr bool HALF_FIRST = !WG && !(NW == 8 && EPI != EPI_DGLU && EPI != EPI_DGLU_G);
-  // The dGLU kernels on packed W2 (N = I = 2048 on the DeepSeek-V3-like
-  // share: 2.2 full-tile units per CU) split each short m-tile once more,
-  // into two 128 x 128 quarter tiles (column halves of the n-tile): with F
+  // The dGLU kernels on packed or K-contiguous plain W2 (N = I = 2048 on the
+  // DeepSeek-V3-like share: 2.2 full-tile units per CU) split each short
+  // m-tile once more, into two 128 x 128 quarter tiles (column halves of
+  // the n-tile): with F
   // full tiles and 2H quarter tiles on P workgroups every workgroup gets F / P
   // full tiles and at most one quarter, where a half tile left the workgroups
   // that drew one idle-free and the rest idle for its duration.
-  constexpr bool QTILE = (EPI == EPI_DGLU || EPI == EPI_DGLU_G) && BLAY == BL_PACKED;
-  static_assert(!QTILE || (HALF_FIRST && BLAY == BL_PACKED), "quarter tiles: packed B, short tiles first");
+  constexpr bool QTILE = (EPI == EPI_DGLU || EPI == EPI_DGLU_G) && (BLAY == BL_PACKED || BLAY == BL_NK);
+  static_assert(!QTILE || HALF_FIRST, "quarter tiles: short tiles first");
   build_group_scan<NTH>(gs, p.counts, p.E, p.M_cap, WGM ? 128 : GM_BM, HALF_FIRST ? GM_BM / 2 : 0,
                           p.offsets_out, p.status_out, blockIdx.x == 0, p.col_blocked != 0);
   if (WG) {
@@ -737,8 +738,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
       }
       const uint32_t kk = (uint32_t)(kt0 + kt);   // K-tile within the rows
       issue_tile(std::integral_constant<int, TBM>{}, in ? rsA : rsZ, sa, a_stride, kk * 128u);
-      if (BLAY == BL_NK)
-        issue_tile(std::integral_constant<int, GM_BN>{}, in ? rsB : rsZ, sa + GM_TILE_BYTES,
+      if (BLAY == BL_NK)   // the tile's TBN rows of B from n0 (a quarter tile's 128)
+        issue_tile(std::integral_constant<int, TBN>{}, in ? rsB : rsZ, sa + GM_TILE_BYTES,
                    b_stride, kk * 128u);
       if (BLAY == BL_PACKED)
         issue_block(in ? rsB : rsZ, sa + GM_TILE_BYTES, (uint32_t)kt * GM_TILE_BYTES);
