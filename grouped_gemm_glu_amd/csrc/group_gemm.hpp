@@ -9,15 +9,16 @@
 // a group is partial and handled by clamped loads and masked stores ([MEGA]
 // §5.3).
 //
-// Tile 256 x 256 x 64.  The step's kernels on packed or K-contiguous plain
-// weights (gm_waves) run 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128
-// sub-tiles: FC1, FC2, dX and dgrad + dGLU (with or without the parameter
-// gradients), and the non-gated forms, as 4 x 8 blocks of
-// v_mfma_f32_16x16x32_bf16 (the dGLU's 128 x 128 quarter tiles: 32 x 64 per
-// wave, 1 x 2 blocks of v_mfma_f32_32x32x16_bf16), MXFP8 operands as 2 x 4
-// blocks of the block-scaled 32 x 32 x 64; the other kernels (weight
-// gradients, N-contiguous plain B) 4 waves in a 2 x 2 grid of 128 x 128
-// sub-tiles.  Operands are
+// Tile 256 x 256 x 64.  Every kernel but the weight gradients (gm_waves)
+// runs 8 waves (two per SIMD) in a 4 x 2 grid of 64 x 128 sub-tiles: FC1,
+// FC2, dX and dgrad + dGLU (with or without the parameter gradients), and
+// the non-gated forms, on packed or K-contiguous plain weights as 4 x 8
+// blocks of v_mfma_f32_16x16x32_bf16 (the dGLU's 128 x 128 quarter tiles:
+// 32 x 64 per wave, 1 x 2 blocks of v_mfma_f32_32x32x16_bf16), the
+// GroupGemm on N-contiguous plain weights as 2 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16, MXFP8 operands as 2 x 4 blocks of the
+// block-scaled 32 x 32 x 64; the weight gradients 4 waves in a 2 x 2 grid of
+// 128 x 128 sub-tiles.  Operands are
 // staged in LDS as [rows][128 bytes] (64 bf16 or 128 fp8 values), with the
 // 16-byte chunk index XOR-swizzled by row bits 0..4 (swz_key) so that the
 // fragment reads of both MFMA shapes are free of bank conflicts.  Two LDS
@@ -102,18 +103,11 @@ enum { AT_BF16 = 0, AT_MX = 1, AT_MX_A5 = 2, AT_MX_B5 = 3, AT_MX_AB5 = 4 };
 // bit for bit; the dGLU kernel with d(bias) / d(row_scale) 6.5% faster once
 // its epilogue stopped spilling, the non-gated FC1 14% and its backward 3%;
 // on K-contiguous plain weights, whose B DMA is row-strided like A's, dX 10%
-// and dgrad's GEMM 3%).
-constexpr int gm_waves(int epi, int blay, int at) {
-  return (blay == BL_PACKED &&
-          ((at == AT_BF16 &&
-            (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE || epi == EPI_DGLU || epi == EPI_DGLU_G ||
-             epi == EPI_ACT || epi == EPI_DACT)) ||
-           ((at == AT_MX || at == AT_MX_A5) && (epi == EPI_GLU || epi == EPI_GLU_MX || epi == EPI_STORE)))) ||
-                 (blay == BL_NK && at == AT_BF16 &&
-                  (epi == EPI_STORE || epi == EPI_DGLU || epi == EPI_DGLU_G || epi == EPI_DACT))
-             ? 8
-             : 4;
-}
+// and dgrad's GEMM 3%; on N-contiguous ones FC2 3%).
+// The weight gradients keep 4 waves: their 128 x 128 fp32 sub-tile per wave
+// and its staging need the register file of one wave per SIMD (8 waves
+// measured +-0.5%).
+constexpr int gm_waves(int epi, int /*blay*/, int /*at*/) { return epi == EPI_WGRAD ? 4 : 8; }
 
 struct GemmArgs {
   const uint16_t* A;        // [M_cap][K] grouped rows, K contiguous
@@ -448,7 +442,8 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
   constexpr bool KNR = BLAY == BL_KN && !WG;
   constexpr int NW = gm_waves(EPI, BLAY, AT);   // waves per workgroup (4 or 8)
   constexpr int NTH = 64 * NW;           // threads
-  static_assert(NW == 4 || (!WG && !KNR), "8 waves: packed B");
+  static_assert(NW == 4 || !WG, "8 waves: not the weight gradients");
+  static_assert(64 * 32 % NTH == 0 && (NTH == 256 || NTH == 512), "N-contiguous B transpose: 4 or 8 waves");
   // Two distinct stage arrays: the compiler can then see that the LDS-DMA
   // writes of the next stage never alias the fragment reads of the current
   // one, and does not wait for the prefetch before computing.
@@ -638,11 +633,13 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
                  : make_rsrc(p.b_scales + ((long long)e * NT + nt) * nk * 1024, (long long)nk * 1024);
     }
 
-    // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (8 rows);
-    // the column chunk is clamped inside the row so no load leaves the matrix.
+    // N-contiguous B: n-chunk tid % 32 (8 columns), k-group tid / 32 (KR rows:
+    // 8 with 256 threads, 4 with 512); the column chunk is clamped inside the
+    // row so no load leaves the matrix.
+    constexpr int KR = 64 * 32 / NTH;
     const int kn_c = (tid + zt) & 31, kn_g = (tid + zt) >> 5;
     const uint32_t kn_voff =
-        (uint32_t)(kn_g * 8) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
+        (uint32_t)(kn_g * KR) * b_stride + (uint32_t)min(n0 + kn_c * 8, p.N - 8) * 2u;
 
     // bf16 on 8 waves (FC1, the plain GroupGemm, and dgrad + dGLU with or
     // without the parameter gradients on full and half tiles): the main
@@ -653,7 +650,7 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
     // v_mfma_f32_32x32x16_bf16 or the block-scaled 32 x 32 x 64 form.  With
     // conflict-free 16 x 16 reads the dGLU kernel gains 0.4-0.7% (it measured
     // even while those reads had two-way bank conflicts).
-    constexpr bool M16 = NW == 8 && !MXT && !WG && ((EPI != EPI_DGLU && EPI != EPI_DGLU_G) || NBW == 4);
+    constexpr bool M16 = NW == 8 && !MXT && !WG && BLAY != BL_KN && ((EPI != EPI_DGLU && EPI != EPI_DGLU_G) || NBW == 4);
     constexpr bool MX8 = NW == 8 && MXT && !WG;
     static_assert(NBW == 4 || ((EPI == EPI_DGLU || EPI == EPI_DGLU_G) && !M16 && !MX8),
                   "narrow tiles: the dGLU kernels' 32 x 32 loop only");
@@ -762,28 +759,31 @@ __global__ __launch_bounds__(64 * gm_waves(EPI, BLAY, AT), 1) void group_gemm_ke
             4, r * (ah ? sa_stride : 4u), kk * (ah ? 4u : 1024u), 0, 0);
       }
     };
-    u32x4 rb[8];
+    u32x4 rb[KR];
     auto kn_load = [&](int kt) {
       const bool in = kt < nk_t;
       const int ktc = in ? kt : 0;
       const long long krow = (long long)ktc * 64;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < KR; ++i)
         rb[i] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsB : rsZ, kn_voff,
                                                       (uint32_t)((krow + i) * b_stride), 0);
     };
-    // r[i] holds 8 columns at k = 8*kn_g + i; transposed to 8 k-values per column
-    auto kn_put = [&](const u32x4 (&r)[8], uint8_t* t) {
+    // r[i] holds 8 columns at k = KR*kn_g + i; transposed to KR k-values per
+    // column: a whole 16-byte chunk (KR = 8) or its half 8 (kn_g % 2) bytes in
+    auto kn_put = [&](const u32x4 (&r)[KR], uint8_t* t) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint32_t o[4];
+        uint32_t o[KR / 2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < KR / 2; ++q) {
           const uint32_t lo = r[2 * q][j >> 1], hi = r[2 * q + 1][j >> 1];
           o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
         }
-        *reinterpret_cast<uint4*>(t + swz_off(kn_c * 8 + j, kn_g)) =
-            make_uint4(o[0], o[1], o[2], o[3]);
+        if constexpr (KR == 8)
+          *reinterpret_cast<uint4*>(t + swz_off(kn_c * 8 + j, kn_g)) = make_uint4(o[0], o[1], o[2], o[3]);
+        else
+          *reinterpret_cast<uint2*>(t + swz_off(kn_c * 8 + j, kn_g >> 1) + 8 * (kn_g & 1)) = make_uint2(o[0], o[1]);
       }
     };
     auto kn_store = [&](uint8_t* stage) { kn_put(rb, stage + GM_TILE_BYTES); };
